@@ -1,0 +1,410 @@
+"""Pins of the CPU oracle to facts fixed outside it: the pages' printed
+numbers and worked examples, closed forms, library routines and brute force.
+
+Each test names the passage it follows. A plausible slip in the oracle (a
+transposed quantization axis, half-away rounding, a dropped zero-point, a
+wrong GQA head mapping, a missing softmax scale) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+from oracle import kvq_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+F32 = np.float32
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# --- "KV Cache Quantization" (infra.bea.ai) §1 table --------------------------
+def test_memory_table_matches_page():
+    t = _golden("bea_memory_table.json")
+    m = t["model"]
+    for row in t["rows"]:
+        per_token = O.kv_bytes_per_token(m["n_layers"], m["n_kv_heads"], m["head_dim"],
+                                         row["bytes_per_element"])
+        assert per_token == row["kv_per_token_kb"] * 1024
+        ctx_gib = per_token * t["context_tokens"] / 2 ** 30
+        # printed to two decimals, half up (0.625 -> 0.63)
+        assert math.floor(ctx_gib * 100 + 0.5) / 100 == row["context_gb"]
+        # the page divides the budget by its own rounded GB column
+        assert math.floor(t["available_gb"] / row["context_gb"]) == row["max_requests"]
+
+
+def test_memory_formula_llms_intro():
+    # "Memory per Token = 2 x 2 x n_layers x n_kv_heads x d_head bytes" (16-bit)
+    assert O.kv_bytes_per_token(80, 8, 128, 2) == 2 * 2 * 80 * 8 * 128
+    # halving the element width halves the bytes (update section, capacity math)
+    assert O.kv_bytes_per_token(80, 8, 128, 1) * 2 == O.kv_bytes_per_token(80, 8, 128, 2)
+
+
+# --- §3 "Key: Per-Channel Quantization" worked example ----------------------
+def test_key_example_per_channel_scale_is_page_value():
+    g = _golden("bea_kivi_examples.json")
+    K = np.array(g["key_matrix"], F32)                   # rows tokens, cols channels
+    ch = g["key_outlier_channel_1based"] - 1
+    num, den = g["key_outlier_scale"]["numerator"], g["key_outlier_scale"]["denominator"]
+    # per channel = one symmetric absmax/127 scale per column
+    codes, s = O.quantize_int8_per_token(K.T)
+    assert s[ch] == F32(num) / F32(den)
+    # the outlier does not affect the other channels' scales
+    for c in range(K.shape[1]):
+        if c != ch:
+            assert s[c] == np.max(np.abs(K[:, c])) / F32(127)
+            assert s[c] < s[ch] / 20
+    # per-token scaling of the same matrix would mix the outlier into every row
+    _, s_tok = O.quantize_int8_per_token(K)
+    assert np.all(s_tok > F32(7.4) / F32(127))
+    # largest element of each channel maps to the top code
+    assert np.all(np.max(np.abs(codes.astype(int)), axis=1) == 127)
+
+
+def test_key_example_kivi_asymmetric_int4():
+    K = np.array(_golden("bea_kivi_examples.json")["key_matrix"], F32)
+    codes, s, z = O.kivi_quantize_key_group(K, 4)
+    # channel 3 (1-based): min 7.5, max 9.0 -> s = 1.5 / 15 = 0.1, z = 7.5
+    assert s[2] == F32(1.5) / F32(15)
+    assert z[2] == F32(7.5)
+    assert list(codes[:, 2]) == [5, 15, 0]
+    # channel 4: values 0.1, 0.2, 0.1 -> min 0.1, max 0.2 -> codes 0, 15, 0
+    assert list(codes[:, 3]) == [0, 15, 0]
+    assert np.all(codes <= 15)
+
+
+def test_value_example_per_token():
+    V = np.array(_golden("bea_kivi_examples.json")["value_matrix"], F32)
+    codes, s, z = O.kivi_quantize_value_tokens(V, 4, group=4)
+    assert s.shape == (3, 1) and z.shape == (3, 1)
+    # each token gets its own range: [0.3, 0.6], [1.8, 2.1], [0.1, 0.3]
+    np.testing.assert_array_equal(z[:, 0], F32([0.3, 1.8, 0.1]))
+    np.testing.assert_allclose(s[:, 0], [0.3 / 15, 0.3 / 15, 0.2 / 15], rtol=1e-6)
+    assert list(codes[0]) == [10, 0, 5, 15]
+    assert list(codes[1]) == [10, 0, 15, 5]
+    assert codes[2, 0] == 0 and codes[2, 3] == 15
+    # per-token: scaling one token leaves the others' codes unchanged
+    V2 = V.copy()
+    V2[1] *= F32(64.0)
+    c2, _, _ = O.kivi_quantize_value_tokens(V2, 4, group=4)
+    np.testing.assert_array_equal(c2[[0, 2]], codes[[0, 2]])
+
+
+def test_value_groups_split_channels():
+    # two channel groups of 2: each has its own (s, z)
+    v = np.array([[0.0, 3.0, 100.0, 130.0]], F32)
+    codes, s, z = O.kivi_quantize_value_tokens(v, 2, group=2)
+    assert list(s[0]) == [F32(1.0), F32(10.0)]
+    assert list(z[0]) == [F32(0.0), F32(100.0)]
+    assert list(codes[0]) == [0, 3, 0, 3]
+
+
+# --- rounding mode: "Step 3" of the n4n.ai guide uses torch .round() -> half to even
+def test_round_half_even_asymmetric():
+    x = np.array([0.0, 15.0, 2.5, 3.5, 0.5, 14.5, 1.5], F32)[:, None]   # one channel, 7 tokens
+    codes, s, z = O.kivi_quantize_key_group(x, 4)
+    assert s[0] == F32(1.0) and z[0] == F32(0.0)
+    assert list(codes[:, 0]) == [0, 15, 2, 4, 0, 14, 2]
+    # same ties through torch's round (the routine the page calls)
+    assert list(torch.round(torch.tensor([2.5, 3.5, 0.5, 14.5, 1.5])).int()) == [2, 4, 0, 14, 2]
+
+
+def test_round_half_even_int8():
+    x = np.array([[127.0, 62.5, -62.5, 63.5, 0.5, -0.5, 1.5]], F32)
+    codes, s = O.quantize_int8_per_token(x)
+    assert s[0] == F32(1.0)
+    assert list(codes[0]) == [127, 62, -62, 64, 0, 0, 2]
+
+
+def test_int8_range_is_symmetric_127():
+    # "INT8 symmetric quantization maps values to [-127, 127]" (llms.blog, 2.)
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((200, 128)).astype(F32)
+    codes, s = O.quantize_int8_per_token(x)
+    assert codes.min() >= -127 and codes.max() <= 127
+    row_absmax = np.abs(codes.astype(int)).max(axis=1)
+    assert np.all(row_absmax == 127)
+
+
+# --- round-trip error bounds (integer formats: |x - xhat| <= s/2) ------------
+def _fp32_slack(*mags):
+    return 2.0 ** -20 * np.maximum.reduce([np.abs(np.asarray(m, np.float64)) for m in mags])
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_kivi_round_trip_bound(bits):
+    rng = np.random.default_rng(bits)
+    k = (rng.standard_normal((64, 128)) * np.exp(rng.standard_normal((1, 128)))).astype(F32)
+    codes, s, z = O.kivi_quantize_key_group(k, bits)
+    err = np.abs(O.kivi_dequantize_keys(codes, s, z) - k.astype(np.float64))
+    bound = s.astype(np.float64)[None, :] / 2 + _fp32_slack(z, s)[None, :] + _fp32_slack(k)
+    assert np.all(err <= bound)
+    v = (rng.standard_normal((64, 128)) * np.exp(rng.standard_normal((64, 1)))).astype(F32)
+    cv, sv, zv = O.kivi_quantize_value_tokens(v, bits, 32)
+    errv = np.abs(O.kivi_dequantize_values(cv, sv, zv, 32) - v.astype(np.float64))
+    sv_full = np.repeat(sv.astype(np.float64), 32, axis=1)
+    zv_full = np.repeat(zv.astype(np.float64), 32, axis=1)
+    assert np.all(errv <= sv_full / 2 + _fp32_slack(zv_full, sv_full) + _fp32_slack(v))
+
+
+def test_int8_round_trip_bound():
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((300, 128)) * 30).astype(F32)
+    codes, s = O.quantize_int8_per_token(x)
+    err = np.abs(O.dequantize_int8(codes, s) - x.astype(np.float64))
+    assert np.all(err <= s.astype(np.float64)[:, None] * (0.5 + 2.0 ** -20))
+
+
+def test_fp8_round_trip_half_spacing():
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal((300, 128)) * np.exp(rng.standard_normal((300, 1)))).astype(F32)
+    codes, s = O.quantize_fp8_per_token(x)
+    xh = O.dequantize_fp8(codes, s)
+    y = np.abs(x.astype(np.float64) / s.astype(np.float64)[:, None])
+    # E4M3 spacing at |y|: 2**(e-3) for normals, 2**-9 below 2**-6
+    e = np.floor(np.log2(np.maximum(y, 2.0 ** -6)))
+    half = 2.0 ** (e - 4)
+    err = np.abs(xh - x.astype(np.float64)) / s.astype(np.float64)[:, None]
+    assert np.all(err <= half * (1 + 2.0 ** -18) + 2.0 ** -20)
+    # the row maximum reaches the top code 448 (0x7E / 0xFE)
+    top = np.abs(O.e4m3_decode(codes)).max(axis=1)
+    assert np.all(top == 448.0)
+
+
+def test_grid_points_round_trip_exactly():
+    s = F32(0.25)
+    mn = F32(-3.0)
+    ks = np.array([0, 3, 7, 15, 9, 1], F32)
+    x = (mn + ks * s).astype(F32)[:, None]
+    codes, s_, z_ = O.kivi_quantize_key_group(x, 4)
+    assert s_[0] == s and z_[0] == mn
+    np.testing.assert_array_equal(codes[:, 0], ks.astype(np.uint8))
+    np.testing.assert_array_equal(O.kivi_dequantize_keys(codes, s_, z_)[:, 0], x[:, 0].astype(np.float64))
+
+
+def test_degenerate_groups():
+    c = np.full((32, 4), F32(1.25))
+    codes, s, z = O.kivi_quantize_key_group(c, 4)
+    assert np.all(s == 0) and np.all(codes == 0) and np.all(z == F32(1.25))
+    np.testing.assert_array_equal(O.kivi_dequantize_keys(codes, s, z), c.astype(np.float64))
+    zero = np.zeros((3, 16), F32)
+    q8, s8 = O.quantize_int8_per_token(zero)
+    qf, sf = O.quantize_fp8_per_token(zero)
+    assert np.all(q8 == 0) and np.all(s8 == 0) and np.all(qf == 0) and np.all(sf == 0)
+    # signed zeros are canonicalised in the stored zero-point and scale
+    mixed = np.array([[-0.0], [0.0], [-0.0]], F32)
+    _, s0, z0 = O.kivi_quantize_key_group(mixed, 2)
+    assert not np.signbit(z0[0]) and not np.signbit(s0[0])
+
+
+# --- E4M3 codec vs torch's float8_e4m3fn cast (a library routine) -----------
+def test_e4m3_decode_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = O.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(ours[ok], ref[ok])
+    assert O.e4m3_decode(np.uint8(0x7E)) == 448.0
+    assert O.e4m3_decode(np.uint8(0x01)) == 2.0 ** -9
+
+
+def _torch_e4m3(x):
+    return torch.from_numpy(np.ascontiguousarray(x, F32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_encode_all_bf16_in_range_match_torch():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.int16)
+    vals = torch.from_numpy(bits).view(torch.bfloat16).float().numpy()
+    m = np.isfinite(vals) & (np.abs(vals) <= 448.0)
+    np.testing.assert_array_equal(O.e4m3_encode(vals[m]), _torch_e4m3(vals[m]))
+
+
+def test_e4m3_encode_midpoints_and_neighbours_match_torch():
+    reps = O.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))     # non-negative finite codes
+    reps = np.unique(reps)
+    mids = ((reps[:-1] + reps[1:]) / 2).astype(F32)
+    pts = [mids, np.nextafter(mids, F32(np.inf)), np.nextafter(mids, F32(-np.inf)), reps.astype(F32)]
+    rng = np.random.default_rng(3)
+    pts.append((rng.uniform(0, 448, 200000)).astype(F32))
+    pts.append((2.0 ** rng.uniform(-14, -5, 100000)).astype(F32))
+    x = np.concatenate(pts)
+    x = x[np.abs(x) <= 448]
+    x = np.concatenate([x, -x])
+    np.testing.assert_array_equal(O.e4m3_encode(x), _torch_e4m3(x))
+    # named cases: 3 * 2**-11 is the midpoint between 2**-10 and 2**-9 -> even mantissa (2**-9 has m=1... )
+    assert O.e4m3_encode(np.array([3 * 2.0 ** -11], F32))[0] == _torch_e4m3(np.array([3 * 2.0 ** -11]))[0]
+
+
+# --- flush rule: §3 "Residual Cache for Streaming" example ------------------
+def test_residual_example_200_tokens_groups_of_64():
+    ex = _golden("bea_kivi_examples.json")["residual_example"]
+    n, G = ex["tokens"], ex["group"]
+    lo, hi = ex["residual_tokens_1based"]
+    n_resid = hi - lo + 1
+    for R in range(0, n_resid + 1):
+        nq = O.kivi_quantized_prefix(n, G, R)
+        assert nq == ex["quantized_groups_1based"][-1][1]
+        assert n - nq == n_resid
+    seq = O.SequenceCache("kivi", 64, bits=4, group=G, residual=8)
+    rng = np.random.default_rng(1)
+    seq.append(rng.standard_normal((n, 64)).astype(F32), rng.standard_normal((n, 64)).astype(F32))
+    assert seq.n_quantized == 192 and seq.resid_k.shape[0] == 8
+    assert len(seq.k_codes) == 3
+
+
+def test_flush_rule_workload_sizes():
+    assert O.kivi_quantized_prefix(256, 32, 16) == 224      # tiny KIVI workload
+    assert O.kivi_quantized_prefix(32768, 32, 128) == 32640
+    assert O.kivi_quantized_prefix(100, 64, 128) == 0
+    assert O.kivi_quantized_prefix(128 + 64, 64, 128) == 64
+
+
+@pytest.mark.parametrize("fmt,bits,G,R", [("kivi", 4, 32, 16), ("kivi", 2, 32, 40), ("int8", 8, 0, 0),
+                                          ("fp8", 8, 0, 0)])
+def test_append_chunking_invariance(fmt, bits, G, R):
+    rng = np.random.default_rng(11)
+    k = (rng.standard_normal((257, 64)) * 3).astype(F32)
+    v = rng.standard_normal((257, 64)).astype(F32)
+    whole = O.SequenceCache(fmt, 64, bits, G, R)
+    whole.append(k, v)
+    single = O.SequenceCache(fmt, 64, bits, G, R)
+    for t in range(257):
+        single.append(k[t:t + 1], v[t:t + 1])
+    mixed = O.SequenceCache(fmt, 64, bits, G, R)
+    cuts = [0, 5, 6, 70, 71, 200, 257]
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        mixed.append(k[a:b], v[a:b])
+    for other in (single, mixed):
+        Kw, Vw = whole.dequantized()
+        Ko, Vo = other.dequantized()
+        np.testing.assert_array_equal(Kw, Ko)
+        np.testing.assert_array_equal(Vw, Vo)
+        np.testing.assert_array_equal(whole.key_codes(), other.key_codes())
+        np.testing.assert_array_equal(whole.value_codes(), other.value_codes())
+
+
+# --- packing -----------------------------------------------------------------
+def test_pack_known_bytes():
+    assert list(O.pack_codes(np.array([1, 2, 3, 4], np.uint8), 4)) == [0x21, 0x43]
+    assert list(O.pack_codes(np.array([1, 2, 3, 0, 3, 3, 3, 3], np.uint8), 2)) == [0x39, 0xFF]
+    rng = np.random.default_rng(2)
+    for bits in (2, 4):
+        c = rng.integers(0, 2 ** bits, (5, 64)).astype(np.uint8)
+        p = O.pack_codes(c, bits)
+        assert p.shape == (5, 64 * bits // 8)
+        np.testing.assert_array_equal(O.unpack_codes(p, bits), c)
+        # brute force: bit j of element i sits at absolute bit bits*i + j
+        for row in range(5):
+            allbits = np.unpackbits(p[row], bitorder="little")
+            for i in range(64):
+                val = sum(int(allbits[bits * i + j]) << j for j in range(bits))
+                assert val == c[row, i]
+
+
+# --- attention: closed forms and a library softmax ----------------------------
+def _seq_from_rows(K, V):
+    """A float cache holding K, V exactly: KIVI with a residual window larger
+    than the sequence keeps every token at full precision."""
+    s = O.SequenceCache("kivi", K.shape[1], bits=4, group=32, residual=10 ** 6)
+    s.append(K.astype(F32), V.astype(F32))
+    return s
+
+
+def test_attention_single_token_returns_its_value():
+    rng = np.random.default_rng(4)
+    K = rng.standard_normal((1, 8)).astype(F32)
+    V = rng.standard_normal((1, 8)).astype(F32)
+    out = O.decode_attention([_seq_from_rows(K, V)], rng.standard_normal((2, 8)), F32(0.3))
+    np.testing.assert_array_equal(out, np.repeat(V.astype(np.float64), 2, axis=0))
+
+
+def test_attention_zero_query_is_mean_of_values():
+    rng = np.random.default_rng(5)
+    K = rng.standard_normal((9, 8)).astype(F32)
+    V = rng.standard_normal((9, 8)).astype(F32)
+    out = O.decode_attention([_seq_from_rows(K, V)], np.zeros((1, 8)), F32(0.125))
+    np.testing.assert_allclose(out[0], V.astype(np.float64).mean(axis=0), rtol=0, atol=1e-15)
+
+
+def test_attention_two_tokens_log3_split_with_scale():
+    # scores differ by ln 3 after the softmax scale -> weights 3/4, 1/4
+    d = 4
+    scale = F32(0.5)
+    q = np.array([[1.0, 0, 0, 0]])
+    K = np.array([[2 * math.log(3), 0, 0, 0], [0, 0, 0, 0]])
+    V = np.array([[1.0, 0, 4, 8], [0, 1, 0, 8]], F32)
+    seq = O.SequenceCache("kivi", d, bits=4, group=32, residual=100)
+    seq.resid_k = K.astype(F32)            # the residual stores whatever precision it is given
+    seq.resid_v = V
+    seq.n = 2
+    out = O.decode_attention([seq], q, scale)
+    k_exact = np.float64(F32(2 * math.log(3)))
+    w0 = 1 / (1 + math.exp(-np.float64(scale) * k_exact))
+    V64 = V.astype(np.float64)
+    np.testing.assert_allclose(out[0], w0 * V64[0] + (1 - w0) * V64[1], rtol=1e-15, atol=1e-15)
+    np.testing.assert_allclose(out[0], [0.75, 0.25, 3.0, 8.0], atol=1e-6)
+
+
+def test_attention_gqa_head_mapping():
+    rng = np.random.default_rng(6)
+    seqs = []
+    for h in range(2):
+        K = rng.standard_normal((5, 8)).astype(F32)
+        V = (np.ones((5, 8)) * (h + 1) * 10).astype(F32)   # each KV head's values are constant
+        seqs.append(_seq_from_rows(K, V))
+    out = O.decode_attention(seqs, rng.standard_normal((8, 8)), F32(0.3))
+    # query heads 0..3 read KV head 0, 4..7 read KV head 1 (h // (Hq/Hkv))
+    np.testing.assert_allclose(out[:4], 10.0, rtol=1e-14)
+    np.testing.assert_allclose(out[4:], 20.0, rtol=1e-14)
+
+
+def test_attention_matches_scipy_softmax_brute_force():
+    rng = np.random.default_rng(9)
+    for fmt, bits, G, R in (("kivi", 4, 32, 16), ("int8", 8, 0, 0), ("fp8", 8, 0, 0), ("kivi", 2, 32, 8)):
+        hkv, hq, d, n = 2, 8, 64, 100
+        seqs = [O.SequenceCache(fmt, d, bits, G, R) for _ in range(hkv)]
+        raw = []
+        for s in seqs:
+            k = (rng.standard_normal((n, d)) * 2).astype(F32)
+            v = rng.standard_normal((n, d)).astype(F32)
+            s.append(k, v)
+            raw.append(s.dequantized())
+        q = rng.standard_normal((hq, d))
+        scale = F32(1 / 8)
+        out = O.decode_attention(seqs, q, scale)
+        for h in range(hq):
+            K, V = raw[h // (hq // hkv)]
+            logits = [float(np.float64(scale) * sum(q[h, c] * K[t, c] for c in range(d))) for t in range(n)]
+            w = scipy.special.softmax(logits)
+            ref = np.array([sum(w[t] * V[t, c] for t in range(n)) for c in range(d)])
+            np.testing.assert_allclose(out[h], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_dominant_key():
+    rng = np.random.default_rng(10)
+    K = rng.standard_normal((50, 16)).astype(F32) * F32(0.01)
+    K[17] = 40.0
+    V = rng.standard_normal((50, 16)).astype(F32)
+    out = O.decode_attention([_seq_from_rows(K, V)], np.ones((1, 16)), F32(1.0))
+    np.testing.assert_allclose(out[0], V[17], atol=1e-12)
+
+
+def test_kivi_dequantized_cache_orders_quantized_then_residual():
+    rng = np.random.default_rng(12)
+    k = rng.standard_normal((70, 32)).astype(F32)
+    v = rng.standard_normal((70, 32)).astype(F32)
+    s = O.SequenceCache("kivi", 32, 4, 32, 4)
+    s.append(k, v)
+    K, V = s.dequantized()
+    assert K.shape == (70, 32)
+    assert s.n_quantized == 64
+    np.testing.assert_array_equal(K[64:], k[64:].astype(np.float64))   # residual untouched
+    assert np.max(np.abs(K[:64] - k[:64])) < 0.5
