@@ -1,0 +1,280 @@
+"""Benchmark of the quantized KV cache hot path on one MI355X.
+
+A step is one decode iteration over every cache copy ("layer"): append one
+new K/V token per sequence (quantize, or residual write + group flush) and
+run decode attention over the whole cache. Workload 2 (FP8 E4M3 per-token,
+batch 16, 8 KV heads, 32 query heads, head_dim 128, 4096 tokens) is the
+default; its 139 MB cache fits in the 256 MB Infinity Cache, so the step
+rotates over enough independent copies to touch >= 2 GB. Workload 5 runs its
+80 layers instead. Inputs are seeded synthetic data already resident in HBM.
+
+Prints one JSON line: value = algorithmic bytes of the timed steps (cache
+bytes read by decode + q + out, plus append input and cache writes) per
+second of the timed region; "roofline" covers the decode-attention call
+(split-K kernel + merge kernel) timed with HIP events on its stream;
+"cpu_baseline" times the CPU oracle on a bounded sample of the same work.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", type=int, default=2, help="workload index 1..5")
+    p.add_argument("--split", type=int, default=0, help="tokens per decode split (0 = library choice)")
+    p.add_argument("--min-bytes", type=float, default=2.0e9, help="bytes the rotated copies must span")
+    p.add_argument("--layers", type=int, default=0, help="override the number of cache copies")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def bytes_per_token_head(w):
+    """Algorithmic bytes of one quantized token for one KV head (K + V)."""
+    d = w.head_dim
+    if w.fmt in ("fp8", "int8"):
+        return 2 * d + 2 * 4
+    codes = 2 * d * w.bits // 8
+    key_meta = 2 * 4 * d / w.group        # per-channel scale + zero, amortized over G tokens
+    val_meta = 2 * 4 * (d // w.group)     # per-token scale + zero per channel group
+    return codes + key_meta + val_meta
+
+
+def resid_bytes_per_token_head(w):
+    return 2 * w.head_dim * (2 if w.dtype == "bf16" else 4)
+
+
+def nq_of(w, n):
+    if w.fmt != "kivi":
+        return n
+    return w.group * (max(n - w.residual, 0) // w.group)
+
+
+def decode_bytes(w, lens):
+    """Cache bytes read for sequences of the given lengths, plus q and out."""
+    total = 0.0
+    for n in lens:
+        nq = nq_of(w, int(n))
+        total += w.n_kv_heads * (nq * bytes_per_token_head(w) + (int(n) - nq) * resid_bytes_per_token_head(w))
+    elem = 2 if w.dtype == "bf16" else 4
+    total += len(lens) * w.n_q_heads * w.head_dim * (elem + 4)
+    return total
+
+
+def append_bytes(w, lens_before, t):
+    """Input read + cache bytes written when t tokens are appended to
+    sequences of the given lengths (KIVI: ring writes and group flushes)."""
+    elem = 2 if w.dtype == "bf16" else 4
+    d = w.head_dim
+    total = 0.0
+    for n in lens_before:
+        n = int(n)
+        per_head = 2 * t * d * elem                       # read new K and V
+        if w.fmt in ("fp8", "int8"):
+            per_head += t * bytes_per_token_head(w)       # codes + scales written
+        else:
+            q0, q1 = nq_of(w, n), nq_of(w, n + t)
+            flushed = q1 - q0
+            from_ring = max(0, min(n, q1) - q0)
+            per_head += from_ring * 2 * d * elem          # old residual tokens read back
+            per_head += flushed * bytes_per_token_head(w)  # codes + metadata written
+            per_head += (n + t - max(n, q1)) * 2 * d * elem  # tokens left in the ring
+        total += w.n_kv_heads * per_head
+    return total
+
+
+def cpu_baseline(w, k_host, v_host, q_host, lens, seconds):
+    """Time the CPU oracle (as it is) on whole sequences of copy 0: append
+    every token, then decode, until about `seconds` of work is done."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import kvq_oracle as O
+    sm = O.default_sm_scale(w.head_dim)
+    done_bytes, done_seqs, t_used = 0.0, 0, 0.0
+    with threadpool_limits(limits=1):
+        for b in range(w.batch):
+            n = int(lens[b])
+            t0 = time.perf_counter()
+            seqs = []
+            for h in range(w.n_kv_heads):
+                s = O.SequenceCache(w.fmt, w.head_dim, w.bits, w.group, w.residual)
+                s.append(k_host[b, h, :n], v_host[b, h, :n])
+                seqs.append(s)
+            O.decode_attention(seqs, q_host[b], sm)
+            t_used += time.perf_counter() - t0
+            done_bytes += append_bytes(w, [0], n) + decode_bytes(w, [n])
+            done_seqs += 1
+            if t_used >= seconds:
+                break
+    return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done_seqs} of {w.batch} sequences of copy 0 (bulk append of n tokens + one decode, "
+                      f"all {w.n_kv_heads} KV heads), numpy with one BLAS thread, {t_used:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: the quantized KV cache path here is single-GPU "
+              "(sequence/head sharding across GPUs is a design note, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import quantized_kv_cache_06_amd as kvq
+    from kvq_workloads import WORKLOADS, context_lengths, kv_tokens, queries
+    if not os.path.exists(kvq.LIB_PATH):
+        from quantized_kv_cache_06_amd import build as _b
+        _b.build()
+
+    w = WORKLOADS[args.config]
+    dev = torch.device("cuda:0")
+    lens0 = context_lengths(w)
+    n_max = int(lens0.max())
+    grow = args.warmup + args.steps + 1
+    fmt = {"fp8": kvq.FMT_FP8_E4M3, "int8": kvq.FMT_INT8, "kivi": kvq.FMT_KIVI}[w.fmt]
+    cfg = kvq.make_config(fmt, w.bits, w.group, w.residual, w.batch, w.n_kv_heads, w.n_q_heads, w.head_dim,
+                          n_max + grow, kvq.DT_BF16 if w.dtype == "bf16" else kvq.DT_F32)
+    lay = kvq.kvq_get_layout(cfg)
+    if args.layers:
+        copies = args.layers
+    elif w.layers > 1:
+        copies = w.layers
+    else:
+        copies = max(1, math.ceil(args.min_bytes / lay.total_bytes))
+    ws_bytes = kvq.kvq_decode_workspace_bytes(cfg, args.split)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    caches, seq_lens, qs, outs = [], [], [], []
+    fill_ms = []
+    k_host = v_host = None
+    for c in range(copies):
+        buf = torch.zeros(lay.total_bytes, dtype=torch.uint8, device=dev)
+        sl = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+        k, v = kv_tokens(w, n_max, layer=c, device=dev)
+        al = lens0.to(dev) if w.ragged else None
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        kvq.kvq_quantize_append(cfg, buf, sl, k, v, n_max, al)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        fill_ms.append(e0.elapsed_time(e1))
+        if c == 0 and not args.no_cpu_baseline:
+            k_host = k.float().cpu().numpy()
+            v_host = v.float().cpu().numpy()
+        del k, v
+        caches.append(buf)
+        seq_lens.append(sl)
+        qs.append(queries(w, layer=c, device=dev))
+        outs.append(torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device=dev))
+    torch.cuda.synchronize()
+    bulk_tokens = float(lens0.sum())
+    bulk_bytes = sum(append_bytes(w, [0], int(n)) for n in lens0)
+    bulk_ms = float(np.median(fill_ms))
+
+    # new tokens for every step and copy (small), generated up front
+    steps_total = args.warmup + args.steps
+    new_k, new_v = [], []
+    for c in range(copies):
+        k, v = kv_tokens(w, steps_total, layer=c, stream=1, device=dev)
+        new_k.append([k[:, :, s:s + 1].contiguous() for s in range(steps_total)])
+        new_v.append([v[:, :, s:s + 1].contiguous() for s in range(steps_total)])
+    sm = 1.0 / math.sqrt(w.head_dim)
+
+    dec_events = []
+
+    def step(s, timed):
+        for c in range(copies):
+            kvq.kvq_quantize_append(cfg, caches[c], seq_lens[c], new_k[c][s], new_v[c][s], 1)
+            if timed:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            kvq.kvq_decode_attention(cfg, caches[c], seq_lens[c], qs[c], sm, outs[c], ws, ws_bytes, args.split)
+            if timed:
+                e1.record(stream)
+                dec_events.append((e0, e1))
+
+    for s in range(args.warmup):
+        step(s, False)
+    torch.cuda.synchronize()
+    lens_start = lens0.numpy().astype(np.int64) + args.warmup
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for s in range(args.warmup, steps_total):
+        step(s, True)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+
+    dec_bytes_total, app_bytes_total = 0.0, 0.0
+    for i in range(args.steps):
+        before = lens_start + i
+        app_bytes_total += copies * append_bytes(w, before, 1)
+        dec_bytes_total += copies * decode_bytes(w, before + 1)
+    dec_ms = [a.elapsed_time(b) for a, b in dec_events]
+    dec_avg_ms = float(np.mean(dec_ms))
+    dec_bytes_per_call = dec_bytes_total / (args.steps * copies)
+    achieved = dec_bytes_per_call / (dec_avg_ms * 1e-3) / 1e9
+    value = (dec_bytes_total + app_bytes_total) / (total_ms * 1e-3) / 1e9
+    ms_per_step = total_ms / args.steps
+
+    result = {
+        "metric": "decode-attn effective HBM GB/s (% of peak) + appended KV tokens/s, 1 GPU",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3/fp32" if w.fmt == "fp8" else ("int8/fp32" if w.fmt == "int8"
+                                                         else f"u{w.bits}/fp32"),
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "n_kv_heads": w.n_kv_heads, "n_q_heads": w.n_q_heads,
+                   "head_dim": w.head_dim, "context": w.context if not w.ragged else
+                   f"ragged {w.context_min}..{w.context}", "group": w.group, "residual": w.residual,
+                   "input_dtype": w.dtype, "cache_copies": copies, "split_tokens": args.split,
+                   "parallelism": "single GPU"},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "decode_gbps": round(achieved, 2),
+        "decode_pct_of_peak": round(100 * achieved / HBM_PEAK_GBPS, 2),
+        "decode_us_per_call": round(dec_avg_ms * 1e3, 2),
+        "decode_tokens_per_s": round(w.batch * copies * args.steps / (total_ms * 1e-3), 1),
+        "append_bulk_tokens_per_s": round(bulk_tokens / (bulk_ms * 1e-3), 1),
+        "append_bulk_gbps": round(bulk_bytes / (bulk_ms * 1e-3) / 1e9, 2),
+        "wall_s_timed": round(wall, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "decode attention call (split-K partial kernel + merge kernel)",
+                     "bytes_per_launch": round(dec_bytes_per_call, 1)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, k_host, v_host, qs[0].float().cpu().numpy(), lens0.numpy(),
+                                              args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,201 @@
+/*
+ * libkvq — quantized KV cache for AMD MI355X (gfx950): append-time
+ * quantization and single-token decode attention over the quantized cache.
+ *
+ * Sources of the operations (cited by page title and section):
+ *   [BEA]  "KV Cache Quantization", infra.bea.ai inference guide — §3 "KIVI:
+ *          Asymmetric Key/Value Quantization" (Key per-channel, Value
+ *          per-token, "Residual Cache for Streaming"), §4 "FP8 KV Cache"
+ *          (per-token scale from the maximum absolute value, stored beside
+ *          the data).
+ *   [LLMS] "KV Cache Quantization in Production LLM Serving: Comparing FP8,
+ *          INT8, INT4, KIVI, and KVQuant", llms.blog — "1. FP8 KV Cache"
+ *          (OCP E4M3), "2. INT8 and INT4 Uniform Group-Wise Quantization"
+ *          (symmetric INT8 in [-127, 127]), "3. KIVI" (residual window,
+ *          quantize and pack tokens leaving it), "Serving Economics"
+ *          (decode is bandwidth bound).
+ *   [N4N]  "How KV cache quantization reduces GPU memory", n4n.ai blog —
+ *          "Step 3: Implement quantization hooks" (append(layer, k, v) with
+ *          k, v shaped [batch, heads, seq, head_dim]; get(layer) before the
+ *          attention scores), "Step 5" (the dequantize must fuse with the
+ *          attention kernel).
+ *   [DUP]  "KV cache quantization", guide.dupenodi.dev — "Key takeaways":
+ *          the attention kernel must read the quantized cache.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Return value: a kvq_status (0 = KVQ_OK). Argument checks happen on the
+ *    host before any HIP call; a failed check launches nothing and changes
+ *    nothing. KVQ_ERR_HIP reports a failed kernel launch. No C++ exception
+ *    crosses this interface.
+ *  - Memory: every buffer is owned by the caller. Pointers named "device"
+ *    point to GPU memory of the current device and must be 16-byte aligned.
+ *    The library allocates nothing and keeps no global state.
+ *  - Streams: `stream` is a hipStream_t (NULL = the default stream). Calls
+ *    are asynchronous and ordered on that stream; none synchronizes.
+ *  - One cache buffer holds one layer (the `layer_idx` of [N4N] Step 3 is
+ *    the caller's choice of buffer). A zero-filled buffer with all
+ *    seq_lens == 0 is an empty cache; codes and scales of tokens beyond a
+ *    sequence's length are never read.
+ *
+ * Numerics
+ * --------
+ *  Quantization is evaluated in fp32 with IEEE round-to-nearest-even, true
+ *  division and no fused multiply-add, so codes, scales and zero-points are
+ *  reproducible bit for bit:
+ *   FP8 E4M3 per token ([BEA] §4, [LLMS] 1.): a = max|x| over head_dim,
+ *     s = a / 448, code = E4M3_rne(clamp(x / s, -448, 448)); s == 0 -> code 0.
+ *   INT8 symmetric per token ([LLMS] 2.): s = a / 127,
+ *     code = clamp(rint(x / s), -127, 127); s == 0 -> code 0.
+ *   KIVI ([BEA] §3, [LLMS] 3.): Key per channel over a group of G tokens,
+ *     Value per token over groups of G channels; mn, mx = min, max,
+ *     s = (mx - mn) / (2^bits - 1), z = mn, code = clamp(rint((x - mn) / s),
+ *     0, 2^bits - 1); s == 0 -> code 0. Signed zeros in s and z become +0.
+ *     A sequence of n tokens keeps its first n_q = G * floor(max(n - R, 0) / G)
+ *     tokens quantized and tokens [n_q, n) bit-unchanged in a residual ring.
+ *  Dequantized value: code * s (FP8, INT8) or code * s + z (KIVI).
+ *  Attention is fp32 with an online softmax: for query head h of sequence
+ *  b, kv = h / (n_q_heads / n_kv_heads),
+ *    out[b,h,:] = sum_t softmax_t(sm_scale * <q[b,h,:], K^[b,kv,t,:]>) V^[b,kv,t,:]
+ *  over all seq_lens[b] cached tokens. An empty sequence gives zeros.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID = 1,     /* null pointer, bad size, inconsistent config   */
+  KVQ_ERR_UNSUPPORTED = 2, /* well-formed request outside what is built      */
+  KVQ_ERR_WORKSPACE = 3,   /* decode workspace smaller than required         */
+  KVQ_ERR_HIP = 4          /* HIP reported an error when launching a kernel  */
+} kvq_status;
+
+typedef enum kvq_format {
+  KVQ_FMT_FP8_E4M3 = 1,    /* per-token OCP FP8 E4M3, fp32 scale per token   */
+  KVQ_FMT_INT8 = 2,        /* per-token symmetric INT8, fp32 scale per token */
+  KVQ_FMT_KIVI = 3         /* KIVI asymmetric INT4/INT2 + residual window    */
+} kvq_format;
+
+typedef enum kvq_dtype {
+  KVQ_DT_F32 = 0,          /* IEEE binary32                                  */
+  KVQ_DT_BF16 = 1          /* bfloat16                                       */
+} kvq_dtype;
+
+/* Shape and format of one layer's cache. Supported: head_dim 64 or 128;
+ * n_q_heads = g * n_kv_heads with g in 1..8; bits 8 for FP8/INT8 (group and
+ * residual must be 0), bits 4 or 2 for KIVI with group 32 or 64 dividing
+ * head_dim and 0 <= residual <= 4096; 1 <= max_tokens <= 2^24. */
+typedef struct kvq_config {
+  int32_t format;      /* kvq_format                                         */
+  int32_t bits;        /* code width: 8 (FP8, INT8), 4 or 2 (KIVI)           */
+  int32_t group;       /* KIVI G: tokens per Key group = channels per Value group */
+  int32_t residual;    /* KIVI R: most recent tokens always kept unquantized */
+  int32_t batch;       /* B sequences                                        */
+  int32_t n_kv_heads;  /* Hkv                                                */
+  int32_t n_q_heads;   /* Hq                                                 */
+  int32_t head_dim;    /* d                                                  */
+  int32_t max_tokens;  /* capacity per sequence                              */
+  int32_t in_dtype;    /* kvq_dtype of K/V inputs, q and the residual ring   */
+} kvq_config;
+
+/* Where each array sits inside one layer's cache buffer (byte offsets from
+ * the buffer start, each a multiple of 256). Index order is always
+ * [b][kv_head][...] with b-major order. cap = token_capacity.
+ *
+ *  k_codes  [B][Hkv][cap][row_bytes]       token-major; within a row, code of
+ *           channel c sits in byte c*bits/8 at bit (c % (8/bits))*bits
+ *           (low bits first; one byte per channel for FP8/INT8).
+ *  v_codes  [B][Hkv][cap/8][d][bits]       tokens in blocks of 8; for each
+ *           block and channel c one little-endian word of 8*bits bits whose
+ *           bits [i*bits, (i+1)*bits) hold token 8*blk+i (FP8/INT8: byte i).
+ *  FP8/INT8: k_scale, v_scale [B][Hkv][cap] fp32; k_zero, v_zero unused (0).
+ *  KIVI:    k_scale, k_zero [B][Hkv][cap/G][d] fp32 (per group, per channel);
+ *           v_scale, v_zero [B][Hkv][cap][d/G] fp32 (per token, per channel
+ *           group); k_resid, v_resid [B][Hkv][resid_slots][d] in in_dtype,
+ *           token t of a sequence in slot t % resid_slots.
+ *  Unused regions have offset 0. INT8 codes are two's complement bytes. */
+typedef struct kvq_layout {
+  uint64_t total_bytes;
+  uint64_t k_codes_off, v_codes_off;
+  uint64_t k_scale_off, v_scale_off;
+  uint64_t k_zero_off, v_zero_off;
+  uint64_t k_resid_off, v_resid_off;
+  int32_t token_capacity;  /* cap: max_tokens rounded up to 32 (FP8/INT8) or to G (KIVI) */
+  int32_t resid_slots;     /* KIVI ring slots = residual + group; 0 otherwise */
+  int32_t row_bytes;       /* head_dim * bits / 8                             */
+  int32_t elem_bytes;      /* bytes of one in_dtype element (4 or 2)          */
+} kvq_layout;
+
+/* Message for a status code (static storage; never NULL). */
+const char* kvq_status_string(int32_t status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t kvq_version(void);
+
+/* Fills *layout for cfg ([N4N] Step 3 constructor arguments: layers are
+ * separate buffers; heads, head_dim, dtype and group size set the shape).
+ * Host only, no HIP call. Errors: KVQ_ERR_INVALID (null pointer, bad value),
+ * KVQ_ERR_UNSUPPORTED (valid but outside the supported shapes above). */
+int32_t kvq_get_layout(const kvq_config* cfg, kvq_layout* layout);
+
+/* Appends new tokens to every sequence of one layer's cache and quantizes
+ * them ([N4N] Step 3 append; [BEA] §3 and §4; [LLMS] 1.-3.).
+ *  cache        device, kvq_layout.total_bytes bytes, modified.
+ *  seq_lens     device int32 [B], tokens held per sequence; advanced by the
+ *               number of tokens appended to each sequence.
+ *  k_new,v_new  device [B][Hkv][t_new][d] in cfg->in_dtype, contiguous,
+ *               oldest token first; read only.
+ *  t_new        tokens per sequence in k_new/v_new, >= 0 (0 is a no-op).
+ *  append_lens  device int32 [B] or NULL: sequence b appends only its first
+ *               append_lens[b] tokens (ragged batches); NULL = t_new for all.
+ * FP8/INT8 quantize each token on arrival. KIVI writes new tokens to the
+ * residual ring and quantizes (and packs) every whole group of G tokens
+ * that the flush rule admits, Key per channel and Value per token; a group
+ * may mix older residual tokens with new ones. The result depends only on
+ * the token sequence, not on how it was split into calls.
+ * A sequence with seq_lens[b] < 0, an append length outside [0, t_new], or
+ * seq_lens[b] + append length > max_tokens is left entirely unchanged
+ * (callers detect this by reading seq_lens). Calls that overlap in time on
+ * the same cache race. Errors: KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED,
+ * KVQ_ERR_HIP. */
+int32_t kvq_quantize_append(const kvq_config* cfg, void* cache, int32_t* seq_lens,
+                            const void* k_new, const void* v_new, int32_t t_new,
+                            const int32_t* append_lens, void* stream);
+
+/* Workspace bytes that kvq_decode_attention needs for split_tokens (0 =
+ * the library's choice for cfg). Host only. Errors: KVQ_ERR_INVALID,
+ * KVQ_ERR_UNSUPPORTED (split_tokens not a positive multiple of 64). */
+int32_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t split_tokens, uint64_t* bytes);
+
+/* Single-token decode attention that reads the quantized cache directly and
+ * dequantizes in registers ([DUP] "Key takeaways"; [N4N] Step 5: no separate
+ * dequantize pass). Split-K over the token axis (flash-decoding): each
+ * split of split_tokens tokens produces a partial softmax state (running
+ * max, running sum, unnormalized output), and a second kernel merges the
+ * splits of each (sequence, query head) with the log-sum-exp rule.
+ *  cache        device, one layer's cache; read only.
+ *  seq_lens     device int32 [B]; values are clamped to [0, max_tokens].
+ *  q            device [B][Hq][d] in cfg->in_dtype (the new query token).
+ *  sm_scale     softmax scale applied to the dot products (1/sqrt(d) is usual).
+ *  out          device fp32 [B][Hq][d], written.
+ *  workspace    device scratch of at least kvq_decode_workspace_bytes(cfg,
+ *               split_tokens) bytes; contents on entry are ignored.
+ *  split_tokens tokens per split, a positive multiple of 64, or 0 for auto.
+ * Errors: KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE,
+ * KVQ_ERR_HIP. */
+int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache, const int32_t* seq_lens,
+                             const void* q, float sm_scale, float* out, void* workspace,
+                             uint64_t workspace_bytes, int32_t split_tokens, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

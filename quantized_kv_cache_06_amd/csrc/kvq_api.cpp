@@ -1,0 +1,225 @@
+// Host side of libkvq: argument validation, the cache layout, split planning
+// and kernel dispatch. Every check here runs before any HIP call, so a
+// rejected call changes nothing and needs no GPU.
+#include <stdint.h>
+#include <string.h>
+
+#include "kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr int64_t kMaxTokens = int64_t(1) << 24;
+constexpr int kMaxResidual = 4096;
+
+uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+int32_t validate(const kvq_config* c) {
+  if (!c) return KVQ_ERR_INVALID;
+  if (c->batch < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1 || c->head_dim < 1 || c->max_tokens < 1)
+    return KVQ_ERR_INVALID;
+  if (c->n_q_heads % c->n_kv_heads != 0) return KVQ_ERR_INVALID;
+  if (c->in_dtype != KVQ_DT_F32 && c->in_dtype != KVQ_DT_BF16) return KVQ_ERR_INVALID;
+  if (c->max_tokens > kMaxTokens) return KVQ_ERR_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128) return KVQ_ERR_UNSUPPORTED;
+  const int g = c->n_q_heads / c->n_kv_heads;
+  if (g > 8) return KVQ_ERR_UNSUPPORTED;
+  // Batch and KV heads index grid dimensions y and z (at most 65535 each).
+  if (c->batch > 65535 || c->n_kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
+  switch (c->format) {
+    case KVQ_FMT_FP8_E4M3:
+    case KVQ_FMT_INT8:
+      if (c->bits != 8 || c->group != 0 || c->residual != 0) return KVQ_ERR_INVALID;
+      break;
+    case KVQ_FMT_KIVI:
+      if (c->bits != 4 && c->bits != 2) return KVQ_ERR_INVALID;
+      if (c->group <= 0 || c->residual < 0) return KVQ_ERR_INVALID;
+      if (c->head_dim % c->group != 0) return KVQ_ERR_INVALID;
+      if (c->group != 32 && c->group != 64) return KVQ_ERR_UNSUPPORTED;
+      if (c->residual > kMaxResidual) return KVQ_ERR_UNSUPPORTED;
+      break;
+    default:
+      return KVQ_ERR_INVALID;
+  }
+  return KVQ_OK;
+}
+
+void make_layout(const kvq_config* c, kvq_layout* L) {
+  memset(L, 0, sizeof(*L));
+  const bool kivi = c->format == KVQ_FMT_KIVI;
+  const uint64_t pairs = uint64_t(c->batch) * c->n_kv_heads;
+  const int D = c->head_dim;
+  const int unit = kivi ? c->group : 32;
+  const uint64_t cap = (uint64_t(c->max_tokens) + unit - 1) / unit * unit;
+  L->token_capacity = int32_t(cap);
+  L->row_bytes = D * c->bits / 8;
+  L->elem_bytes = c->in_dtype == KVQ_DT_BF16 ? 2 : 4;
+  uint64_t off = 0;
+  auto region = [&](uint64_t bytes) {
+    const uint64_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  L->k_codes_off = region(pairs * cap * L->row_bytes);
+  L->v_codes_off = region(pairs * cap * L->row_bytes);
+  if (!kivi) {
+    L->k_scale_off = region(pairs * cap * 4);
+    L->v_scale_off = region(pairs * cap * 4);
+  } else {
+    const uint64_t groups = cap / c->group;
+    const uint64_t vgroups = D / c->group;
+    L->k_scale_off = region(pairs * groups * D * 4);
+    L->k_zero_off = region(pairs * groups * D * 4);
+    L->v_scale_off = region(pairs * cap * vgroups * 4);
+    L->v_zero_off = region(pairs * cap * vgroups * 4);
+    L->resid_slots = c->residual + c->group;
+    L->k_resid_off = region(pairs * L->resid_slots * D * L->elem_bytes);
+    L->v_resid_off = region(pairs * L->resid_slots * D * L->elem_bytes);
+  }
+  L->total_bytes = off;
+}
+
+kvq::CacheView make_view(const kvq_config* c, const kvq_layout& L, const void* cache) {
+  kvq::CacheView v;
+  uint8_t* base = static_cast<uint8_t*>(const_cast<void*>(cache));
+  const bool kivi = c->format == KVQ_FMT_KIVI;
+  v.fmt = c->format;
+  v.bits = c->bits;
+  v.G = c->group;
+  v.R = c->residual;
+  v.B = c->batch;
+  v.Hkv = c->n_kv_heads;
+  v.Hq = c->n_q_heads;
+  v.D = c->head_dim;
+  v.g = c->n_q_heads / c->n_kv_heads;
+  v.max_tokens = c->max_tokens;
+  v.bf16 = c->in_dtype == KVQ_DT_BF16;
+  v.cap = L.token_capacity;
+  v.C = L.resid_slots;
+  v.row_bytes = L.row_bytes;
+  v.k_codes = base + L.k_codes_off;
+  v.v_codes = base + L.v_codes_off;
+  v.k_scale = reinterpret_cast<float*>(base + L.k_scale_off);
+  v.v_scale = reinterpret_cast<float*>(base + L.v_scale_off);
+  v.k_zero = kivi ? reinterpret_cast<float*>(base + L.k_zero_off) : nullptr;
+  v.v_zero = kivi ? reinterpret_cast<float*>(base + L.v_zero_off) : nullptr;
+  v.k_resid = kivi ? base + L.k_resid_off : nullptr;
+  v.v_resid = kivi ? base + L.v_resid_off : nullptr;
+  return v;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Tokens per split when the caller passes 0: enough (b, kv head, split)
+// workgroups to cover the 256 compute units several times over, with splits
+// of 256..4096 tokens (multiples of 64 so KIVI groups never straddle).
+int auto_split(const kvq_config* c) {
+  const int64_t pairs = int64_t(c->batch) * c->n_kv_heads;
+  const int64_t target = 2048;
+  int64_t splits = (target + pairs - 1) / pairs;
+  if (splits < 1) splits = 1;
+  int64_t L = (c->max_tokens + splits - 1) / splits;
+  L = (L + 63) / 64 * 64;
+  if (L < 256) L = 256;
+  if (L > 4096) L = 4096;
+  return int(L);
+}
+
+int32_t split_plan(const kvq_config* c, int32_t split_tokens, int* L, int* S) {
+  if (split_tokens < 0 || (split_tokens > 0 && split_tokens % 64 != 0)) return KVQ_ERR_UNSUPPORTED;
+  *L = split_tokens ? split_tokens : auto_split(c);
+  *S = c->max_tokens / *L + 1;
+  return KVQ_OK;
+}
+
+uint64_t workspace_bytes(const kvq_config* c, int S) {
+  const uint64_t rows = uint64_t(c->batch) * c->n_q_heads * S;
+  return align256(rows * c->head_dim * 4) + align256(rows * 4) + align256(rows * 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_status_string(int32_t s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_INVALID: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVQ_ERR_WORKSPACE: return "workspace too small";
+    case KVQ_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t kvq_version(void) { return kVersion; }
+
+int32_t kvq_get_layout(const kvq_config* cfg, kvq_layout* layout) {
+  if (!layout) return KVQ_ERR_INVALID;
+  const int32_t st = validate(cfg);
+  if (st != KVQ_OK) return st;
+  make_layout(cfg, layout);
+  return KVQ_OK;
+}
+
+int32_t kvq_quantize_append(const kvq_config* cfg, void* cache, int32_t* seq_lens, const void* k_new,
+                            const void* v_new, int32_t t_new, const int32_t* append_lens, void* stream) {
+  const int32_t st = validate(cfg);
+  if (st != KVQ_OK) return st;
+  if (!cache || !seq_lens || t_new < 0) return KVQ_ERR_INVALID;
+  if (t_new == 0) return KVQ_OK;
+  if (!k_new || !v_new) return KVQ_ERR_INVALID;
+  if (!aligned16(cache) || !aligned16(k_new) || !aligned16(v_new) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3) || (reinterpret_cast<uintptr_t>(append_lens) & 3))
+    return KVQ_ERR_INVALID;
+  if (int64_t(t_new) > kMaxTokens) return KVQ_ERR_UNSUPPORTED;
+  kvq_layout L;
+  make_layout(cfg, &L);
+  const kvq::CacheView v = make_view(cfg, L, cache);
+  const hipError_t e = kvq::launch_append(v, seq_lens, k_new, v_new, t_new, append_lens,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+int32_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t split_tokens, uint64_t* bytes) {
+  if (!bytes) return KVQ_ERR_INVALID;
+  const int32_t st = validate(cfg);
+  if (st != KVQ_OK) return st;
+  int L, S;
+  const int32_t sp = split_plan(cfg, split_tokens, &L, &S);
+  if (sp != KVQ_OK) return sp;
+  *bytes = workspace_bytes(cfg, S);
+  return KVQ_OK;
+}
+
+int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache, const int32_t* seq_lens, const void* q,
+                             float sm_scale, float* out, void* workspace, uint64_t ws_bytes,
+                             int32_t split_tokens, void* stream) {
+  const int32_t st = validate(cfg);
+  if (st != KVQ_OK) return st;
+  if (!cache || !seq_lens || !q || !out || !workspace) return KVQ_ERR_INVALID;
+  if (!aligned16(cache) || !aligned16(q) || !aligned16(out) || !aligned16(workspace) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3))
+    return KVQ_ERR_INVALID;
+  if (!(sm_scale == sm_scale) || sm_scale > 3.0e38f || sm_scale < -3.0e38f) return KVQ_ERR_INVALID;
+  int L, S;
+  const int32_t sp = split_plan(cfg, split_tokens, &L, &S);
+  if (sp != KVQ_OK) return sp;
+  if (ws_bytes < workspace_bytes(cfg, S)) return KVQ_ERR_WORKSPACE;
+  kvq_layout lay;
+  make_layout(cfg, &lay);
+  const kvq::CacheView v = make_view(cfg, lay, cache);
+  const uint64_t rows = uint64_t(cfg->batch) * cfg->n_q_heads * S;
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  kvq::DecodeWork work;
+  work.o = reinterpret_cast<float*>(w);
+  work.m = reinterpret_cast<float*>(w + align256(rows * cfg->head_dim * 4));
+  work.l = reinterpret_cast<float*>(w + align256(rows * cfg->head_dim * 4) + align256(rows * 4));
+  work.S = S;
+  work.L = L;
+  const hipError_t e = kvq::launch_decode(v, seq_lens, q, sm_scale, out, work, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// Internal interface between the host entry points (kvq_api.cpp) and the
+// HIP kernels (kvq_append.hip, kvq_decode.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+// One layer's cache, resolved to device pointers. Built on the host from a
+// validated kvq_config and its kvq_layout; passed to kernels by value.
+struct CacheView {
+  int fmt;         // kvq_format
+  int bits;        // 8, 4 or 2
+  int G;           // KIVI group (0 for per-token formats)
+  int R;           // KIVI residual window
+  int B, Hkv, Hq, D, g;
+  int max_tokens;
+  int bf16;        // in_dtype is bf16 (else fp32)
+  int cap;         // token capacity of the code arrays
+  int C;           // residual ring slots (KIVI)
+  int row_bytes;   // D * bits / 8
+  uint8_t* k_codes;
+  uint8_t* v_codes;
+  float* k_scale;
+  float* v_scale;
+  float* k_zero;
+  float* v_zero;
+  uint8_t* k_resid;
+  uint8_t* v_resid;
+};
+
+// Decode workspace split into its three arrays.
+struct DecodeWork {
+  float* o;   // [B][Hq][S][D] unnormalized partial outputs
+  float* m;   // [B][Hq][S] running maxima
+  float* l;   // [B][Hq][S] running sums
+  int S;      // split slots per (b, q head)
+  int L;      // tokens per split
+};
+
+hipError_t launch_append(const CacheView& cv, int32_t* seq_lens, const void* k_new,
+                         const void* v_new, int T, const int32_t* append_lens, hipStream_t stream);
+
+hipError_t launch_decode(const CacheView& cv, const int32_t* seq_lens, const void* q,
+                         float sm_scale, float* out, const DecodeWork& work, hipStream_t stream);
+
+}  // namespace kvq

@@ -1,0 +1,294 @@
+"""GPU parity: libkvq (through the C ABI) against the CPU oracle on the same
+seeded inputs. Codes, scales, zero-points, residual rows and seq_lens must be
+bit-exact; fp32 attention must be within max-abs 1e-3 and rel-L2 1e-4 of the
+oracle's fp64 attention over the same dequantized cache."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import kvq_testlib as T
+from kvq_workloads import WORKLOADS, context_lengths, kv_tokens, queries
+from oracle import kvq_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+F32 = np.float32
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# Small versions of the five workloads: same formats, groups, residual windows
+# and distributions; several 256-token chunks, splits and a ragged tail.
+SMALL = {
+    1: WORKLOADS[1],
+    2: WORKLOADS[2].scaled(batch=3, n_kv_heads=2, n_q_heads=8, context=1000, context_min=1000),
+    3: WORKLOADS[3].scaled(batch=2, n_kv_heads=2, n_q_heads=16, context=777, context_min=777),
+    4: WORKLOADS[4].scaled(batch=2, n_kv_heads=2, n_q_heads=16, context=1500, context_min=1500),
+    5: WORKLOADS[5].scaled(batch=3, n_kv_heads=2, n_q_heads=16, context=1500, context_min=700, layers=1),
+}
+
+
+def _lens(w):
+    return context_lengths(w) if w.ragged else torch.full((w.batch,), w.context, dtype=torch.int32)
+
+
+def _oracle_all(w, k, v, lens, chunks=None):
+    """Oracle sequences [b][h] after appending each sequence's first lens[b]
+    tokens (in the given chunk boundaries, if any)."""
+    kf, vf = T.as_f32(k), T.as_f32(v)
+    seqs = []
+    for b in range(w.batch):
+        n = int(lens[b])
+        row = []
+        for h in range(w.n_kv_heads):
+            cuts = [0, n] if chunks is None else chunks
+            ks = [kf[b, h, a:c] for a, c in zip(cuts[:-1], cuts[1:])]
+            vs = [vf[b, h, a:c] for a, c in zip(cuts[:-1], cuts[1:])]
+            row.append(T.oracle_sequence(w, ks, vs))
+        seqs.append(row)
+    return seqs
+
+
+def _check_decode(w, cache, seqs, q, sm, split_tokens=None, label=""):
+    out = cache.decode(q, sm, split_tokens).cpu().numpy()
+    qf = T.as_f32(q)
+    worst = (0.0, 0.0)
+    for b in range(w.batch):
+        ref = O.decode_attention(seqs[b], qf[b], sm)
+        ma, rel = T.attention_errors(out[b], ref)
+        worst = (max(worst[0], ma), max(worst[1], rel))
+        assert ma <= T.MAX_ABS_TOL and rel <= T.REL_L2_TOL, f"{label} b={b}: max-abs {ma:.3g} rel-L2 {rel:.3g}"
+    _log(f"  decode {label} split={split_tokens}: max-abs {worst[0]:.3g} rel-L2 {worst[1]:.3g}")
+    return out
+
+
+@pytest.mark.parametrize("idx", sorted(SMALL))
+def test_small_workload_append_and_decode(idx):
+    w = SMALL[idx]
+    _log(f"[small workload {idx}: {w.name} B={w.batch} Hkv={w.n_kv_heads} Hq={w.n_q_heads} n<={w.context}]")
+    torch.manual_seed(0)
+    cache = T.GpuCache(T.config(w, w.context + 70))
+    k, v = kv_tokens(w, w.context, device="cuda")
+    lens = _lens(w)
+    cache.append(k, v, lens if w.ragged else None)
+    torch.cuda.synchronize()
+    seqs = _oracle_all(w, k, v, lens)
+    contents = T.CacheContents(cache)
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            T.assert_cache_matches(contents, b, h, seqs[b][h], w)
+    _log("  append: bit-exact")
+    q = queries(w, device="cuda")
+    sm = O.default_sm_scale(w.head_dim)
+    out0 = _check_decode(w, cache, seqs, q, sm, 0, "auto")
+    for st in (64, 128, 512):
+        _check_decode(w, cache, seqs, q, sm, st, f"split{st}")
+    # the same call twice gives the same bits
+    out1 = cache.decode(q, sm, 0).cpu().numpy()
+    np.testing.assert_array_equal(out0.view(np.uint32), out1.view(np.uint32))
+
+    # streaming: single-token appends, crossing KIVI flush boundaries
+    steps = 70
+    kk, vv = kv_tokens(w, steps, stream=1, device="cuda")
+    kf, vf = T.as_f32(kk), T.as_f32(vv)
+    for s in range(steps):
+        cache.append(kk[:, :, s:s + 1], vv[:, :, s:s + 1])
+    torch.cuda.synchronize()
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            seqs[b][h].append(kf[b, h], vf[b, h])
+    contents = T.CacheContents(cache)
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            T.assert_cache_matches(contents, b, h, seqs[b][h], w)
+    _log(f"  {steps} single-token appends: bit-exact")
+    _check_decode(w, cache, seqs, queries(w, step=1, device="cuda"), sm, 0, "after-stream")
+
+
+@pytest.mark.parametrize("idx", [1, 4, 2])
+def test_chunked_append_equals_bulk(idx):
+    w = SMALL[idx]
+    n = min(w.context, 600)
+    _log(f"[chunking invariance workload {idx}, n={n}]")
+    cuts = [0, 1, 8, 32, 33, 100, 229, 256, 300, 301, 599, n]
+    k, v = kv_tokens(w, n, device="cuda")
+    bulk = T.GpuCache(T.config(w, n + 8))
+    bulk.append(k, v)
+    chunked = T.GpuCache(T.config(w, n + 8))
+    for a, c in zip(cuts[:-1], cuts[1:]):
+        chunked.append(k[:, :, a:c], v[:, :, a:c])
+    torch.cuda.synchronize()
+    lens = torch.full((w.batch,), n, dtype=torch.int32)
+    seqs = _oracle_all(w, k, v, lens)
+    cb, cc = T.CacheContents(bulk), T.CacheContents(chunked)
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            T.assert_cache_matches(cb, b, h, seqs[b][h], w)
+            T.assert_cache_matches(cc, b, h, seqs[b][h], w)
+    q = queries(w, device="cuda")
+    sm = O.default_sm_scale(w.head_dim)
+    ob = bulk.decode(q, sm).cpu().numpy()
+    oc = chunked.decode(q, sm).cpu().numpy()
+    np.testing.assert_array_equal(ob.view(np.uint32), oc.view(np.uint32))
+
+
+def test_edge_cases_empty_single_residual_only_and_overflow():
+    w = SMALL[5].scaled(batch=4, context=300, context_min=300)
+    _log("[edge cases: empty / n=1 / residual-only / overflow / bad append_lens]")
+    cache = T.GpuCache(T.config(w, 300))
+    sm = O.default_sm_scale(w.head_dim)
+    q = queries(w, device="cuda")
+    # empty cache -> zeros
+    out = cache.decode(q, sm).cpu().numpy()
+    assert np.all(out == 0)
+    k, v = kv_tokens(w, 300, device="cuda")
+    # ragged: 0 tokens, 1 token, fewer than R (all residual), exactly R + G
+    lens = torch.tensor([0, 1, 100, w.residual + w.group], dtype=torch.int32)
+    cache.append(k, v, lens)
+    seqs = _oracle_all(w, k, v, lens)
+    contents = T.CacheContents(cache)
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            T.assert_cache_matches(contents, b, h, seqs[b][h], w)
+    out = _check_decode(w, cache, seqs, q, sm, 0, "ragged-small")
+    assert np.all(out[0] == 0)
+    # n = 1: output equals that token's value row for every query head of its KV head
+    vf = T.as_f32(v)
+    for hq in range(w.n_q_heads):
+        np.testing.assert_allclose(out[1, hq], vf[1, hq // (w.n_q_heads // w.n_kv_heads), 0], rtol=1e-6, atol=1e-6)
+    # overflow for sequence 3 (capacity 300) and malformed lengths leave sequences unchanged
+    before = cache.seq_lens.clone()
+    k2, v2 = kv_tokens(w, 250, stream=2, device="cuda")
+    cache.append(k2, v2, torch.tensor([0, -1, 251, 250], dtype=torch.int32))
+    torch.cuda.synchronize()
+    assert torch.equal(cache.seq_lens.cpu(), before.cpu())
+    contents = T.CacheContents(cache)
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            T.assert_cache_matches(contents, b, h, seqs[b][h], w)
+
+
+def test_fp8_encoder_all_bf16_values_and_midpoints():
+    """Every bf16 value in [-448, 448] plus E4M3 midpoints +-1 ulp through the
+    per-token FP8 kernel: rows anchored at 448 have scale exactly 1, so the
+    codes are the E4M3 rounding of the values themselves."""
+    _log("[FP8 E4M3 encoder sweep]")
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.int16)
+    vals = torch.from_numpy(bits).view(torch.bfloat16).float().numpy()
+    vals = vals[np.isfinite(vals) & (np.abs(vals) <= 448)]
+    reps = np.unique(np.abs(O.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))))
+    mids = ((reps[:-1] + reps[1:]) / 2).astype(F32)
+    extra = np.concatenate([mids, np.nextafter(mids, F32(1e9)), np.nextafter(mids, F32(-1e9))])
+    extra = np.concatenate([extra, -extra, np.float32([3 * 2.0 ** -11, -0.0, 2.0 ** -10, 1e-30])])
+    allv = np.concatenate([vals, extra]).astype(F32)
+    d = 128
+    rows = -(-allv.size // (d - 1))
+    x = np.zeros((rows, d), F32)
+    flat = np.zeros(rows * (d - 1), F32)
+    flat[:allv.size] = allv
+    x[:, 0] = 448.0
+    x[:, 1:] = flat.reshape(rows, d - 1)
+    w = WORKLOADS[2].scaled(batch=1, n_kv_heads=1, n_q_heads=1, dtype="f32", context=rows, context_min=rows)
+    cache = T.GpuCache(T.config(w, rows))
+    kt = torch.from_numpy(x).reshape(1, 1, rows, d).cuda()
+    cache.append(kt, kt)
+    torch.cuda.synchronize()
+    c = T.CacheContents(cache)
+    ks, vs = c.token_scales(0, 0, rows)
+    assert np.all(ks == 1.0) and np.all(vs == 1.0)
+    ref = O.e4m3_encode(x)
+    np.testing.assert_array_equal(c.key_codes(0, 0, rows), ref)
+    np.testing.assert_array_equal(c.value_codes(0, 0, rows), ref)
+
+
+def test_int8_and_kivi_round_half_even_ties():
+    _log("[round-half-even ties: INT8 and KIVI]")
+    d = 64
+    # INT8: rows anchored at 127 (scale exactly 1) holding .5 ties
+    ties = np.array([0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 62.5, -62.5, 126.5, -126.5], F32)
+    x = np.zeros((4, d), F32)
+    x[:, 0] = 127.0
+    x[:, 1:1 + ties.size] = ties
+    w8 = WORKLOADS[3].scaled(batch=1, n_kv_heads=1, n_q_heads=1, head_dim=d, dtype="f32", context=4,
+                             context_min=4)
+    c8 = T.GpuCache(T.config(w8, 64))
+    xt = torch.from_numpy(x).reshape(1, 1, 4, d).cuda()
+    c8.append(xt, xt)
+    torch.cuda.synchronize()
+    got = T.CacheContents(c8).key_codes(0, 0, 4).view(np.int8)
+    assert list(got[0, 1:1 + ties.size]) == [0, 2, 2, 0, -2, -2, 62, -62, 126, -126]
+    # KIVI: a Key group whose channels run 0..15 (s = 1, z = 0) with .5 ties;
+    # a Value token whose channel group spans 0..15 likewise
+    G = 32
+    wk = WORKLOADS[1].scaled(batch=1, n_kv_heads=1, n_q_heads=1, residual=0, context=G, context_min=G)
+    kx = np.zeros((G, d), F32)
+    kx[1, :] = 15.0
+    kx[2:, :] = (np.arange((G - 2) * d).reshape(G - 2, d) % 31 / 2.0).astype(F32)
+    ck = T.GpuCache(T.config(wk, G))
+    kt = torch.from_numpy(kx).reshape(1, 1, G, d).cuda()
+    vt = torch.from_numpy(kx.T.copy()[:G, :d] if d == G else np.tile(kx[:, :G], (1, d // G))).reshape(
+        1, 1, G, d).cuda()
+    ck.append(kt, vt)
+    torch.cuda.synchronize()
+    ref = T.oracle_sequence(wk, [kx], [T.as_f32(vt)[0, 0]])
+    T.assert_cache_matches(T.CacheContents(ck), 0, 0, ref, wk)
+    codes = T.CacheContents(ck).key_codes(0, 0, G)
+    expect = np.clip(np.rint(kx), 0, 15).astype(np.uint8)
+    np.testing.assert_array_equal(codes, expect)
+
+
+# --- full-size workloads: sampled (b, kv head) pairs ------------------------
+def _sampled_full(idx, pairs, n_decode_pairs, layer=0):
+    w = WORKLOADS[idx]
+    lens = context_lengths(w, layer)
+    n_max = int(lens.max())
+    _log(f"[full workload {idx}: {w.name} B={w.batch} n<={n_max} layer={layer}]")
+    cache = T.GpuCache(T.config(w, n_max + 64))
+    k, v = kv_tokens(w, n_max, layer=layer, device="cuda")
+    cache.append(k, v, lens if w.ragged else None)
+    torch.cuda.synchronize()
+    assert torch.equal(cache.seq_lens.cpu(), lens)
+    contents = T.CacheContents(cache)
+    rng = np.random.default_rng(1234 + idx + layer)
+    picks = [(int(rng.integers(w.batch)), int(rng.integers(w.n_kv_heads))) for _ in range(pairs)]
+    picks[0] = (int(np.argmax(lens.numpy())), w.n_kv_heads - 1)
+    refs = {}
+    for b, h in picks:
+        n = int(lens[b])
+        ref = T.oracle_sequence(w, [T.as_f32(k[b, h, :n])], [T.as_f32(v[b, h, :n])])
+        T.assert_cache_matches(contents, b, h, ref, w)
+        refs[(b, h)] = ref
+    _log(f"  append: {len(picks)} sampled (b, kv head) pairs bit-exact")
+    del k, v
+    q = queries(w, layer=layer, device="cuda")
+    sm = O.default_sm_scale(w.head_dim)
+    out = cache.decode(q, sm).cpu().numpy()
+    qf = T.as_f32(q)
+    g = w.n_q_heads // w.n_kv_heads
+    worst = (0.0, 0.0)
+    for b, h in picks[:n_decode_pairs]:
+        K, V = refs[(b, h)].dequantized()
+        for j in range(g):
+            hq = h * g + j
+            ref = O.attention_one_head(qf[b, hq], K, V, sm)
+            ma, rel = T.attention_errors(out[b, hq], ref)
+            worst = (max(worst[0], ma), max(worst[1], rel))
+            assert ma <= T.MAX_ABS_TOL and rel <= T.REL_L2_TOL, f"b={b} hq={hq}: {ma:.3g} {rel:.3g}"
+    _log(f"  decode: sampled heads max-abs {worst[0]:.3g} rel-L2 {worst[1]:.3g}")
+    assert np.all(np.isfinite(out))
+
+
+@pytest.mark.parametrize("idx", [2, 3, 4])
+def test_full_size_workload_sampled(idx):
+    _sampled_full(idx, pairs=3, n_decode_pairs=2)
+
+
+@pytest.mark.parametrize("layer", [0, 79])
+def test_full_size_long_context_layer_sampled(layer):
+    _sampled_full(5, pairs=2, n_decode_pairs=2, layer=layer)
