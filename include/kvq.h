@@ -112,9 +112,14 @@ typedef struct kvq_config {
  *  k_codes  [B][Hkv][cap][row_bytes]       token-major; within a row, code of
  *           channel c sits in byte c*bits/8 at bit (c % (8/bits))*bits
  *           (low bits first; one byte per channel for FP8/INT8).
- *  v_codes  [B][Hkv][cap/8][d][bits]       tokens in blocks of 8; for each
- *           block and channel c one little-endian word of 8*bits bits whose
- *           bits [i*bits, (i+1)*bits) hold token 8*blk+i (FP8/INT8: byte i).
+ *  v_codes  [B][Hkv][cap/TB][d][TB*bits/8] tokens in blocks of TB = 8 (8-bit
+ *           codes, INT4) or TB = 16 (INT2); for each block, d little-endian
+ *           words of TB*bits bits (8 bytes for 8-bit codes, else 4) whose bits
+ *           [i*bits, (i+1)*bits) hold token TB*blk+i of one channel (8-bit:
+ *           byte i). Word slots are permuted within chunks of 16*W channels,
+ *           W = 16 / word bytes (2 or 4): slot W*m + x of a chunk holds the
+ *           word of channel 16*x + m of that chunk, so a 16-byte load at slot
+ *           W*m returns channel m of W consecutive 16-channel tiles.
  *  FP8/INT8: k_scale, v_scale [B][Hkv][cap] fp32; k_zero, v_zero unused (0).
  *  KIVI:    k_scale, k_zero [B][Hkv][cap/G][d] fp32 (per group, per channel);
  *           v_scale, v_zero [B][Hkv][cap][d/G] fp32 (per token, per channel

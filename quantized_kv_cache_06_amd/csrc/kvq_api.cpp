@@ -111,25 +111,28 @@ kvq::CacheView make_view(const kvq_config* c, const kvq_layout& L, const void* c
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-// Tokens per split when the caller passes 0: enough (b, kv head, split)
-// workgroups to cover the 256 compute units several times over, with splits
-// of 256..4096 tokens (multiples of 64 so KIVI groups never straddle).
+// Tokens per split when the caller passes 0: about 1024 workgroups of 4
+// waves over the longest possible sequences (four waves per SIMD fill the
+// 256 compute units once), splits of 256..4096 tokens in multiples of 64 so
+// KIVI groups never straddle a split.
 int auto_split(const kvq_config* c) {
   const int64_t pairs = int64_t(c->batch) * c->n_kv_heads;
-  const int64_t target = 2048;
-  int64_t splits = (target + pairs - 1) / pairs;
-  if (splits < 1) splits = 1;
-  int64_t L = (c->max_tokens + splits - 1) / splits;
+  const int64_t target = 1024;
+  int64_t L = (int64_t(c->max_tokens) * pairs + target - 1) / target;
   L = (L + 63) / 64 * 64;
   if (L < 256) L = 256;
   if (L > 4096) L = 4096;
   return int(L);
 }
 
+// Split plan: L tokens per split, S partial slots per (sequence, query
+// head): ceil(max_tokens / L) for quantized tokens plus one for the KIVI
+// residual window (unused by the per-token formats).
 int32_t split_plan(const kvq_config* c, int32_t split_tokens, int* L, int* S) {
   if (split_tokens < 0 || (split_tokens > 0 && split_tokens % 64 != 0)) return KVQ_ERR_UNSUPPORTED;
+  if (split_tokens > (1 << 24)) return KVQ_ERR_UNSUPPORTED;
   *L = split_tokens ? split_tokens : auto_split(c);
-  *S = c->max_tokens / *L + 1;
+  *S = (c->max_tokens + *L - 1) / *L + 1;
   return KVQ_OK;
 }
 

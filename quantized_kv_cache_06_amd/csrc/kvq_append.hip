@@ -97,10 +97,10 @@ __global__ __launch_bounds__(kThreads) void append_per_token(CacheView cv, const
         }
         if (lane == 0) cv.k_scale[pair * cv.cap + t] = s;
       } else {
-        // Value codes: 8-token blocks, one 8-byte word per channel.
+        // Value codes: 8-token blocks, one 8-byte word per channel slot.
         uint8_t* blk = cv.v_codes + (pair * (cv.cap / 8) + t / 8) * (size_t(D) * 8) + (t & 7);
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) blk[size_t(lane * CPL + j) * 8] = uint8_t(codes >> (8 * j));
+        for (int j = 0; j < CPL; ++j) blk[size_t(value_slot<2>(lane * CPL + j)) * 8] = uint8_t(codes >> (8 * j));
         if (lane == 0) cv.v_scale[pair * cv.cap + t] = s;
       }
     }
@@ -231,25 +231,21 @@ __global__ __launch_bounds__(kThreads) void kivi_flush(CacheView cv, const int32
   }
   __syncthreads();
   {
-    // 8-token blocks; a 32-bit word holds 8 tokens of one channel (INT4) or
-    // of two adjacent channels, 16 bits each (INT2).
-    constexpr int CPW = BITS == 4 ? 1 : 2;
-    constexpr int WPB = D / CPW;
-    uint32_t* blocks =
-        reinterpret_cast<uint32_t*>(cv.v_codes + (pair * (cv.cap / 8) + size_t(grp) * (G / 8)) * (D * BITS));
-    for (int w = tid; w < (G / 8) * WPB; w += kThreads) {
-      const int blk = w / WPB, wc = w % WPB;
+    // Blocks of TB tokens (8 for INT4, 16 for INT2): one 32-bit word per
+    // channel slot holds the block's codes of that channel, token k in bits
+    // [k * BITS, (k + 1) * BITS).
+    constexpr int TB = BITS == 2 ? 16 : 8;
+    constexpr int NB = G / TB;
+    uint32_t* blocks = reinterpret_cast<uint32_t*>(cv.v_codes) + (pair * (cv.cap / TB) + size_t(grp) * NB) * D;
+    for (int w = tid; w < NB * D; w += kThreads) {
+      const int blk = w / D, c = w % D, j = c / G;
       uint32_t word = 0;
 #pragma unroll
-      for (int cc = 0; cc < CPW; ++cc) {
-        const int c = wc * CPW + cc, j = c / G;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int i = blk * 8 + k;
-          word |= asym_code(xs[i][c], sv[i][j], zv[i][j], QMAX) << ((cc * 8 + k) * BITS);
-        }
+      for (int k = 0; k < TB; ++k) {
+        const int i = blk * TB + k;
+        word |= asym_code(xs[i][c], sv[i][j], zv[i][j], QMAX) << (k * BITS);
       }
-      blocks[w] = word;
+      blocks[blk * D + value_slot<4>(c)] = word;
     }
   }
 }

@@ -1,21 +1,45 @@
-// Decode attention over the quantized cache (gfx950): split-K partials and
-// the cross-split merge.
+// Decode attention over the quantized cache (gfx950): split-K partials on
+// the matrix cores and the cross-split merge.
 //
 // Operation: one query token per sequence attends to every cached token
-// while the codes are dequantized in registers — "KV cache quantization"
+// while the codes are dequantized on the fly — "KV cache quantization"
 // (guide.dupenodi.dev) "Key takeaways": the attention kernel must read the
 // quantized cache; "How KV cache quantization reduces GPU memory" (n4n.ai)
 // "Step 5": a separate dequantize pass gives the bandwidth savings away;
 // "KV Cache Quantization in Production LLM Serving" (llms.blog) "Serving
 // Economics": decode is bound by memory bandwidth.
 //
-// decode_split: one workgroup per (split, kv head, sequence). The split's
-// tokens are processed in chunks of 256: one thread per token computes the
-// g query heads' scores, an online softmax keeps (running max m, running sum
-// l) per head, and threads laid out over (channel, token part) accumulate the
-// unnormalized output. KIVI's last split also covers the residual ring.
-// decode_merge: per (query head, sequence), rescales the splits' partial
-// states to a common maximum and normalizes.
+// How the work maps onto CDNA4
+// ----------------------------
+// One workgroup (4 waves) per (split, kv head, sequence); each wave owns a
+// contiguous run of 32-token tiles of the split and keeps its own online
+// softmax state; the waves are merged through LDS at the end. Per tile:
+//
+//  scores (QK): S^T[32 tokens x 16 cols] = K[32 x d] * Qt[d x 16] with
+//    v_mfma_f32_16x16x32_bf16. Column c = 8 * term + head: every query
+//    head of the GQA group (up to 8) appears twice, as the bf16 "hi" part
+//    of its query and as the bf16 "lo" remainder, so the products keep
+//    about 16 significant bits of the fp32 query; the two columns are added
+//    with one DPP row rotation. Codes enter the matrix core exactly as bf16:
+//    E4M3 and INT8 codes convert exactly; INT4/INT2 codes c become 128 + c by
+//    OR-ing them under the bf16 pattern of 128 (the 128 * sum(q) this adds is
+//    subtracted again per group). Per-token scales multiply the finished
+//    scores; KIVI per-channel Key scales are folded into the query once per
+//    group (score = sum_c (q_c s_c) code_c + sum_c q_c z_c).
+//  softmax: running maximum and sum per head in the log2 domain (exp2).
+//  values (PV): O^T[d x 16] += V^T[d x 32] * P^T[32 x 16], again with the
+//    probabilities (times the per-token Value scale) split into bf16 hi and
+//    lo columns; the KIVI per-token zero-points add sum_t p_t z_t per channel
+//    group on the vector ALU.
+// The cache layout (include/kvq.h) is chosen so that every lane loads its
+// operand bytes with 16-byte loads and no shuffles: Key rows token-major,
+// Value words per channel in blocks of 8 (16 for INT2) tokens, channel words
+// permuted so 16 consecutive lanes read 16 consecutive channels.
+//
+// KIVI residual tokens (full precision, fewer than R + G per sequence) are
+// handled by one extra workgroup per (kv head, sequence) on the vector ALU,
+// writing the last partial slot. decode_merge then combines, per (query head,
+// sequence), every partial by the log-sum-exp rule and normalizes.
 #include <hip/hip_runtime.h>
 
 #include "kvq_device.h"
@@ -23,230 +47,779 @@
 namespace kvq {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kChunk = 256;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kTile = 32;        // tokens per wave iteration (two 16-token score tiles)
+constexpr int kResidChunk = 256; // tokens per residual chunk (one per thread)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr uint32_t kMagic128 = 0x43004300u;  // two bf16 128.0
 
-typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Dequantized value of code k (KIVI: code * s + z).
-__device__ __forceinline__ float kivi_value(uint32_t code, float s, float z) { return fmaf(float(code), s, z); }
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                 c, 0, 0, 0);
+}
 
-template <int FMT, int BITS, int D, int NH, bool BF16>
-__global__ __launch_bounds__(kThreads) void decode_split(CacheView cv, const int32_t* __restrict__ seq_lens,
-                                                        const void* __restrict__ q, float sm_scale, DecodeWork wk) {
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                0, 0, 0);
+}
+
+// Two floats to an f16 pair, round to nearest even (x0 in the low half).
+__device__ __forceinline__ uint32_t pack_f16(float x0, float x1) {
+  const f32x2 v = {x0, x1};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+__device__ __forceinline__ float f16_lo(uint32_t w) { return float(__builtin_bit_cast(f16x2_t, w)[0]); }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return float(__builtin_bit_cast(f16x2_t, w)[1]); }
+
+// f16 pair holding 1024 + m (m the mantissa bits) minus 1024: exactly m.
+constexpr uint32_t kMagic1024 = 0x64006400u;  // two f16 1024.0
+__device__ __forceinline__ uint32_t f16_sub1024(uint32_t w) {
+  const f16x2_t x = __builtin_bit_cast(f16x2_t, w);
+  const f16x2_t y = x - f16x2_t{_Float16(1024.0f), _Float16(1024.0f)};
+  return __builtin_bit_cast(uint32_t, y);
+}
+
+// Two floats to a bf16 pair, round to nearest even (x0 in the low half).
+__device__ __forceinline__ uint32_t pack_bf16(float x0, float x1) {
+  const f32x2 v = {x0, x1};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// hi = bf16(x), lo = bf16(x - hi) for a pair of floats.
+struct Split2 {
+  uint32_t hi, lo;
+};
+__device__ __forceinline__ Split2 split_pair(float x0, float x1) {
+  Split2 s;
+  s.hi = pack_bf16(x0, x1);
+  s.lo = pack_bf16(x0 - bf_lo(s.hi), x1 - bf_hi(s.hi));
+  return s;
+}
+
+// x + (x of the lane 8 places along the same 16-lane row): adds the hi and
+// lo columns of one head.
+__device__ __forceinline__ float add_ror8(float x) {
+  const int y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false);
+  return x + __builtin_bit_cast(float, y);
+}
+__device__ __forceinline__ float max_rows(float x) {  // max over lanes l, l^16, l^32, l^48
+  x = fmaxf(x, __shfl_xor(x, 16, kWave));
+  return fmaxf(x, __shfl_xor(x, 32, kWave));
+}
+__device__ __forceinline__ float sum_rows(float x) {
+  x += __shfl_xor(x, 16, kWave);
+  return x + __shfl_xor(x, 32, kWave);
+}
+
+// FP8 E4M3 byte pair (bytes 2*sel, 2*sel+1 of w) to a bf16 pair, exact.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, SEL != 0));
+}
+// Signed INT8 byte pair to a bf16 pair, exact.
+template <int SEL>
+__device__ __forceinline__ uint32_t i8x2_bf16(uint32_t w) {
+  return pack_bf16(float(int8_t(uint8_t(w >> (16 * SEL)))), float(int8_t(uint8_t(w >> (16 * SEL + 8)))));
+}
+// Byte pair SEL of w (8-bit formats) to a bf16 pair, exact.
+template <int FMT, int SEL>
+__device__ __forceinline__ uint32_t byte_pair_bf16(uint32_t w) {
+  if constexpr (FMT == KVQ_FMT_FP8_E4M3) return fp8x2_bf16<SEL>(w);
+  else return i8x2_bf16<SEL>(w);
+}
+
+// ---------------------------------------------------------------------------
+// Index maps shared by the loads and the operands (see the file header).
+//
+// Channel of element i of k-step kk held by row group r in the score MFMA:
+// lanes of row group r hold the contiguous channels [CPL*r, CPL*(r+1)), CPL =
+// D/4, and element i of k-step kk is the following one of them.
+template <int BITS>
+__device__ __forceinline__ constexpr int cperm(int kk, int i) {
+  if constexpr (BITS == 8) return 8 * kk + i;
+  else if constexpr (BITS == 4) return 8 * kk + (i >> 1) + 4 * (i & 1);
+  else return 16 * (kk >> 1) + 4 * (kk & 1) + (i >> 1) + 8 * (i & 1);
+}
+// Token (within a 32-token tile) of score tile t, row 4r + j. The same
+// token is element j (t = 0) / 4 + j (t = 1) of row group r in the value
+// MFMA's K dimension, up to the per-format pairing of the operand halves.
+template <int BITS>
+__device__ __forceinline__ constexpr int tok(int t, int r, int j) {
+  if constexpr (BITS == 2) return 16 * (r >> 1) + 8 * t + 4 * (r & 1) + j;
+  else return 8 * r + 4 * t + j;
+}
+
+// Loads of NB bytes (4, 8, 16 or 32) into dwords.
+template <int NB>
+__device__ __forceinline__ void load_bytes(const uint8_t* p, uint32_t* w) {
+  if constexpr (NB == 32) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(p + 16);
+    w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
+    w[4] = b[0]; w[5] = b[1]; w[6] = b[2]; w[7] = b[3];
+  } else if constexpr (NB == 16) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+    w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
+  } else if constexpr (NB == 8) {
+    const u32x2 a = *reinterpret_cast<const u32x2*>(p);
+    w[0] = a[0]; w[1] = a[1];
+  } else {
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+  }
+}
+
+// N consecutive input elements (bf16 or fp32) starting at element i, as
+// fp32, with 8/16-byte vector loads (i is a multiple of N).
+template <bool BF16, int N>
+__device__ __forceinline__ void load_elems(const void* p, size_t i, float* x) {
+  if constexpr (BF16) {
+    const uint16_t* s = static_cast<const uint16_t*>(p) + i;
+    if constexpr (N % 8 == 0) {
+#pragma unroll
+      for (int v = 0; v < N / 8; ++v) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(s + 8 * v);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          x[8 * v + 2 * k] = bf_lo(w[k]);
+          x[8 * v + 2 * k + 1] = bf_hi(w[k]);
+        }
+      }
+    } else if constexpr (N == 2) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(s);
+      x[0] = bf_lo(w);
+      x[1] = bf_hi(w);
+    } else {
+      static_assert(N % 4 == 0, "bf16 groups of 4");
+#pragma unroll
+      for (int v = 0; v < N / 4; ++v) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(s + 4 * v);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          x[4 * v + 2 * k] = bf_lo(w[k]);
+          x[4 * v + 2 * k + 1] = bf_hi(w[k]);
+        }
+      }
+    }
+  } else {
+    const float* s = static_cast<const float*>(p) + i;
+    static_assert(N % 2 == 0, "fp32 pairs");
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+      for (int v = 0; v < N / 4; ++v) {
+        const f32x4 w = *reinterpret_cast<const f32x4*>(s + 4 * v);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[4 * v + k] = w[k];
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < N / 2; ++v) {
+        const f32x2 w = *reinterpret_cast<const f32x2*>(s + 2 * v);
+        x[2 * v] = w[0];
+        x[2 * v + 1] = w[1];
+      }
+    }
+  }
+}
+
+// Key operand (16 tokens x 32 channels) of k-step kk from the lane's raw
+// Key bytes. 8-bit codes: bf16, exact. KIVI codes: f16, each element exactly
+// code * 2^kfactor_log2(kk, i): the nibble (or 2-bit field) is masked in
+// place under the f16 pattern of 1024 and 1024 is subtracted, which is exact.
+template <int BITS>
+__device__ __forceinline__ constexpr int kfactor_log2(int kk, int i) {
+  if constexpr (BITS == 4) {
+    return ((i >> 1) & 1) ? 4 : 0;
+  } else {
+    const int j = 4 * (kk & 1) + (i >> 1);
+    return j <= 4 ? 2 * j : 2 * (j - 5);
+  }
+}
+
+template <int FMT, int BITS>
+__device__ __forceinline__ u32x4 key_operand(const uint32_t* kw, int kk) {
+  u32x4 a;
+  if constexpr (BITS == 8) {
+    a[0] = byte_pair_bf16<FMT, 0>(kw[2 * kk]);
+    a[1] = byte_pair_bf16<FMT, 1>(kw[2 * kk]);
+    a[2] = byte_pair_bf16<FMT, 0>(kw[2 * kk + 1]);
+    a[3] = byte_pair_bf16<FMT, 1>(kw[2 * kk + 1]);
+  } else if constexpr (BITS == 4) {
+    // pairs (nibble j, nibble j+4): j = 0, 2 at bits 0-3 (x1), j = 1, 3 at bits 4-7 (x16)
+    const uint32_t w = kw[kk], w8 = w >> 8;
+    a[0] = f16_sub1024((w & 0x000F000Fu) | kMagic1024);
+    a[1] = f16_sub1024((w & 0x00F000F0u) | kMagic1024);
+    a[2] = f16_sub1024((w8 & 0x000F000Fu) | kMagic1024);
+    a[3] = f16_sub1024((w8 & 0x00F000F0u) | kMagic1024);
+  } else {
+    // pairs (code j, code j+8), j = 4*(kk&1) + e: fields j <= 4 at bits 2j
+    // (x4^j), fields 5..7 shifted down by 10 (x4^(j-5))
+    const uint32_t w = kw[kk >> 1], w10 = w >> 10;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = 4 * (kk & 1) + e;
+      const uint32_t src = j <= 4 ? w : w10;
+      const int sh = j <= 4 ? 2 * j : 2 * (j - 5);
+      a[e] = f16_sub1024((src & (0x00030003u << sh)) | kMagic1024);
+    }
+  }
+  return a;
+}
+
+// Value operand (16 channels x 32 tokens as bf16) of channel tile mt from
+// the lane's raw Value words (row group r).
+template <int FMT, int BITS>
+__device__ __forceinline__ u32x4 value_operand(const uint32_t* vw, int mt, int r) {
+  u32x4 a;
+  if constexpr (BITS == 8) {
+    // 16-byte load p holds the 8-byte words of channel tiles 2p, 2p+1
+    const uint32_t* w = vw + 4 * (mt >> 1) + 2 * (mt & 1);
+    a[0] = byte_pair_bf16<FMT, 0>(w[0]);
+    a[1] = byte_pair_bf16<FMT, 1>(w[0]);
+    a[2] = byte_pair_bf16<FMT, 0>(w[1]);
+    a[3] = byte_pair_bf16<FMT, 1>(w[1]);
+  } else if constexpr (BITS == 4) {
+    const uint32_t w = vw[mt];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = ((w >> (4 * j)) & 0x000F000Fu) | kMagic128;
+  } else {
+    const uint32_t w = vw[mt];
+    const int sh = 8 * (r & 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = ((w >> (sh + 2 * j)) & 0x00030003u) | kMagic128;
+  }
+  return a;
+}
+
+// Probability operand (32 tokens x 16 columns) from p[t][j] (token tok(t,
+// r, j)): the element order matches value_operand's token order. Each lane
+// splits every value into bf16 hi + lo and keeps the term of its column.
+template <int BITS>
+__device__ __forceinline__ u32x4 prob_operand(const float (&p)[2][4], bool lo) {
+  u32x4 b;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float x0, x1;
+    if constexpr (BITS == 8) {
+      x0 = p[k >> 1][2 * (k & 1)];
+      x1 = p[k >> 1][2 * (k & 1) + 1];
+    } else {
+      x0 = p[0][k];
+      x1 = p[1][k];
+    }
+    const Split2 s = split_pair(x0, x1);
+    b[k] = lo ? s.lo : s.hi;
+  }
+  return b;
+}
+
+// Zeroes the halves of a bf16 operand whose token index is >= valid, for the
+// last, partial tile of a per-token format (8-bit order: element e is token
+// 8r + e of the tile).
+__device__ __forceinline__ u32x4 mask_tokens8(u32x4 a, int r, int valid) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int e = 8 * r + 2 * k;
+    const uint32_t keep = (e < valid ? 0x0000ffffu : 0u) | (e + 1 < valid ? 0xffff0000u : 0u);
+    a[k] &= keep;
+  }
+  return a;
+}
+
+// LDS of one workgroup: the quantized-split path and the residual path use
+// it differently; the larger of the two sizes it.
+template <int D>
+struct SmemQuant {
+  float q[8][D];              // query of the GQA group (KIVI)
+  float o[kWaves][8][D];      // each wave's unnormalized output
+  float m[kWaves][8];
+  float l[kWaves][8];
+  // per-wave staging of a tile's metadata: per-token scales (8-bit
+  // formats: [K | V][32 tokens]); KIVI: Value [scale | zero][32 * D/32]
+  // and Key group [scale | zero][D]
+  float meta[kWaves][2][32 * (D / 32)];
+  float kgrp[kWaves][2][D];
+};
+template <int D>
+struct SmemResid {
+  float q[8][D];
+  float sc[8][kResidChunk];   // scores, then probabilities; reused for the final reduction
+  float st_m[8], st_l[8], st_a[8];
+};
+template <int D>
+constexpr size_t smem_floats() {
+  return (sizeof(SmemQuant<D>) > sizeof(SmemResid<D>) ? sizeof(SmemQuant<D>) : sizeof(SmemResid<D>)) /
+         sizeof(float);
+}
+
+// Row of one partial state (unnormalized output, log2-domain maximum and
+// sum) of query head j of kv head h in split slot s.
+__device__ __forceinline__ size_t partial_row(const CacheView& cv, const DecodeWork& wk, int b, int h, int j,
+                                              int s) {
+  return (size_t(b) * cv.Hq + size_t(h) * cv.g + j) * wk.S + s;
+}
+
+// Orders this wave's LDS writes before its later LDS reads by other lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------------------
+// Quantized tokens [t0, t1) of one split: 4 waves on the matrix cores.
+// Every global load of a tile (codes, scales, zero-points, and the Key
+// group parameters when the tile opens a group) is issued one tile ahead in
+// a single batch, so a wave always has the next tile in flight while it
+// computes the current one; metadata is re-laid out through the wave's own
+// LDS area.
+// ---------------------------------------------------------------------------
+template <int FMT, int BITS, int D, int G, bool BF16>
+__device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int h, int s, int t0, int t1,
+                                                const void* __restrict__ q, float sm_log2, const DecodeWork& wk,
+                                                SmemQuant<D>& sm) {
   constexpr bool KIVI = FMT == KVQ_FMT_KIVI;
-  constexpr int P = kThreads / D;           // token parts in the PV phase
-  constexpr int RB = D * BITS / 8;          // bytes per Key code row
-  constexpr int KGRP = kChunk / 32;         // Key groups per chunk at the smallest group (32)
-  constexpr int NVG_MAX = D / 32;           // Value groups per token at the smallest group
-  static_assert(P * D == kThreads, "thread layout");
+  constexpr int CPL = D / 4;                  // channels per row group (score MFMA)
+  constexpr int NKK = D / 32;                 // k-steps of the score MFMA
+  constexpr int NMT = D / 16;                 // channel tiles of the value MFMA
+  constexpr int KB = D * BITS / 8;            // bytes per Key row
+  constexpr int LKB = CPL * BITS / 8;         // Key bytes per lane per token
+  constexpr int VWB = BITS == 8 ? 8 : 4;      // bytes per Value word (one channel, one block)
+  constexpr int TB = BITS == 2 ? 16 : 8;      // tokens per Value block
+  constexpr int VW = 16 / VWB;                // Value words per 16-byte load
+  constexpr int NVL = D / (16 * VW);          // 16-byte Value loads per lane per tile
+  constexpr int NVG = KIVI ? D / (G > 0 ? G : 1) : 1;  // Value channel groups
+  constexpr int MPG = KIVI ? G / 16 : NMT;    // channel tiles per Value channel group
+  constexpr int KGL = D / 32;                 // Key group floats per lane (lanes 0-31 scale, 32-63 zero)
+  static_assert(KGL == 2 || KGL == 4, "group load width");
 
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int m = lane & 15, r = lane >> 4;
+  const int hh = m & 7;            // head within the GQA group for this column
+  const bool lo_col = m >= 8;      // column holds the lo term
   const int g = cv.g;
-  const int G = cv.G;
-  int n = seq_lens[b];
-  n = min(max(n, 0), cv.max_tokens);
-  const int nq = KIVI ? kivi_quantized(n, G, cv.R) : n;
-  const int L = wk.L;
-  if (s > nq / L) return;
-  const int t0 = s * L;
-  const int t1 = min(t0 + L, nq);
-  const bool has_resid = KIVI && (s == nq / L) && (n > nq);
   const size_t pair = pair_index(cv, b, h);
 
-  __shared__ float qs[NH][D];
-  __shared__ float sc[NH > 8 ? NH : 8][kChunk];   // scores -> probabilities; reused for the final reduction
-  __shared__ float pv[NH][kChunk];                  // probability x Value scale (per-token formats)
-  __shared__ float st_m[NH], st_l[NH], st_a[NH];
-  __shared__ float kss[KIVI ? KGRP : 1][D], kzs[KIVI ? KGRP : 1][D];
-  __shared__ float vss[KIVI ? kChunk : 1][NVG_MAX], vzs[KIVI ? kChunk : 1][NVG_MAX];
+  // ---- query: per-token formats build the operand once; KIVI stages q ----
+  // (vector loads of a clamped head; heads beyond the GQA group read as 0)
+  u32x4 bq[NKK];
+  if constexpr (KIVI) {
+    constexpr int EPT = 8 * D / kThreads;  // 4 (D = 128) or 2 (D = 64) elements per thread
+    const int e0 = tid * EPT, j = e0 / D, c = e0 % D;
+    const size_t qi = (size_t(b) * cv.Hq + size_t(h) * g + min(j, g - 1)) * D + c;
+    float x[EPT];
+    load_elems<BF16, EPT>(q, qi, x);
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) sm.q[j][c + i] = j < g ? x[i] : 0.0f;
+    __syncthreads();
+  } else {
+    const size_t qrow = (size_t(b) * cv.Hq + size_t(h) * g + min(hh, g - 1)) * D + CPL * r;
+    float x[CPL];
+    load_elems<BF16, CPL>(q, qrow, x);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = hh < g ? x[cperm<BITS>(kk, 2 * e)] : 0.0f;
+        const float x1 = hh < g ? x[cperm<BITS>(kk, 2 * e + 1)] : 0.0f;
+        const Split2 sp = split_pair(x0, x1);
+        bq[kk][e] = lo_col ? sp.lo : sp.hi;
+      }
+    }
+  }
 
+  // ---- this wave's contiguous run of tiles (whole KIVI groups) ----
+  const int ntile = (t1 - t0 + kTile - 1) / kTile;
+  constexpr int GG = KIVI ? G : kTile;         // group size (KIVI), else a harmless divisor
+  constexpr int TPG = GG / kTile;
+  int tpw = (ntile + kWaves - 1) / kWaves;
+  tpw = (tpw + TPG - 1) / TPG * TPG;
+  const int ta = min(wave * tpw, ntile), tb = min(ta + tpw, ntile);
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x4 o[NMT];
+#pragma unroll
+  for (int i = 0; i < NMT; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // KIVI: per channel group, sum_t p_t (z_t + kCenter s_t): the zero-points
+  // plus the centre the Value codes are taken about in the matrix core
+  constexpr float kCenter = BITS == 4 ? 7.0f : 1.0f;
+  const uint32_t cpair = pack_bf16(-(128.0f + kCenter), -(128.0f + kCenter));
+  const u32x4 kCenterA = {cpair, cpair, cpair, cpair};
+  float zb[NVG];
+#pragma unroll
+  for (int j = 0; j < NVG; ++j) zb[j] = 0.0f;
+  float kbias = 0.0f, kscale = 1.0f;
+
+  const uint8_t* kbase = cv.k_codes + pair * size_t(cv.cap) * KB + LKB * r;
+  const uint8_t* vbase = cv.v_codes + pair * size_t(cv.cap / TB) * D * VWB;
+  float* meta0 = sm.meta[wave][0];
+  float* meta1 = sm.meta[wave][1];
+
+  // prefetch registers: codes, tile metadata, Key group parameters
+  uint32_t kw[2][LKB / 4], vw[NVL * 4];
+  float mw[NVG], gw[KGL];
+  auto load_tile = [&](int T0, bool new_group) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) load_bytes<LKB>(kbase + size_t(T0 + tok<BITS>(t, m >> 2, m & 3)) * KB, kw[t]);
+    const int blk = T0 / TB + (BITS == 2 ? (r >> 1) : r);
+    const uint8_t* vb = vbase + (size_t(blk) * D + VW * m) * VWB;
+#pragma unroll
+    for (int p = 0; p < NVL; ++p) load_bytes<16>(vb + size_t(p) * 16 * VW * VWB, vw + 4 * p);
+    // metadata: lanes 0-31 the Key (or Value scale) half, lanes 32-63 the
+    // Value (or Value zero) half, NVG floats per lane
+    const int part = lane >> 5, qi = lane & 31;
+    if constexpr (!KIVI) {
+      mw[0] = (part ? cv.v_scale : cv.k_scale)[pair * cv.cap + T0 + qi];
+    } else {
+      const float* src = (part ? cv.v_zero : cv.v_scale) + (pair * cv.cap + T0 + qi) * NVG;
+      if constexpr (NVG == 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(src);
+        mw[0] = x[0]; mw[1] = x[1]; mw[2] = x[2]; mw[3] = x[3];
+      } else if constexpr (NVG == 2) {
+        const f32x2 x = *reinterpret_cast<const f32x2*>(src);
+        mw[0] = x[0]; mw[1] = x[1];
+      } else {
+        mw[0] = src[0];
+      }
+      if (new_group) {
+        const float* gsrc = (part ? cv.k_zero : cv.k_scale) + (pair * (cv.cap / GG) + T0 / GG) * D + qi * KGL;
+        if constexpr (KGL == 4) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(gsrc);
+          gw[0] = x[0]; gw[1] = x[1]; gw[2] = x[2]; gw[3] = x[3];
+        } else {
+          const f32x2 x = *reinterpret_cast<const f32x2*>(gsrc);
+          gw[0] = x[0]; gw[1] = x[1];
+        }
+      }
+    }
+  };
+  auto opens_group = [&](int ti) { return KIVI && (ti == ta || ((t0 + ti * kTile) % GG) == 0); };
+
+  if (ta < tb) load_tile(t0 + ta * kTile, opens_group(ta));
+  for (int ti = ta; ti < tb; ++ti) {
+    const int T0 = t0 + ti * kTile;
+    const bool grp_open = opens_group(ti);
+    uint32_t kc[2][LKB / 4], vc[NVL * 4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < LKB / 4; ++i) kc[t][i] = kw[t][i];
+#pragma unroll
+    for (int i = 0; i < NVL * 4; ++i) vc[i] = vw[i];
+    {
+      const int part = lane >> 5, qi = lane & 31;
+      float* mdst = (part ? meta1 : meta0) + qi * NVG;
+#pragma unroll
+      for (int j = 0; j < NVG; ++j) mdst[j] = mw[j];
+      if constexpr (KIVI) {
+        if (grp_open) {
+          float* gdst = sm.kgrp[wave][part] + qi * KGL;
+#pragma unroll
+          for (int j = 0; j < KGL; ++j) gdst[j] = gw[j];
+        }
+      }
+    }
+    wave_lds_sync();
+    if (ti + 1 < tb) load_tile(T0 + kTile, opens_group(ti + 1));  // prefetch the next tile
+
+    // ---- KIVI: fold this group's per-channel Key scales into the query ----
+    // x_c = q_c * s_c is scaled by 2^ke (per head) so its largest magnitude
+    // is below 2^15, divided by the key operand's power-of-two factor, and
+    // split into f16 hi + lo (about 22 significant bits).
+    if constexpr (KIVI) {
+      if (grp_open) {
+        const float* qr = &sm.q[hh][CPL * r];
+        const float* ksr = &sm.kgrp[wave][0][CPL * r];
+        const float* kzr = &sm.kgrp[wave][1][CPL * r];
+        float xq[NKK][8];
+        float qzs = 0.0f, amax = 0.0f;
+#pragma unroll
+        for (int u = 0; u < NKK / 2; ++u) {  // 16 channels (two k-steps) at a time
+          float ks[16], kz[16], qv[16];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(ksr + 16 * u + 4 * v);
+            const f32x4 z = *reinterpret_cast<const f32x4*>(kzr + 16 * u + 4 * v);
+            const f32x4 x = *reinterpret_cast<const f32x4*>(qr + 16 * u + 4 * v);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              ks[4 * v + i] = a[i];
+              kz[4 * v + i] = z[i];
+              qv[4 * v + i] = x[i];
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 16; ++i) qzs += qv[i] * kz[i];
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh) {
+            const int kk = 2 * u + kh;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int c = cperm<BITS>(kk, i) - 16 * u;
+              xq[kk][i] = qv[c] * ks[c];
+              amax = fmaxf(amax, fabsf(xq[kk][i]));
+            }
+          }
+        }
+        amax = max_rows(amax);
+        const int ke = amax > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(amax) : 0;
+        kscale = __builtin_amdgcn_ldexpf(1.0f, -ke);
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x0 = __builtin_amdgcn_ldexpf(xq[kk][2 * e], ke - kfactor_log2<BITS>(kk, 2 * e));
+            const float x1 = __builtin_amdgcn_ldexpf(xq[kk][2 * e + 1], ke - kfactor_log2<BITS>(kk, 2 * e + 1));
+            const uint32_t hi = pack_f16(x0, x1);
+            const uint32_t lo = pack_f16(x0 - f16_lo(hi), x1 - f16_hi(hi));
+            bq[kk][e] = lo_col ? lo : hi;
+          }
+        }
+        kbias = sum_rows(qzs);
+      }
+    }
+
+    // ---- scores ----
+    f32x4 acc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        if constexpr (KIVI) acc[t] = mfma_f16(key_operand<FMT, BITS>(kc[t], kk), bq[kk], acc[t]);
+        else acc[t] = mfma_bf16(key_operand<FMT, BITS>(kc[t], kk), bq[kk], acc[t]);
+      }
+    }
+    const int valid = KIVI ? kTile : min(kTile, t1 - T0);
+    // this lane's tokens: tok(t, r, j) = base_t + j, 4 consecutive per t
+    f32x4 ks[2], vs[2];
+    if constexpr (!KIVI) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        ks[t] = *reinterpret_cast<const f32x4*>(meta0 + tok<BITS>(t, r, 0));
+        vs[t] = *reinterpret_cast<const f32x4*>(meta1 + tok<BITS>(t, r, 0));
+      }
+    }
+    float sc[2][4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float x = add_ror8(acc[t][j]);
+        if constexpr (KIVI) x = (x * kscale + kbias) * sm_log2;
+        else x = x * ks[t][j] * sm_log2;
+        if (tok<BITS>(t, r, j) >= valid) x = -INFINITY;
+        sc[t][j] = x;
+        tmax = fmaxf(tmax, x);
+      }
+    }
+    tmax = max_rows(tmax);
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p = __builtin_amdgcn_exp2f(sc[t][j] - m_new);
+        sc[t][j] = p;
+        psum += p;
+      }
+    l_run = l_run * alpha + psum;
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int i = 0; i < NMT; ++i) o[i] *= alpha;
+#pragma unroll
+      for (int j = 0; j < NVG; ++j) zb[j] *= alpha;
+    }
+
+    // ---- values ----
+    if constexpr (!KIVI) {
+      float pv[2][4];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pv[t][j] = tok<BITS>(t, r, j) < valid ? sc[t][j] * vs[t][j] : 0.0f;
+      const u32x4 bp = prob_operand<BITS>(pv, lo_col);
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+        u32x4 a = value_operand<FMT, BITS>(vc, mt, r);
+        if (valid < kTile) a = mask_tokens8(a, r, valid);
+        o[mt] = mfma_bf16(a, bp, o[mt]);
+      }
+    } else {
+      // per-token Value scale and zero of each channel group: 4 consecutive
+      // tokens per score tile, NVG values each
+      float vsf[2][4 * NVG], vzf[2][4 * NVG];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int v = 0; v < NVG; ++v) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(meta0 + tok<BITS>(t, r, 0) * NVG + 4 * v);
+          const f32x4 z = *reinterpret_cast<const f32x4*>(meta1 + tok<BITS>(t, r, 0) * NVG + 4 * v);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            vsf[t][4 * v + i] = a[i];
+            vzf[t][4 * v + i] = z[i];
+          }
+        }
+      }
+#pragma unroll
+      for (int jg = 0; jg < NVG; ++jg) {
+        float pv[2][4];
+        float zs = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float vsc = vsf[t][j * NVG + jg];
+            pv[t][j] = sc[t][j] * vsc;
+            zs += sc[t][j] * (vzf[t][j * NVG + jg] + kCenter * vsc);
+          }
+        zb[jg] += zs;
+        const u32x4 bp = prob_operand<BITS>(pv, lo_col);
+#pragma unroll
+        for (int mt = jg * MPG; mt < (jg + 1) * MPG; ++mt) {
+          o[mt] = mfma_bf16(value_operand<FMT, BITS>(vc, mt, r), bp, o[mt]);
+          // the codes entered as 128 + code: take (128 + kCenter) * p' off
+          // in the same accumulator every tile, leaving (code - kCenter) * p'
+          o[mt] = mfma_bf16(kCenterA, bp, o[mt]);
+        }
+      }
+    }
+    wave_lds_sync();  // metadata reads done before the next tile overwrites it
+  }
+
+  // ---- merge the 4 waves through LDS ----
+  const float l_tot = sum_rows(l_run);
+  float zt[NVG];
+#pragma unroll
+  for (int j = 0; j < NVG; ++j) zt[j] = sum_rows(zb[j]);
+  if (lane < 8) {
+    sm.m[wave][lane] = m_run;
+    sm.l[wave][lane] = l_tot;
+  }
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float x = add_ror8(o[mt][j]);
+      if constexpr (KIVI) x += zt[mt / MPG];
+      if (!lo_col) sm.o[wave][hh][16 * mt + 4 * r + j] = x;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < g * D; e += kThreads) {
+    const int j = e / D, c = e % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.m[w][j]);
+    float ov = 0.0f, L = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = __builtin_amdgcn_exp2f(sm.m[w][j] - M);
+        ov += sm.o[w][j][c] * f;
+        L += sm.l[w][j] * f;
+      }
+    }
+    const size_t row = partial_row(cv, wk, b, h, j, s);
+    wk.o[row * D + c] = ov;
+    if (c == 0) {
+      wk.m[row] = M;
+      wk.l[row] = L;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// KIVI residual ring (tokens [nq, n), full precision): one workgroup on the
+// vector ALU, one thread per token for the scores, threads over (channel,
+// token part) for the values. Writes partial slot s.
+// ---------------------------------------------------------------------------
+template <int D, bool BF16>
+__device__ __forceinline__ void split_residual(const CacheView& cv, int b, int h, int s, int nq, int n,
+                                               const void* __restrict__ q, float sm_log2, const DecodeWork& wk,
+                                               SmemResid<D>& sm) {
+  constexpr int NH = 8;
+  constexpr int P = kThreads / D;  // token parts in the value phase
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int g = cv.g, C = cv.C;
+  const size_t pair = pair_index(cv, b, h);
   for (int e = tid; e < NH * D; e += kThreads) {
     const int j = e / D, c = e % D;
-    qs[j][c] = j < g ? load_elem<BF16>(q, (size_t(b) * cv.Hq + size_t(h) * g + j) * D + c) : 0.0f;
+    sm.q[j][c] = j < g ? load_elem<BF16>(q, (size_t(b) * cv.Hq + size_t(h) * g + j) * D + c) : 0.0f;
   }
   if (tid < NH) {
-    st_m[tid] = -INFINITY;
-    st_l[tid] = 0.0f;
-    st_a[tid] = 1.0f;
+    sm.st_m[tid] = -INFINITY;
+    sm.st_l[tid] = 0.0f;
+    sm.st_a[tid] = 1.0f;
   }
   const int c = tid % D, part = tid / D;
   float acc[NH];
 #pragma unroll
   for (int j = 0; j < NH; ++j) acc[j] = 0.0f;
   __syncthreads();
-
-  // Online-softmax update over the nt scores of one chunk (waves take heads).
-  auto softmax_chunk = [&](int nt, int cs) {
-    for (int j = wave; j < NH; j += kThreads / kWave) {
-      if (j >= g) continue;
-      float mx = -INFINITY;
-      for (int i = lane; i < nt; i += kWave) mx = fmaxf(mx, sc[j][i]);
-      mx = wave_max(mx);
-      const float m_old = st_m[j];
-      const float m_new = fmaxf(m_old, mx);
-      const float alpha = __expf(m_old - m_new);
-      float sum = 0.0f;
-      for (int i = lane; i < nt; i += kWave) {
-        const float p = __expf(sc[j][i] - m_new);
-        sc[j][i] = p;
-        sum += p;
-        if constexpr (!KIVI) pv[j][i] = p * cv.v_scale[pair * cv.cap + cs + i];
-      }
-      sum = wave_sum(sum);
-      if (lane == 0) {
-        st_m[j] = m_new;
-        st_l[j] = st_l[j] * alpha + sum;
-        st_a[j] = alpha;
-      }
-    }
-  };
-
-  // ---------------- quantized tokens ----------------
-  for (int cs = t0; cs < t1; cs += kChunk) {
-    const int nt = min(kChunk, t1 - cs);
-    if constexpr (KIVI) {
-      const int g0 = cs / G, ng = (nt + G - 1) / G, nvg = D / G;
-      for (int e = tid; e < ng * D; e += kThreads) {
-        const int gi = e / D, cc = e % D;
-        const size_t si = (pair * (cv.cap / G) + g0 + gi) * D + cc;
-        kss[gi][cc] = cv.k_scale[si];
-        kzs[gi][cc] = cv.k_zero[si];
-      }
-      for (int e = tid; e < nt * nvg; e += kThreads) {
-        const size_t vi = (pair * cv.cap + cs) * nvg + e;
-        vss[e / nvg][e % nvg] = cv.v_scale[vi];
-        vzs[e / nvg][e % nvg] = cv.v_zero[vi];
-      }
-      __syncthreads();
-    }
-    // QK: one thread per token.
+  for (int cs = nq; cs < n; cs += kResidChunk) {
+    const int nt = min(kResidChunk, n - cs);
     if (tid < nt) {
-      const int t = cs + tid;
+      const size_t rbase = (pair * C + ((cs + tid) % C)) * D;
       float sco[NH];
 #pragma unroll
       for (int j = 0; j < NH; ++j) sco[j] = 0.0f;
-      const uint4* row = reinterpret_cast<const uint4*>(cv.k_codes + (pair * cv.cap + t) * RB);
-      const int gl = KIVI ? tid / G : 0;
+      for (int ch = 0; ch < D; ++ch) {
+        const float x = load_elem<BF16>(cv.k_resid, rbase + ch);
 #pragma unroll
-      for (int vi = 0; vi < RB / 16; ++vi) {
-        const uint4 w4 = row[vi];
-        const uint32_t words[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-        for (int wi = 0; wi < 4; ++wi) {
-          constexpr int CPW = 32 / BITS;
-#pragma unroll
-          for (int k = 0; k < CPW; k += (FMT == KVQ_FMT_FP8_E4M3 ? 2 : 1)) {
-            const int ch = (vi * 4 + wi) * CPW + k;
-            float x0, x1 = 0.0f;
-            if constexpr (KIVI) {
-              const uint32_t code = (words[wi] >> (k * BITS)) & ((1u << BITS) - 1u);
-              x0 = kivi_value(code, kss[gl][ch], kzs[gl][ch]);
-            } else if constexpr (FMT == KVQ_FMT_INT8) {
-              x0 = float(int8_t(uint8_t(words[wi] >> (8 * k))));
-            } else {
-              const float2_t f = __builtin_amdgcn_cvt_pk_f32_fp8(int(words[wi] >> (8 * k)), false);
-              x0 = f[0];
-              x1 = f[1];
-            }
-#pragma unroll
-            for (int j = 0; j < NH; ++j) {
-              sco[j] = fmaf(qs[j][ch], x0, sco[j]);
-              if constexpr (FMT == KVQ_FMT_FP8_E4M3) sco[j] = fmaf(qs[j][ch + 1], x1, sco[j]);
-            }
-          }
-        }
+        for (int j = 0; j < NH; ++j) sco[j] = fmaf(sm.q[j][ch], x, sco[j]);
       }
-      const float ks = KIVI ? 1.0f : cv.k_scale[pair * cv.cap + t];
 #pragma unroll
-      for (int j = 0; j < NH; ++j) sc[j][tid] = sco[j] * ks * sm_scale;
+      for (int j = 0; j < NH; ++j) sm.sc[j][tid] = sco[j] * sm_log2;
     }
     __syncthreads();
-    softmax_chunk(nt, cs);
+    for (int j = wave; j < g; j += kWaves) {
+      float mx = -INFINITY;
+      for (int i = lane; i < nt; i += kWave) mx = fmaxf(mx, sm.sc[j][i]);
+      mx = wave_max(mx);
+      const float m_old = sm.st_m[j];
+      const float m_new = fmaxf(m_old, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_old - m_new);
+      float sum = 0.0f;
+      for (int i = lane; i < nt; i += kWave) {
+        const float p = __builtin_amdgcn_exp2f(sm.sc[j][i] - m_new);
+        sm.sc[j][i] = p;
+        sum += p;
+      }
+      sum = wave_sum(sum);
+      if (lane == 0) {
+        sm.st_m[j] = m_new;
+        sm.st_l[j] = sm.st_l[j] * alpha + sum;
+        sm.st_a[j] = alpha;
+      }
+    }
     __syncthreads();
-    // PV: thread (channel c, part) walks 8-token blocks part, part+P, ...
 #pragma unroll
-    for (int j = 0; j < NH; ++j) acc[j] *= st_a[j];
-    const int nblk = (nt + 7) / 8;
-    for (int blk = part; blk < nblk; blk += P) {
-      const size_t tb0 = size_t(cs) + size_t(blk) * 8;
-      const uint8_t* wp = cv.v_codes + ((pair * (cv.cap / 8) + tb0 / 8) * D + c) * BITS;
-      uint32_t w0, w1 = 0;
-      if constexpr (BITS == 8) {
-        const uint2 w = *reinterpret_cast<const uint2*>(wp);
-        w0 = w.x;
-        w1 = w.y;
-      } else if constexpr (BITS == 4) {
-        w0 = *reinterpret_cast<const uint32_t*>(wp);
-      } else {
-        w0 = *reinterpret_cast<const uint16_t*>(wp);
-      }
+    for (int j = 0; j < NH; ++j) acc[j] *= sm.st_a[j];
+    for (int i = part; i < nt; i += P) {
+      const float v = load_elem<BF16>(cv.v_resid, (pair * C + ((cs + i) % C)) * D + c);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int i = blk * 8 + k;
-        if (i < nt) {
-          if constexpr (KIVI) {
-            const uint32_t code = (w0 >> (k * BITS)) & ((1u << BITS) - 1u);
-            const float v = kivi_value(code, vss[i][c / G], vzs[i][c / G]);
-#pragma unroll
-            for (int j = 0; j < NH; ++j) acc[j] = fmaf(sc[j][i], v, acc[j]);
-          } else {
-            const uint32_t wd = k < 4 ? w0 : w1;
-            float v;
-            if constexpr (FMT == KVQ_FMT_INT8) {
-              v = float(int8_t(uint8_t(wd >> (8 * (k & 3)))));
-            } else {
-              const float2_t f = __builtin_amdgcn_cvt_pk_f32_fp8(int(wd >> (8 * (k & 2))), false);
-              v = f[k & 1];
-            }
-#pragma unroll
-            for (int j = 0; j < NH; ++j) acc[j] = fmaf(pv[j][i], v, acc[j]);
-          }
-        }
-      }
+      for (int j = 0; j < NH; ++j) acc[j] = fmaf(sm.sc[j][i], v, acc[j]);
     }
     __syncthreads();
   }
-
-  // ---------------- residual ring (KIVI, last split only) ----------------
-  if constexpr (KIVI) {
-    if (has_resid) {
-      const int C = cv.C;
-      for (int cs = nq; cs < n; cs += kChunk) {
-        const int nt = min(kChunk, n - cs);
-        if (tid < nt) {
-          const int t = cs + tid;
-          const size_t rbase = (pair * C + (t % C)) * D;
-          float sco[NH];
-#pragma unroll
-          for (int j = 0; j < NH; ++j) sco[j] = 0.0f;
-          for (int ch = 0; ch < D; ++ch) {
-            const float x = load_elem<BF16>(cv.k_resid, rbase + ch);
-#pragma unroll
-            for (int j = 0; j < NH; ++j) sco[j] = fmaf(qs[j][ch], x, sco[j]);
-          }
-#pragma unroll
-          for (int j = 0; j < NH; ++j) sc[j][tid] = sco[j] * sm_scale;
-        }
-        __syncthreads();
-        softmax_chunk(nt, cs);
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < NH; ++j) acc[j] *= st_a[j];
-        for (int i = part; i < nt; i += P) {
-          const int t = cs + i;
-          const float v = load_elem<BF16>(cv.v_resid, (pair * C + (t % C)) * D + c);
-#pragma unroll
-          for (int j = 0; j < NH; ++j) acc[j] = fmaf(sc[j][i], v, acc[j]);
-        }
-        __syncthreads();
-      }
-    }
-  }
-
-  // ---------------- combine token parts, write the partial state --------------
-  float* red = &sc[0][0];  // P * NH * D <= 8 * kChunk floats
+  float* red = &sm.sc[0][0];  // P * NH * D <= NH * kResidChunk floats
 #pragma unroll
   for (int j = 0; j < NH; ++j) red[(part * NH + j) * D + c] = acc[j];
   __syncthreads();
@@ -255,59 +828,100 @@ __global__ __launch_bounds__(kThreads) void decode_split(CacheView cv, const int
       float o = 0.0f;
 #pragma unroll
       for (int p = 0; p < P; ++p) o += red[(p * NH + j) * D + c];
-      wk.o[((size_t(b) * cv.Hq + size_t(h) * g + j) * wk.S + s) * D + c] = o;
+      wk.o[partial_row(cv, wk, b, h, j, s) * D + c] = o;
     }
   }
   if (tid < g) {
-    const size_t mi = (size_t(b) * cv.Hq + size_t(h) * g + tid) * wk.S + s;
-    wk.m[mi] = st_m[tid];
-    wk.l[mi] = st_l[tid];
+    const size_t row = partial_row(cv, wk, b, h, tid, s);
+    wk.m[row] = sm.st_m[tid];
+    wk.l[row] = sm.st_l[tid];
   }
 }
 
-// One workgroup (D threads) per (query head, sequence).
+// Grid (S, Hkv, B). Slot s < S-1 covers quantized tokens [s*L, (s+1)*L);
+// slot S-1 covers the KIVI residual ring. Slots with no tokens return
+// without writing (the merge does not read them).
+template <int FMT, int BITS, int D, int G, bool BF16>
+__global__ __launch_bounds__(kThreads) void decode_split(CacheView cv, const int32_t* __restrict__ seq_lens,
+                                                        const void* __restrict__ q, float sm_log2, DecodeWork wk) {
+  constexpr bool KIVI = FMT == KVQ_FMT_KIVI;
+  __shared__ float smem[smem_floats<D>()];
+  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int n = min(max(seq_lens[b], 0), cv.max_tokens);
+  const int nq = KIVI ? kivi_quantized(n, G, cv.R) : n;
+  if (s == wk.S - 1) {
+    if constexpr (KIVI) {
+      if (n > nq) split_residual<D, BF16>(cv, b, h, s, nq, n, q, sm_log2, wk, *reinterpret_cast<SmemResid<D>*>(smem));
+    }
+    return;
+  }
+  const int t0 = s * wk.L;
+  if (t0 >= nq) return;
+  const int t1 = min(t0 + wk.L, nq);
+  split_quantized<FMT, BITS, D, G, BF16>(cv, b, h, s, t0, t1, q, sm_log2, wk, *reinterpret_cast<SmemQuant<D>*>(smem));
+}
+
+// One workgroup (D threads) per (query head, sequence): log-sum-exp merge of
+// the partial states that hold tokens, then normalization.
 template <bool KIVI>
 __global__ void decode_merge(CacheView cv, const int32_t* __restrict__ seq_lens, float* __restrict__ out,
                              DecodeWork wk) {
   const int hq = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
-  int n = seq_lens[b];
-  n = min(max(n, 0), cv.max_tokens);
+  const int n = min(max(seq_lens[b], 0), cv.max_tokens);
   const int nq = KIVI ? kivi_quantized(n, cv.G, cv.R) : n;
-  const int ns = min(nq / wk.L + 1, wk.S);
+  const int nsq = (nq + wk.L - 1) / wk.L;
+  const bool resid = KIVI && n > nq;
   const size_t row = (size_t(b) * cv.Hq + hq) * wk.S;
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, wk.m[row + s]);
+  for (int s = 0; s < nsq; ++s) M = fmaxf(M, wk.m[row + s]);
+  if (resid) M = fmaxf(M, wk.m[row + wk.S - 1]);
   float o = 0.0f;
   if (M != -INFINITY) {
     float lsum = 0.0f, acc = 0.0f;
-    for (int s = 0; s < ns; ++s) {
-      const float w = __expf(wk.m[row + s] - M);
+    for (int s = 0; s < nsq; ++s) {
+      const float w = __builtin_amdgcn_exp2f(wk.m[row + s] - M);
       lsum = fmaf(wk.l[row + s], w, lsum);
       acc = fmaf(wk.o[(row + s) * cv.D + c], w, acc);
+    }
+    if (resid) {
+      const size_t rs = row + wk.S - 1;
+      const float w = __builtin_amdgcn_exp2f(wk.m[rs] - M);
+      lsum = fmaf(wk.l[rs], w, lsum);
+      acc = fmaf(wk.o[rs * cv.D + c], w, acc);
     }
     o = acc / lsum;
   }
   out[(size_t(b) * cv.Hq + hq) * cv.D + c] = o;
 }
 
-template <int FMT, int BITS, int D, bool BF16>
-void launch_split_nh(const CacheView& cv, const int32_t* sl, const void* q, float sm, const DecodeWork& wk,
-                     hipStream_t st) {
+template <int FMT, int BITS, int D, int G, bool BF16>
+void launch_split(const CacheView& cv, const int32_t* sl, const void* q, float sm, const DecodeWork& wk,
+                  hipStream_t st) {
   const dim3 grid(wk.S, cv.Hkv, cv.B);
-  if (cv.g > 4) decode_split<FMT, BITS, D, 8, BF16><<<grid, kThreads, 0, st>>>(cv, sl, q, sm, wk);
-  else decode_split<FMT, BITS, D, 4, BF16><<<grid, kThreads, 0, st>>>(cv, sl, q, sm, wk);
+  decode_split<FMT, BITS, D, G, BF16><<<grid, kThreads, 0, st>>>(cv, sl, q, sm, wk);
+}
+
+template <int FMT, int BITS, int D, bool BF16>
+void launch_split_g(const CacheView& cv, const int32_t* sl, const void* q, float sm, const DecodeWork& wk,
+                    hipStream_t st) {
+  if constexpr (FMT == KVQ_FMT_KIVI) {
+    if (cv.G == 32) launch_split<FMT, BITS, D, 32, BF16>(cv, sl, q, sm, wk, st);
+    else launch_split<FMT, BITS, D, 64, BF16>(cv, sl, q, sm, wk, st);
+  } else {
+    launch_split<FMT, BITS, D, 0, BF16>(cv, sl, q, sm, wk, st);
+  }
 }
 
 template <int FMT, int BITS, bool BF16>
 void launch_split_d(const CacheView& cv, const int32_t* sl, const void* q, float sm, const DecodeWork& wk,
                     hipStream_t st) {
-  if (cv.D == 128) launch_split_nh<FMT, BITS, 128, BF16>(cv, sl, q, sm, wk, st);
-  else launch_split_nh<FMT, BITS, 64, BF16>(cv, sl, q, sm, wk, st);
+  if (cv.D == 128) launch_split_g<FMT, BITS, 128, BF16>(cv, sl, q, sm, wk, st);
+  else launch_split_g<FMT, BITS, 64, BF16>(cv, sl, q, sm, wk, st);
 }
 
 template <bool BF16>
-void launch_split(const CacheView& cv, const int32_t* sl, const void* q, float sm, const DecodeWork& wk,
-                  hipStream_t st) {
+void launch_split_fmt(const CacheView& cv, const int32_t* sl, const void* q, float sm, const DecodeWork& wk,
+                      hipStream_t st) {
   switch (cv.fmt) {
     case KVQ_FMT_FP8_E4M3: launch_split_d<KVQ_FMT_FP8_E4M3, 8, BF16>(cv, sl, q, sm, wk, st); break;
     case KVQ_FMT_INT8: launch_split_d<KVQ_FMT_INT8, 8, BF16>(cv, sl, q, sm, wk, st); break;
@@ -321,8 +935,9 @@ void launch_split(const CacheView& cv, const int32_t* sl, const void* q, float s
 
 hipError_t launch_decode(const CacheView& cv, const int32_t* seq_lens, const void* q, float sm_scale, float* out,
                          const DecodeWork& work, hipStream_t stream) {
-  if (cv.bf16) launch_split<true>(cv, seq_lens, q, sm_scale, work, stream);
-  else launch_split<false>(cv, seq_lens, q, sm_scale, work, stream);
+  const float sm_log2 = sm_scale * kLog2e;
+  if (cv.bf16) launch_split_fmt<true>(cv, seq_lens, q, sm_log2, work, stream);
+  else launch_split_fmt<false>(cv, seq_lens, q, sm_log2, work, stream);
   const dim3 mgrid(cv.Hq, cv.B);
   if (cv.fmt == KVQ_FMT_KIVI) decode_merge<true><<<mgrid, cv.D, 0, stream>>>(cv, seq_lens, out, work);
   else decode_merge<false><<<mgrid, cv.D, 0, stream>>>(cv, seq_lens, out, work);

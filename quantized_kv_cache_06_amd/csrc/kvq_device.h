@@ -48,6 +48,16 @@ __device__ __forceinline__ int kivi_quantized(int n, int G, int R) {
   return t > 0 ? (t / G) * G : 0;
 }
 
+// Slot of channel c among the Value words of one token block: within each
+// chunk of 16*W channels (W words per 16 bytes: 2 for 8-byte words, 4 for
+// 4-byte words), slot W*m + x holds channel 16*x + m, so that one 16-byte
+// load by lane m yields channel m of W consecutive 16-channel tiles.
+template <int W>
+__device__ __forceinline__ int value_slot(int c) {
+  const int chunk = c / (16 * W), in = c % (16 * W);
+  return chunk * 16 * W + W * (in % 16) + in / 16;
+}
+
 __device__ __forceinline__ size_t pair_index(const CacheView& cv, int b, int h) {
   return size_t(b) * cv.Hkv + h;
 }

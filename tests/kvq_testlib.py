@@ -57,16 +57,33 @@ def _unpack_channels(rows: np.ndarray, bits: int) -> np.ndarray:
     return np.stack(parts, axis=-1).reshape(*rows.shape[:-1], rows.shape[-1] * per)
 
 
+def value_tokens_per_block(bits: int) -> int:
+    """Tokens per Value block: 8 for 8-bit and INT4 codes, 16 for INT2."""
+    return 16 if bits == 2 else 8
+
+
+def value_slot(c: np.ndarray, word_bytes: int) -> np.ndarray:
+    """Slot of channel c among one block's Value words (include/kvq.h): in
+    each chunk of 16*W channels (W = 16 / word_bytes), slot W*m + x holds
+    channel 16*x + m."""
+    W = 16 // word_bytes
+    chunk, inner = c // (16 * W), c % (16 * W)
+    return chunk * 16 * W + W * (inner % 16) + inner // 16
+
+
 def _unpack_value_blocks(blocks: np.ndarray, bits: int) -> np.ndarray:
-    """[nblk, d, bits] bytes -> [nblk*8, d] codes (token 8*blk+i in bits [i*bits, (i+1)*bits))."""
-    nblk, d, _ = blocks.shape
+    """[nblk, d slots, word bytes] -> [nblk*TB, d] codes: the word of channel
+    c sits in slot value_slot(c); token TB*blk+i is in bits [i*bits, (i+1)*bits)."""
+    nblk, d, wb = blocks.shape
+    tb = value_tokens_per_block(bits)
+    words = blocks[:, value_slot(np.arange(d), wb), :]          # [nblk, channel, bytes]
     if bits == 8:
-        return blocks.transpose(0, 2, 1).reshape(nblk * 8, d).copy()
-    word = np.zeros((nblk, d), dtype=np.uint32)
-    for byte in range(bits):
-        word |= blocks[:, :, byte].astype(np.uint32) << (8 * byte)
-    toks = [(word >> (bits * i)) & ((1 << bits) - 1) for i in range(8)]
-    return np.stack(toks, axis=1).reshape(nblk * 8, d).astype(np.uint8)
+        return words.transpose(0, 2, 1).reshape(nblk * tb, d).copy()
+    word = np.zeros((nblk, d), dtype=np.uint64)
+    for byte in range(wb):
+        word |= words[:, :, byte].astype(np.uint64) << np.uint64(8 * byte)
+    toks = [(word >> np.uint64(bits * i)) & np.uint64((1 << bits) - 1) for i in range(tb)]
+    return np.stack(toks, axis=1).reshape(nblk * tb, d).astype(np.uint8)
 
 
 class CacheContents:
@@ -95,7 +112,8 @@ class CacheContents:
 
     def value_codes(self, b, h, n):
         cap, d, bits = self.lay.token_capacity, self.cfg.head_dim, self.cfg.bits
-        blocks = self._per_pair(self.lay.v_codes_off, (cap // 8, d, bits), np.uint8, b, h)
+        tb = value_tokens_per_block(bits)
+        blocks = self._per_pair(self.lay.v_codes_off, (cap // tb, d, tb * bits // 8), np.uint8, b, h)
         return _unpack_value_blocks(blocks, bits)[:n]
 
     def token_scales(self, b, h, n):

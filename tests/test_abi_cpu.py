@@ -2,6 +2,8 @@
 point, computes the documented layout, and rejects bad arguments on the host
 before any HIP call (so none of these needs a GPU)."""
 import ctypes
+
+import numpy as np
 import os
 import re
 
@@ -154,3 +156,18 @@ def test_workspace_grows_with_split_count():
     assert big > small > 0
     rows = cfg.batch * cfg.n_q_heads * (cfg.max_tokens // 64 + 1)
     assert big >= rows * (cfg.head_dim + 2) * 4
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("word_bytes", [8, 4])
+def test_value_slot_permutation_matches_header(d, word_bytes):
+    """Value word slots (include/kvq.h): within each chunk of 16*W channels,
+    slot W*m + x holds channel 16*x + m; the map is a bijection on [0, d)."""
+    import kvq_testlib as T
+    W = 16 // word_bytes
+    slots = T.value_slot(np.arange(d), word_bytes)
+    assert sorted(slots.tolist()) == list(range(d))
+    for c in range(d):
+        chunk, inner = divmod(c, 16 * W)
+        m, x = inner % 16, inner // 16
+        assert slots[c] == chunk * 16 * W + W * m + x
