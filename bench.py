@@ -11,7 +11,8 @@ rotates over enough independent copies to touch >= 2 GB. Workload 5 runs its
 Prints one JSON line: value = algorithmic bytes of the timed steps (cache
 bytes read by decode + q + out, plus append input and cache writes) per
 second of the timed region; "roofline" covers the decode-attention call
-(split-K kernel + merge kernel) timed with HIP events on its stream;
+(one launch of the split-K kernel, whose last split per (sequence, KV head)
+merges the partials) timed with HIP events on its stream;
 "cpu_baseline" times the CPU oracle on a bounded sample of the same work.
 """
 from __future__ import annotations
@@ -37,12 +38,15 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", type=int, default=2, help="workload index 1..5")
-    p.add_argument("--split", type=int, default=0, help="tokens per decode split (0 = library choice)")
+    p.add_argument("--split", type=int, default=0, help="longest decode split in tokens (0 = library choice)")
     p.add_argument("--min-bytes", type=float, default=2.0e9, help="bytes the rotated copies must span")
     p.add_argument("--layers", type=int, default=0, help="override the number of cache copies")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--decode-rounds", type=int, default=20, help="passes over all copies in the decode-only timing")
+    p.add_argument("--stream-ref", type=float, default=0.0,
+                   help="instead of the hot path: time torch's copy and sum over this many GiB (the "
+                        "attainable streaming bandwidth, and the plain copy used to scale HBM counters)")
     return p.parse_args()
 
 
@@ -128,6 +132,28 @@ def cpu_baseline(w, k_host, v_host, q_host, lens, seconds):
                       f"all {w.n_kv_heads} KV heads), numpy with one BLAS thread, {t_used:.1f} s"}
 
 
+def stream_reference(torch, gib):
+    """Plain streaming kernels of known size: a device-to-device copy (reads
+    and writes n bytes) and a sum (reads n bytes), each timed with events over
+    10 runs. Prints one JSON line."""
+    n = int(gib * (1 << 30)) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    res = {}
+    for name, fn, nbytes in (("copy", lambda: dst.copy_(src), 8 * n), ("sum", lambda: src.sum(), 4 * n)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        res[name] = {"bytes": nbytes, "us": round(ms * 1e3, 2), "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    print(json.dumps({"stream_reference": res, "gib": gib}), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -147,6 +173,10 @@ def main():
         from quantized_kv_cache_06_amd import build as _b
         _b.build()
 
+    if args.stream_ref > 0:
+        stream_reference(torch, args.stream_ref)
+        return
+
     w = WORKLOADS[args.config]
     dev = torch.device("cuda:0")
     lens0 = context_lengths(w)
@@ -163,7 +193,7 @@ def main():
     else:
         copies = max(1, math.ceil(args.min_bytes / lay.total_bytes))
     ws_bytes = kvq.kvq_decode_workspace_bytes(cfg, args.split)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)  # arrival counters start at zero
     stream = torch.cuda.current_stream()
 
     caches, seq_lens, qs, outs = [], [], [], []
@@ -235,7 +265,7 @@ def main():
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
 
-    # Decode call alone (split-K kernel + merge kernel), rotating over the
+    # Decode call alone (one kernel launch per call), rotating over the
     # copies: a graph of `rounds` passes, timed with events on its stream.
     rounds = max(1, args.decode_rounds)
     dec_graph = torch.cuda.CUDAGraph()
@@ -294,7 +324,7 @@ def main():
         "decode_calls_timed": rounds * copies,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "decode attention call (split-K partial kernel + merge kernel)",
+                     "kernel": "decode_split (one launch per decode call, merge fused)",
                      "bytes_per_launch": round(dec_bytes_per_call, 1)},
     }
     if not args.no_cpu_baseline:

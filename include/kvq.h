@@ -175,24 +175,42 @@ int32_t kvq_quantize_append(const kvq_config* cfg, void* cache, int32_t* seq_len
                             const int32_t* append_lens, void* stream);
 
 /* Workspace bytes that kvq_decode_attention needs for split_tokens (0 =
- * the library's choice for cfg). Host only. Errors: KVQ_ERR_INVALID,
- * KVQ_ERR_UNSUPPORTED (split_tokens not a positive multiple of 64). */
+ * the library's choice for cfg). Host only; the result does not depend on
+ * the device. For split_tokens > 0 it holds n = ceil(max_tokens /
+ * split_tokens) splits; for 0 it holds n = min(128, max(1, max_tokens /
+ * 256)) splits, the most the library's choice can take on any device. The
+ * workspace starts with batch * n_kv_heads uint32 arrival counters (see
+ * kvq_decode_attention for the zero-fill rule), then per (sequence, query
+ * head) n + 1 partial rows of head_dim + 2 fp32, each array 256-byte
+ * aligned. Errors: KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED (split_tokens not a
+ * positive multiple of 64, or more than 128 splits of max_tokens). */
 int32_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t split_tokens, uint64_t* bytes);
 
 /* Single-token decode attention that reads the quantized cache directly and
  * dequantizes in registers ([DUP] "Key takeaways"; [N4N] Step 5: no separate
- * dequantize pass). Split-K over the token axis (flash-decoding): each
- * split of split_tokens tokens produces a partial softmax state (running
- * max, running sum, unnormalized output), and a second kernel merges the
- * splits of each (sequence, query head) with the log-sum-exp rule.
+ * dequantize pass). Split-K over the token axis (flash-decoding): the
+ * quantized tokens of each sequence are spread evenly over n splits (whole
+ * 32-token tiles, whole groups for KIVI), each producing a partial softmax
+ * state (running max, running sum, unnormalized output); the KIVI residual
+ * window is one more split. The last split of each (sequence, kv head) to
+ * finish merges them with the log-sum-exp rule. One launch.
  *  cache        device, one layer's cache; read only.
  *  seq_lens     device int32 [B]; values are clamped to [0, max_tokens].
  *  q            device [B][Hq][d] in cfg->in_dtype (the new query token).
  *  sm_scale     softmax scale applied to the dot products (1/sqrt(d) is usual).
  *  out          device fp32 [B][Hq][d], written.
  *  workspace    device scratch of at least kvq_decode_workspace_bytes(cfg,
- *               split_tokens) bytes; contents on entry are ignored.
- *  split_tokens tokens per split, a positive multiple of 64, or 0 for auto.
+ *               split_tokens) bytes. Its first batch * n_kv_heads uint32
+ *               (the arrival counters) must be zero on entry: zero-fill the
+ *               workspace once after allocating it (or when batch or
+ *               n_kv_heads change); every call leaves them zero when it
+ *               completes. The rest is scratch. Calls that overlap in time
+ *               on one workspace race.
+ *  split_tokens the longest split, a positive multiple of 64 giving at most
+ *               128 splits of max_tokens: n = ceil(max_tokens /
+ *               split_tokens). 0 = the library's choice: n fills about one
+ *               round of the device's resident workgroups (four rounds for
+ *               KIVI), within the bound kvq_decode_workspace_bytes gives.
  * Errors: KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE,
  * KVQ_ERR_HIP. */
 int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache, const int32_t* seq_lens,

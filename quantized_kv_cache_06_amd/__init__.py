@@ -150,7 +150,9 @@ def kvq_decode_workspace_bytes(cfg: KvqConfig, split_tokens: int = 0) -> int:
 
 def kvq_decode_attention(cfg: KvqConfig, cache, seq_lens, q, sm_scale: float, out, workspace,
                          workspace_bytes: Optional[int] = None, split_tokens: int = 0, stream=None) -> None:
-    """Decode attention of one query token per sequence over the cache."""
+    """Decode attention of one query token per sequence over the cache.
+    The workspace must be zero-filled before its first use (its leading
+    arrival counters are left zero by every call)."""
     lay = kvq_get_layout(cfg)
     if workspace_bytes is None:
         workspace_bytes = (workspace.numel() * workspace.element_size()

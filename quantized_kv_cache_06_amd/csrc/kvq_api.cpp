@@ -111,34 +111,56 @@ kvq::CacheView make_view(const kvq_config* c, const kvq_layout& L, const void* c
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-// Tokens per split when the caller passes 0: about 1024 workgroups of 4
-// waves over the longest possible sequences (four waves per SIMD fill the
-// 256 compute units once), splits of 256..4096 tokens in multiples of 64 so
-// KIVI groups never straddle a split.
-int auto_split(const kvq_config* c) {
-  const int64_t pairs = int64_t(c->batch) * c->n_kv_heads;
-  const int64_t target = 1024;
-  int64_t L = (int64_t(c->max_tokens) * pairs + target - 1) / target;
-  L = (L + 63) / 64 * 64;
-  if (L < 256) L = 256;
-  if (L > 4096) L = 4096;
-  return int(L);
+// Most quantized splits per sequence the automatic choice may use (the
+// workspace for split_tokens == 0 is sized for this many): splits of at
+// least 256 tokens of the longest sequence the cache holds, at most
+// kMaxDecodeSplits.
+int auto_split_bound(const kvq_config* c) {
+  int64_t n = c->max_tokens / 256;
+  if (n < 1) n = 1;
+  if (n > kvq::kMaxDecodeSplits) n = kvq::kMaxDecodeSplits;
+  return int(n);
 }
 
-// Split plan: L tokens per split, S partial slots per (sequence, query
-// head): ceil(max_tokens / L) for quantized tokens plus one for the KIVI
-// residual window (unused by the per-token formats).
-int32_t split_plan(const kvq_config* c, int32_t split_tokens, int* L, int* S) {
+// Automatic split count for a device that holds `resident` decode
+// workgroups at once: enough splits that the B * Hkv * n workgroups fill
+// about kRounds waves of residency, within [1, auto_split_bound()]. The
+// per-token formats stream at the memory bound, where one full round is
+// fastest (each further round adds a prologue and a tail); KIVI's decode is
+// bound by vector-ALU work, where about four rounds let workgroups in
+// different phases (loads, group folds, epilogue) share a compute unit.
+int auto_split(const kvq_config* c, int64_t resident) {
+  const int64_t rounds = c->format == KVQ_FMT_KIVI ? 4 : 1;
+  const int64_t pairs = int64_t(c->batch) * c->n_kv_heads;
+  int64_t n = rounds * resident / pairs;
+  const int bound = auto_split_bound(c);
+  if (n < 1) n = 1;
+  if (n > bound) n = bound;
+  return int(n);
+}
+
+// Quantized splits per sequence the workspace must hold: ceil(max_tokens /
+// split_tokens) for an explicit split length, auto_split_bound() for 0.
+int32_t split_bound(const kvq_config* c, int32_t split_tokens, int* n) {
   if (split_tokens < 0 || (split_tokens > 0 && split_tokens % 64 != 0)) return KVQ_ERR_UNSUPPORTED;
   if (split_tokens > (1 << 24)) return KVQ_ERR_UNSUPPORTED;
-  *L = split_tokens ? split_tokens : auto_split(c);
-  *S = (c->max_tokens + *L - 1) / *L + 1;
+  if (split_tokens == 0) {
+    *n = auto_split_bound(c);
+    return KVQ_OK;
+  }
+  const int64_t nsplit = (int64_t(c->max_tokens) + split_tokens - 1) / split_tokens;
+  if (nsplit > kvq::kMaxDecodeSplits) return KVQ_ERR_UNSUPPORTED;
+  *n = int(nsplit);
   return KVQ_OK;
 }
 
+// Workspace: [B][Hkv] uint32 arrival counters first (they must read zero on
+// entry; each call leaves them zero), then the partial states o, m, l.
+uint64_t counter_bytes(const kvq_config* c) { return align256(uint64_t(c->batch) * c->n_kv_heads * 4); }
+
 uint64_t workspace_bytes(const kvq_config* c, int S) {
   const uint64_t rows = uint64_t(c->batch) * c->n_q_heads * S;
-  return align256(rows * c->head_dim * 4) + align256(rows * 4) + align256(rows * 4);
+  return counter_bytes(c) + align256(rows * c->head_dim * 4) + align256(rows * 4) + align256(rows * 4);
 }
 
 }  // namespace
@@ -189,10 +211,10 @@ int32_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t split_tokens, 
   if (!bytes) return KVQ_ERR_INVALID;
   const int32_t st = validate(cfg);
   if (st != KVQ_OK) return st;
-  int L, S;
-  const int32_t sp = split_plan(cfg, split_tokens, &L, &S);
+  int n;
+  const int32_t sp = split_bound(cfg, split_tokens, &n);
   if (sp != KVQ_OK) return sp;
-  *bytes = workspace_bytes(cfg, S);
+  *bytes = workspace_bytes(cfg, n + 1);
   return KVQ_OK;
 }
 
@@ -206,21 +228,28 @@ int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache, const int
       (reinterpret_cast<uintptr_t>(seq_lens) & 3))
     return KVQ_ERR_INVALID;
   if (!(sm_scale == sm_scale) || sm_scale > 3.0e38f || sm_scale < -3.0e38f) return KVQ_ERR_INVALID;
-  int L, S;
-  const int32_t sp = split_plan(cfg, split_tokens, &L, &S);
+  int n;
+  const int32_t sp = split_bound(cfg, split_tokens, &n);
   if (sp != KVQ_OK) return sp;
-  if (ws_bytes < workspace_bytes(cfg, S)) return KVQ_ERR_WORKSPACE;
+  if (ws_bytes < workspace_bytes(cfg, n + 1)) return KVQ_ERR_WORKSPACE;
   kvq_layout lay;
   make_layout(cfg, &lay);
   const kvq::CacheView v = make_view(cfg, lay, cache);
+  if (split_tokens == 0) {
+    const int resident = kvq::decode_resident_workgroups(v);
+    if (resident <= 0) return KVQ_ERR_HIP;
+    n = auto_split(cfg, resident);
+  }
+  const int S = n + 1;
   const uint64_t rows = uint64_t(cfg->batch) * cfg->n_q_heads * S;
   uint8_t* w = static_cast<uint8_t*>(workspace);
   kvq::DecodeWork work;
+  work.count = reinterpret_cast<uint32_t*>(w);
+  w += counter_bytes(cfg);
   work.o = reinterpret_cast<float*>(w);
   work.m = reinterpret_cast<float*>(w + align256(rows * cfg->head_dim * 4));
   work.l = reinterpret_cast<float*>(w + align256(rows * cfg->head_dim * 4) + align256(rows * 4));
   work.S = S;
-  work.L = L;
   const hipError_t e = kvq::launch_decode(v, seq_lens, q, sm_scale, out, work, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }

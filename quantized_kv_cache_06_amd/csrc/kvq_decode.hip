@@ -38,9 +38,13 @@
 //
 // KIVI residual tokens (full precision, fewer than R + G per sequence) are
 // handled by one extra workgroup per (kv head, sequence) on the vector ALU,
-// writing the last partial slot. decode_merge then combines, per (query head,
-// sequence), every partial by the log-sum-exp rule and normalizes.
+// writing the last partial slot. The workgroup of a (sequence, kv head) that
+// finishes last (an arrival counter in the workspace) combines every partial
+// by the log-sum-exp rule and writes the normalized output: one launch per
+// call.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "kvq_device.h"
 
@@ -51,8 +55,25 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kTile = 32;        // tokens per wave iteration (two 16-token score tiles)
 constexpr int kResidChunk = 256; // tokens per residual chunk (one per thread)
+constexpr int kMaxSplits = kMaxDecodeSplits;  // quantized splits per sequence (S - 1 <= this)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr uint32_t kMagic128 = 0x43004300u;  // two bf16 128.0
+// Tuning knobs (compile-time; the defaults are the measured best on MI355X):
+// non-temporal loads for the streamed cache codes, the 64-byte Key pieces of
+// 8-bit codes at d = 128, and the prefetch ring depth.
+#ifndef KVQ_DECODE_NT
+#define KVQ_DECODE_NT 0
+#endif
+#ifndef KVQ_DECODE_KSPLIT
+#define KVQ_DECODE_KSPLIT 1
+#endif
+#ifndef KVQ_DECODE_INTERLEAVE
+#define KVQ_DECODE_INTERLEAVE 1
+#endif
+#ifndef KVQ_DECODE_NPF
+#define KVQ_DECODE_NPF 2
+#endif
+constexpr bool kStreamNT = KVQ_DECODE_NT != 0;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -140,6 +161,19 @@ __device__ __forceinline__ uint32_t byte_pair_bf16(uint32_t w) {
   else return i8x2_bf16<SEL>(w);
 }
 
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 (unrolled).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for_impl(F& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_impl<I + 1, N>(f);
+  }
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<0, N>(f);
+}
+
 // ---------------------------------------------------------------------------
 // Index maps shared by the loads and the operands (see the file header).
 //
@@ -161,22 +195,28 @@ __device__ __forceinline__ constexpr int tok(int t, int r, int j) {
   else return 8 * r + 4 * t + j;
 }
 
-// Loads of NB bytes (4, 8, 16 or 32) into dwords.
-template <int NB>
+// Loads of NB bytes (4, 8, 16 or 32) into dwords. NT marks the load
+// non-temporal (streamed once: the cache codes of a decode call).
+template <typename V, bool NT>
+__device__ __forceinline__ V load_vec(const uint8_t* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+  else return *reinterpret_cast<const V*>(p);
+}
+template <int NB, bool NT = false>
 __device__ __forceinline__ void load_bytes(const uint8_t* p, uint32_t* w) {
   if constexpr (NB == 32) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(p);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(p + 16);
+    const u32x4 a = load_vec<u32x4, NT>(p);
+    const u32x4 b = load_vec<u32x4, NT>(p + 16);
     w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
     w[4] = b[0]; w[5] = b[1]; w[6] = b[2]; w[7] = b[3];
   } else if constexpr (NB == 16) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+    const u32x4 a = load_vec<u32x4, NT>(p);
     w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
   } else if constexpr (NB == 8) {
-    const u32x2 a = *reinterpret_cast<const u32x2*>(p);
+    const u32x2 a = load_vec<u32x2, NT>(p);
     w[0] = a[0]; w[1] = a[1];
   } else {
-    w[0] = *reinterpret_cast<const uint32_t*>(p);
+    w[0] = load_vec<uint32_t, NT>(p);
   }
 }
 
@@ -358,9 +398,15 @@ struct SmemResid {
   float st_m[8], st_l[8], st_a[8];
 };
 template <int D>
-constexpr size_t smem_floats() {
+constexpr size_t smem_floats_split() {
   return (sizeof(SmemQuant<D>) > sizeof(SmemResid<D>) ? sizeof(SmemQuant<D>) : sizeof(SmemResid<D>)) /
          sizeof(float);
+}
+// ... and the merge's (max, sum) table of up to 8 heads x (kMaxSplits + 1) slots
+template <int D>
+constexpr size_t smem_floats() {
+  constexpr size_t merge = 2 * 8 * (kMaxSplits + 1) + 8;
+  return smem_floats_split<D>() > merge ? smem_floats_split<D>() : merge;
 }
 
 // Row of one partial state (unnormalized output, log2-domain maximum and
@@ -368,6 +414,16 @@ constexpr size_t smem_floats() {
 __device__ __forceinline__ size_t partial_row(const CacheView& cv, const DecodeWork& wk, int b, int h, int j,
                                               int s) {
   return (size_t(b) * cv.Hq + size_t(h) * cv.g + j) * wk.S + s;
+}
+
+// Partial states cross workgroups (and XCDs) inside one launch: they are
+// written and read as relaxed device-scope atomics, which the compiler emits
+// as plain coherent (sc1) stores and loads with no cache write-back.
+__device__ __forceinline__ void put_partial(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float get_partial(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Orders this wave's LDS writes before its later LDS reads by other lanes.
@@ -391,6 +447,11 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
                                                 SmemQuant<D>& sm) {
   constexpr bool KIVI = FMT == KVQ_FMT_KIVI;
   constexpr int CPL = D / 4;                  // channels per row group (score MFMA)
+  // 8-bit codes at d = 128: row group r holds channels [16r, 16r+16) and
+  // [64+16r, 64+16r+16), so each Key load instruction covers 64 contiguous
+  // bytes of every row it touches (elements 8kk + i of the lane's 32 keep
+  // their order: k-steps 0-1 take the first piece, 2-3 the second)
+  constexpr bool KSPLIT = KVQ_DECODE_KSPLIT != 0 && BITS == 8 && D == 128;
   constexpr int NKK = D / 32;                 // k-steps of the score MFMA
   constexpr int NMT = D / 16;                 // channel tiles of the value MFMA
   constexpr int KB = D * BITS / 8;            // bytes per Key row
@@ -402,6 +463,7 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   constexpr int NVG = KIVI ? D / (G > 0 ? G : 1) : 1;  // Value channel groups
   constexpr int MPG = KIVI ? G / 16 : NMT;    // channel tiles per Value channel group
   constexpr int KGL = D / 32;                 // Key group floats per lane (lanes 0-31 scale, 32-63 zero)
+  constexpr int NPF = (KIVI && G == 32 && KVQ_DECODE_NPF > 2) ? 2 : KVQ_DECODE_NPF;  // ring slots (register budget)
   static_assert(KGL == 2 || KGL == 4, "group load width");
 
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
@@ -411,41 +473,29 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   const int g = cv.g;
   const size_t pair = pair_index(cv, b, h);
 
-  // ---- query: per-token formats build the operand once; KIVI stages q ----
-  // (vector loads of a clamped head; heads beyond the GQA group read as 0)
-  u32x4 bq[NKK];
-  if constexpr (KIVI) {
-    constexpr int EPT = 8 * D / kThreads;  // 4 (D = 128) or 2 (D = 64) elements per thread
-    const int e0 = tid * EPT, j = e0 / D, c = e0 % D;
-    const size_t qi = (size_t(b) * cv.Hq + size_t(h) * g + min(j, g - 1)) * D + c;
-    float x[EPT];
-    load_elems<BF16, EPT>(q, qi, x);
-#pragma unroll
-    for (int i = 0; i < EPT; ++i) sm.q[j][c + i] = j < g ? x[i] : 0.0f;
-    __syncthreads();
-  } else {
-    const size_t qrow = (size_t(b) * cv.Hq + size_t(h) * g + min(hh, g - 1)) * D + CPL * r;
-    float x[CPL];
-    load_elems<BF16, CPL>(q, qrow, x);
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x0 = hh < g ? x[cperm<BITS>(kk, 2 * e)] : 0.0f;
-        const float x1 = hh < g ? x[cperm<BITS>(kk, 2 * e + 1)] : 0.0f;
-        const Split2 sp = split_pair(x0, x1);
-        bq[kk][e] = lo_col ? sp.lo : sp.hi;
-      }
-    }
-  }
-
-  // ---- this wave's contiguous run of tiles (whole KIVI groups) ----
+  // ---- this wave's tiles (whole KIVI groups) ----
   const int ntile = (t1 - t0 + kTile - 1) / kTile;
   constexpr int GG = KIVI ? G : kTile;         // group size (KIVI), else a harmless divisor
   constexpr int TPG = GG / kTile;
-  int tpw = (ntile + kWaves - 1) / kWaves;
-  tpw = (tpw + TPG - 1) / TPG * TPG;
-  const int ta = min(wave * tpw, ntile), tb = min(ta + tpw, ntile);
+  // Work units of TPG tiles (one KIVI group, else one tile). With
+  // KVQ_DECODE_INTERLEAVE the 4 waves take units round-robin (the workgroup
+  // sweeps one contiguous region); otherwise each wave takes a contiguous
+  // quarter. tile_of(k) is the k-th tile (0 <= k < nk) of this wave.
+  const int nunit = (ntile + TPG - 1) / TPG;
+  int nk, ua;
+  if constexpr (KVQ_DECODE_INTERLEAVE != 0) {
+    nk = wave < nunit ? (nunit - wave + kWaves - 1) / kWaves * TPG : 0;
+    ua = wave;
+  } else {
+    const int upw = (nunit + kWaves - 1) / kWaves;
+    ua = min(wave * upw, nunit);
+    nk = (min(ua + upw, nunit) - ua) * TPG;
+  }
+  nk = min(nk, ntile - ua * TPG);  // a partial last unit (per-token formats have TPG = 1)
+  auto tile_of = [&](int k) {
+    if constexpr (KVQ_DECODE_INTERLEAVE != 0) return (ua + kWaves * (k / TPG)) * TPG + k % TPG;
+    else return ua * TPG + k;
+  };
 
   float m_run = -INFINITY, l_run = 0.0f;
   f32x4 o[NMT];
@@ -461,77 +511,129 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   for (int j = 0; j < NVG; ++j) zb[j] = 0.0f;
   float kbias = 0.0f, kscale = 1.0f;
 
-  const uint8_t* kbase = cv.k_codes + pair * size_t(cv.cap) * KB + LKB * r;
+  const uint8_t* kbase = cv.k_codes + pair * size_t(cv.cap) * KB + (KSPLIT ? 16 * r : LKB * r);
   const uint8_t* vbase = cv.v_codes + pair * size_t(cv.cap / TB) * D * VWB;
   float* meta0 = sm.meta[wave][0];
   float* meta1 = sm.meta[wave][1];
 
-  // prefetch registers: codes, tile metadata, Key group parameters
-  uint32_t kw[2][LKB / 4], vw[NVL * 4];
-  float mw[NVG], gw[KGL];
-  auto load_tile = [&](int T0, bool new_group) {
+  // Prefetch ring of NPF tile slots (codes, tile metadata, Key group
+  // parameters). Slot u holds the wave's tiles u, u + NPF, ...; a slot is refilled with the
+  // tile NPF ahead as soon as its tile is consumed, so NPF - 1 tiles are in
+  // flight while one is computed. Slot indices are compile-time (the loop
+  // over a round of NPF tiles is unrolled), so the ring lives in registers.
+  struct Slot {
+    uint32_t kw[2][LKB / 4], vw[NVL * 4];
+    float mw[NVG], gw[KGL];
+  };
+  Slot ring[NPF];
+  // Loads are issued unconditionally (a tile index past the wave's run is
+  // clamped to its last tile, whose bytes are then re-read from cache) so
+  // that the number of loads in flight does not depend on the path taken and
+  // the waits before each slot's use stay exact.
+  auto load_tile = [&](Slot& sl, int ti) {
+    const int T0 = t0 + tile_of(min(ti, nk - 1)) * kTile;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) load_bytes<LKB>(kbase + size_t(T0 + tok<BITS>(t, m >> 2, m & 3)) * KB, kw[t]);
+    for (int t = 0; t < 2; ++t) {
+      const uint8_t* row = kbase + size_t(T0 + tok<BITS>(t, m >> 2, m & 3)) * KB;
+      if constexpr (KSPLIT) {
+        load_bytes<16, kStreamNT>(row, sl.kw[t]);
+        load_bytes<16, kStreamNT>(row + 64, sl.kw[t] + 4);
+      } else {
+        load_bytes<LKB, kStreamNT>(row, sl.kw[t]);
+      }
+    }
     const int blk = T0 / TB + (BITS == 2 ? (r >> 1) : r);
     const uint8_t* vb = vbase + (size_t(blk) * D + VW * m) * VWB;
 #pragma unroll
-    for (int p = 0; p < NVL; ++p) load_bytes<16>(vb + size_t(p) * 16 * VW * VWB, vw + 4 * p);
+    for (int p = 0; p < NVL; ++p) load_bytes<16, kStreamNT>(vb + size_t(p) * 16 * VW * VWB, sl.vw + 4 * p);
     // metadata: lanes 0-31 the Key (or Value scale) half, lanes 32-63 the
     // Value (or Value zero) half, NVG floats per lane
     const int part = lane >> 5, qi = lane & 31;
     if constexpr (!KIVI) {
-      mw[0] = (part ? cv.v_scale : cv.k_scale)[pair * cv.cap + T0 + qi];
+      sl.mw[0] = (part ? cv.v_scale : cv.k_scale)[pair * cv.cap + T0 + qi];
     } else {
       const float* src = (part ? cv.v_zero : cv.v_scale) + (pair * cv.cap + T0 + qi) * NVG;
       if constexpr (NVG == 4) {
         const f32x4 x = *reinterpret_cast<const f32x4*>(src);
-        mw[0] = x[0]; mw[1] = x[1]; mw[2] = x[2]; mw[3] = x[3];
+        sl.mw[0] = x[0]; sl.mw[1] = x[1]; sl.mw[2] = x[2]; sl.mw[3] = x[3];
       } else if constexpr (NVG == 2) {
         const f32x2 x = *reinterpret_cast<const f32x2*>(src);
-        mw[0] = x[0]; mw[1] = x[1];
+        sl.mw[0] = x[0]; sl.mw[1] = x[1];
       } else {
-        mw[0] = src[0];
+        sl.mw[0] = src[0];
       }
-      if (new_group) {
-        const float* gsrc = (part ? cv.k_zero : cv.k_scale) + (pair * (cv.cap / GG) + T0 / GG) * D + qi * KGL;
-        if constexpr (KGL == 4) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(gsrc);
-          gw[0] = x[0]; gw[1] = x[1]; gw[2] = x[2]; gw[3] = x[3];
-        } else {
-          const f32x2 x = *reinterpret_cast<const f32x2*>(gsrc);
-          gw[0] = x[0]; gw[1] = x[1];
-        }
+      // the group parameters of the tile's group (used when it opens one)
+      const float* gsrc = (part ? cv.k_zero : cv.k_scale) + (pair * (cv.cap / GG) + T0 / GG) * D + qi * KGL;
+      if constexpr (KGL == 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(gsrc);
+        sl.gw[0] = x[0]; sl.gw[1] = x[1]; sl.gw[2] = x[2]; sl.gw[3] = x[3];
+      } else {
+        const f32x2 x = *reinterpret_cast<const f32x2*>(gsrc);
+        sl.gw[0] = x[0]; sl.gw[1] = x[1];
       }
     }
   };
-  auto opens_group = [&](int ti) { return KIVI && (ti == ta || ((t0 + ti * kTile) % GG) == 0); };
+  auto opens_group = [&](int k) { return KIVI && (k % TPG) == 0; };
 
-  if (ta < tb) load_tile(t0 + ta * kTile, opens_group(ta));
-  for (int ti = ta; ti < tb; ++ti) {
-    const int T0 = t0 + ti * kTile;
+  // ---- query, part 1: issue its loads (a clamped head; heads beyond the
+  // GQA group read as 0). They go out before the first tiles' loads, so the
+  // operand is built below while those tiles are in flight.
+  u32x4 bq[NKK];
+  constexpr int EPT = 8 * D / kThreads;  // KIVI: 4 (D = 128) or 2 (D = 64) elements per thread
+  constexpr int NQX = KIVI ? EPT : CPL;
+  float qx[NQX];
+  if constexpr (KIVI) {
+    const int e0 = tid * EPT, j = e0 / D, c = e0 % D;
+    load_elems<BF16, EPT>(q, (size_t(b) * cv.Hq + size_t(h) * g + min(j, g - 1)) * D + c, qx);
+  } else {
+    const size_t qrow = (size_t(b) * cv.Hq + size_t(h) * g + min(hh, g - 1)) * D;
+    if constexpr (KSPLIT) {
+      load_elems<BF16, CPL / 2>(q, qrow + 16 * r, qx);
+      load_elems<BF16, CPL / 2>(q, qrow + 64 + 16 * r, qx + CPL / 2);
+    } else {
+      load_elems<BF16, CPL>(q, qrow + CPL * r, qx);
+    }
+  }
+  if (nk > 0) static_for<NPF>([&](auto uc) { load_tile(ring[decltype(uc)::value], decltype(uc)::value); });
+
+  // ---- query, part 2: KIVI stages q in LDS; the others build the operand
+  if constexpr (KIVI) {
+    const int e0 = tid * EPT, j = e0 / D, c = e0 % D;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) sm.q[j][c + i] = j < g ? qx[i] : 0.0f;
+    __syncthreads();
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = hh < g ? qx[cperm<BITS>(kk, 2 * e)] : 0.0f;
+        const float x1 = hh < g ? qx[cperm<BITS>(kk, 2 * e + 1)] : 0.0f;
+        const Split2 sp = split_pair(x0, x1);
+        bq[kk][e] = lo_col ? sp.lo : sp.hi;
+      }
+    }
+  }
+
+  auto process = [&](Slot& sl, int ti) {
+    const int T0 = t0 + tile_of(ti) * kTile;
     const bool grp_open = opens_group(ti);
-    uint32_t kc[2][LKB / 4], vc[NVL * 4];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < LKB / 4; ++i) kc[t][i] = kw[t][i];
-#pragma unroll
-    for (int i = 0; i < NVL * 4; ++i) vc[i] = vw[i];
+    const uint32_t (&kc)[2][LKB / 4] = sl.kw;
+    const uint32_t* vc = sl.vw;
     {
       const int part = lane >> 5, qi = lane & 31;
       float* mdst = (part ? meta1 : meta0) + qi * NVG;
 #pragma unroll
-      for (int j = 0; j < NVG; ++j) mdst[j] = mw[j];
+      for (int j = 0; j < NVG; ++j) mdst[j] = sl.mw[j];
       if constexpr (KIVI) {
         if (grp_open) {
           float* gdst = sm.kgrp[wave][part] + qi * KGL;
 #pragma unroll
-          for (int j = 0; j < KGL; ++j) gdst[j] = gw[j];
+          for (int j = 0; j < KGL; ++j) gdst[j] = sl.gw[j];
         }
       }
     }
     wave_lds_sync();
-    if (ti + 1 < tb) load_tile(T0 + kTile, opens_group(ti + 1));  // prefetch the next tile
 
     // ---- KIVI: fold this group's per-channel Key scales into the query ----
     // x_c = q_c * s_c is scaled by 2^ke (per head) so its largest magnitude
@@ -701,6 +803,17 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
       }
     }
     wave_lds_sync();  // metadata reads done before the next tile overwrites it
+  };
+
+  if (nk > 0) {
+    for (int base = 0; base < nk; base += NPF) {
+      static_for<NPF>([&](auto uc) {
+        constexpr int U = decltype(uc)::value;
+        const int ti = base + U;
+        if (ti < nk) process(ring[U], ti);
+        load_tile(ring[U], ti + NPF);
+      });
+    }
   }
 
   // ---- merge the 4 waves through LDS ----
@@ -737,10 +850,10 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
       }
     }
     const size_t row = partial_row(cv, wk, b, h, j, s);
-    wk.o[row * D + c] = ov;
+    put_partial(&wk.o[row * D + c], ov);
     if (c == 0) {
-      wk.m[row] = M;
-      wk.l[row] = L;
+      put_partial(&wk.m[row], M);
+      put_partial(&wk.l[row], L);
     }
   }
 }
@@ -828,107 +941,155 @@ __device__ __forceinline__ void split_residual(const CacheView& cv, int b, int h
       float o = 0.0f;
 #pragma unroll
       for (int p = 0; p < P; ++p) o += red[(p * NH + j) * D + c];
-      wk.o[partial_row(cv, wk, b, h, j, s) * D + c] = o;
+      put_partial(&wk.o[partial_row(cv, wk, b, h, j, s) * D + c], o);
     }
   }
   if (tid < g) {
     const size_t row = partial_row(cv, wk, b, h, tid, s);
-    wk.m[row] = sm.st_m[tid];
-    wk.l[row] = sm.st_l[tid];
+    put_partial(&wk.m[row], sm.st_m[tid]);
+    put_partial(&wk.l[row], sm.st_l[tid]);
   }
 }
 
 // Grid (S, Hkv, B). Slot s < S-1 covers quantized tokens [s*L, (s+1)*L);
-// slot S-1 covers the KIVI residual ring. Slots with no tokens return
-// without writing (the merge does not read them).
+// slot S-1 covers the KIVI residual ring. A workgroup whose slot holds
+// tokens writes its partial state and takes a ticket from the (sequence, kv
+// head) counter; the workgroup that finishes last merges every partial of the
+// g query heads by the log-sum-exp rule, writes the normalized output and
+// resets the counter to zero. Slots with no tokens return at once; an empty
+// sequence gets zeros from slot 0.
 template <int FMT, int BITS, int D, int G, bool BF16>
 __global__ __launch_bounds__(kThreads) void decode_split(CacheView cv, const int32_t* __restrict__ seq_lens,
-                                                        const void* __restrict__ q, float sm_log2, DecodeWork wk) {
+                                                        const void* __restrict__ q, float sm_log2, float* __restrict__ out,
+                                                        DecodeWork wk) {
   constexpr bool KIVI = FMT == KVQ_FMT_KIVI;
   __shared__ float smem[smem_floats<D>()];
+  __shared__ uint32_t ticket;
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int g = cv.g;
   const int n = min(max(seq_lens[b], 0), cv.max_tokens);
   const int nq = KIVI ? kivi_quantized(n, G, cv.R) : n;
-  if (s == wk.S - 1) {
-    if constexpr (KIVI) {
-      if (n > nq) split_residual<D, BF16>(cv, b, h, s, nq, n, q, sm_log2, wk, *reinterpret_cast<SmemResid<D>*>(smem));
-    }
+  // This sequence's quantized tokens spread evenly over the S - 1 split
+  // slots, in whole tiles (whole groups for KIVI, so that a Key group never
+  // straddles two splits).
+  constexpr int kUnit = KIVI ? G : kTile;
+  const int per = (nq + wk.S - 2) / (wk.S - 1);
+  const int len = (per + kUnit - 1) / kUnit * kUnit;
+  const int nsq = len > 0 ? (nq + len - 1) / len : 0;
+  const bool resid = KIVI && n > nq;
+  const int nact = nsq + (resid ? 1 : 0);
+  if (nact == 0) {
+    if (s == 0)
+      for (int e = tid; e < g * D; e += kThreads) out[(size_t(b) * cv.Hq + size_t(h) * g) * D + e] = 0.0f;
     return;
   }
-  const int t0 = s * wk.L;
-  if (t0 >= nq) return;
-  const int t1 = min(t0 + wk.L, nq);
-  split_quantized<FMT, BITS, D, G, BF16>(cv, b, h, s, t0, t1, q, sm_log2, wk, *reinterpret_cast<SmemQuant<D>*>(smem));
-}
-
-// One workgroup (D threads) per (query head, sequence): log-sum-exp merge of
-// the partial states that hold tokens, then normalization.
-template <bool KIVI>
-__global__ void decode_merge(CacheView cv, const int32_t* __restrict__ seq_lens, float* __restrict__ out,
-                             DecodeWork wk) {
-  const int hq = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
-  const int n = min(max(seq_lens[b], 0), cv.max_tokens);
-  const int nq = KIVI ? kivi_quantized(n, cv.G, cv.R) : n;
-  const int nsq = (nq + wk.L - 1) / wk.L;
-  const bool resid = KIVI && n > nq;
-  const size_t row = (size_t(b) * cv.Hq + hq) * wk.S;
-  float M = -INFINITY;
-  for (int s = 0; s < nsq; ++s) M = fmaxf(M, wk.m[row + s]);
-  if (resid) M = fmaxf(M, wk.m[row + wk.S - 1]);
-  float o = 0.0f;
-  if (M != -INFINITY) {
-    float lsum = 0.0f, acc = 0.0f;
-    for (int s = 0; s < nsq; ++s) {
-      const float w = __builtin_amdgcn_exp2f(wk.m[row + s] - M);
-      lsum = fmaf(wk.l[row + s], w, lsum);
-      acc = fmaf(wk.o[(row + s) * cv.D + c], w, acc);
+  if (s == wk.S - 1) {
+    if constexpr (KIVI) {
+      if (!resid) return;
+      split_residual<D, BF16>(cv, b, h, s, nq, n, q, sm_log2, wk, *reinterpret_cast<SmemResid<D>*>(smem));
+    } else {
+      return;
     }
-    if (resid) {
-      const size_t rs = row + wk.S - 1;
-      const float w = __builtin_amdgcn_exp2f(wk.m[rs] - M);
-      lsum = fmaf(wk.l[rs], w, lsum);
-      acc = fmaf(wk.o[rs * cv.D + c], w, acc);
-    }
-    o = acc / lsum;
-  }
-  out[(size_t(b) * cv.Hq + hq) * cv.D + c] = o;
-}
-
-template <int FMT, int BITS, int D, int G, bool BF16>
-void launch_split(const CacheView& cv, const int32_t* sl, const void* q, float sm, const DecodeWork& wk,
-                  hipStream_t st) {
-  const dim3 grid(wk.S, cv.Hkv, cv.B);
-  decode_split<FMT, BITS, D, G, BF16><<<grid, kThreads, 0, st>>>(cv, sl, q, sm, wk);
-}
-
-template <int FMT, int BITS, int D, bool BF16>
-void launch_split_g(const CacheView& cv, const int32_t* sl, const void* q, float sm, const DecodeWork& wk,
-                    hipStream_t st) {
-  if constexpr (FMT == KVQ_FMT_KIVI) {
-    if (cv.G == 32) launch_split<FMT, BITS, D, 32, BF16>(cv, sl, q, sm, wk, st);
-    else launch_split<FMT, BITS, D, 64, BF16>(cv, sl, q, sm, wk, st);
   } else {
-    launch_split<FMT, BITS, D, 0, BF16>(cv, sl, q, sm, wk, st);
+    if (s >= nsq) return;
+    const int t0 = s * len;
+    const int t1 = min(t0 + len, nq);
+    split_quantized<FMT, BITS, D, G, BF16>(cv, b, h, s, t0, t1, q, sm_log2, wk,
+                                           *reinterpret_cast<SmemQuant<D>*>(smem));
+  }
+
+  // ---- arrival: the last workgroup of this (sequence, kv head) merges ----
+  const size_t pair = pair_index(cv, b, h);
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed ...
+  __syncthreads();                 // ... for every thread, before the ticket is taken
+  if (tid == 0) ticket = __hip_atomic_fetch_add(&wk.count[pair], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (ticket != uint32_t(nact - 1)) return;
+
+  // Merge: gather every split's (max, sum) of the g heads into LDS with one
+  // parallel batch of loads, turn them into weights exp2(m - M) and 1 / L per
+  // head, then sum the weighted partial outputs eight splits at a time.
+  // nact <= kMaxSplits + 1 (the host caps the split count).
+  float* wgt = smem;                     // [g][nact] maxima, then weights
+  float* lsm = smem + 8 * (kMaxSplits + 1);  // [g][nact] sums
+  float* inv = lsm + 8 * (kMaxSplits + 1);   // [g] 1 / L
+  auto slot = [&](int k) { return k < nsq ? k : wk.S - 1; };
+  for (int e = tid; e < g * nact; e += kThreads) {
+    const int j = e / nact, k = e % nact;
+    const size_t r = (size_t(b) * cv.Hq + size_t(h) * g + j) * wk.S + slot(k);
+    wgt[e] = get_partial(&wk.m[r]);
+    lsm[e] = get_partial(&wk.l[r]);
+  }
+  __syncthreads();
+  if (tid < g) {
+    float M = -INFINITY;
+    for (int k = 0; k < nact; ++k) M = fmaxf(M, wgt[tid * nact + k]);
+    float L = 0.0f;
+    for (int k = 0; k < nact; ++k) {
+      const float w = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(wgt[tid * nact + k] - M);
+      wgt[tid * nact + k] = w;
+      L = fmaf(lsm[tid * nact + k], w, L);
+    }
+    inv[tid] = L > 0.0f ? 1.0f / L : 0.0f;
+  }
+  __syncthreads();
+  for (int e = tid; e < g * D; e += kThreads) {
+    const int j = e / D, c = e % D;
+    const size_t row = (size_t(b) * cv.Hq + size_t(h) * g + j) * wk.S;
+    float acc = 0.0f;
+    for (int k0 = 0; k0 < nact; k0 += 8) {
+      float ov[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) ov[u] = get_partial(&wk.o[(row + slot(min(k0 + u, nact - 1))) * D + c]);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (k0 + u < nact) acc = fmaf(ov[u], wgt[j * nact + k0 + u], acc);
+    }
+    out[(size_t(b) * cv.Hq + size_t(h) * g + j) * D + c] = acc * inv[j];
+  }
+  if (tid == 0) __hip_atomic_store(&wk.count[pair], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One kernel instantiation per (format, bits, head_dim, group, input type).
+template <int FMT_, int BITS_, int D_, int G_, bool BF16_>
+struct Variant {
+  static constexpr int FMT = FMT_, BITS = BITS_, D = D_, G = G_;
+  static constexpr bool BF16 = BF16_;
+};
+
+template <int FMT, int BITS, int D, bool BF16, class F>
+void visit_g(const CacheView& cv, F&& f) {
+  if constexpr (FMT == KVQ_FMT_KIVI) {
+    if (cv.G == 32) f(Variant<FMT, BITS, D, 32, BF16>{});
+    else f(Variant<FMT, BITS, D, 64, BF16>{});
+  } else {
+    f(Variant<FMT, BITS, D, 0, BF16>{});
   }
 }
 
-template <int FMT, int BITS, bool BF16>
-void launch_split_d(const CacheView& cv, const int32_t* sl, const void* q, float sm, const DecodeWork& wk,
-                    hipStream_t st) {
-  if (cv.D == 128) launch_split_g<FMT, BITS, 128, BF16>(cv, sl, q, sm, wk, st);
-  else launch_split_g<FMT, BITS, 64, BF16>(cv, sl, q, sm, wk, st);
+template <int FMT, int BITS, bool BF16, class F>
+void visit_d(const CacheView& cv, F&& f) {
+  if (cv.D == 128) visit_g<FMT, BITS, 128, BF16>(cv, f);
+  else visit_g<FMT, BITS, 64, BF16>(cv, f);
 }
 
-template <bool BF16>
-void launch_split_fmt(const CacheView& cv, const int32_t* sl, const void* q, float sm, const DecodeWork& wk,
-                      hipStream_t st) {
+template <bool BF16, class F>
+void visit_fmt(const CacheView& cv, F&& f) {
   switch (cv.fmt) {
-    case KVQ_FMT_FP8_E4M3: launch_split_d<KVQ_FMT_FP8_E4M3, 8, BF16>(cv, sl, q, sm, wk, st); break;
-    case KVQ_FMT_INT8: launch_split_d<KVQ_FMT_INT8, 8, BF16>(cv, sl, q, sm, wk, st); break;
+    case KVQ_FMT_FP8_E4M3: visit_d<KVQ_FMT_FP8_E4M3, 8, BF16>(cv, f); break;
+    case KVQ_FMT_INT8: visit_d<KVQ_FMT_INT8, 8, BF16>(cv, f); break;
     default:
-      if (cv.bits == 4) launch_split_d<KVQ_FMT_KIVI, 4, BF16>(cv, sl, q, sm, wk, st);
-      else launch_split_d<KVQ_FMT_KIVI, 2, BF16>(cv, sl, q, sm, wk, st);
+      if (cv.bits == 4) visit_d<KVQ_FMT_KIVI, 4, BF16>(cv, f);
+      else visit_d<KVQ_FMT_KIVI, 2, BF16>(cv, f);
   }
+}
+
+// Calls f(Variant<...>{}) for the kernel instantiation that serves cv.
+template <class F>
+void visit_variant(const CacheView& cv, F&& f) {
+  if (cv.bf16) visit_fmt<true>(cv, f);
+  else visit_fmt<false>(cv, f);
 }
 
 }  // namespace
@@ -936,12 +1097,28 @@ void launch_split_fmt(const CacheView& cv, const int32_t* sl, const void* q, flo
 hipError_t launch_decode(const CacheView& cv, const int32_t* seq_lens, const void* q, float sm_scale, float* out,
                          const DecodeWork& work, hipStream_t stream) {
   const float sm_log2 = sm_scale * kLog2e;
-  if (cv.bf16) launch_split_fmt<true>(cv, seq_lens, q, sm_log2, work, stream);
-  else launch_split_fmt<false>(cv, seq_lens, q, sm_log2, work, stream);
-  const dim3 mgrid(cv.Hq, cv.B);
-  if (cv.fmt == KVQ_FMT_KIVI) decode_merge<true><<<mgrid, cv.D, 0, stream>>>(cv, seq_lens, out, work);
-  else decode_merge<false><<<mgrid, cv.D, 0, stream>>>(cv, seq_lens, out, work);
+  visit_variant(cv, [&](auto v) {
+    using V = decltype(v);
+    // the residual slot S-1 exists only for KIVI
+    const dim3 grid(V::FMT == KVQ_FMT_KIVI ? work.S : work.S - 1, cv.Hkv, cv.B);
+    decode_split<V::FMT, V::BITS, V::D, V::G, V::BF16><<<grid, kThreads, 0, stream>>>(cv, seq_lens, q, sm_log2, out,
+                                                                                       work);
+  });
   return hipGetLastError();
+}
+
+int decode_resident_workgroups(const CacheView& cv) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  hipError_t e = hipSuccess;
+  visit_variant(cv, [&](auto v) {
+    using V = decltype(v);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split<V::FMT, V::BITS, V::D, V::G, V::BF16>,
+                                                     kThreads, 0);
+  });
+  if (e != hipSuccess) return 0;
+  return cus * per_cu;
 }
 
 }  // namespace kvq

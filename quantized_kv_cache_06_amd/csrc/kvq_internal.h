@@ -33,12 +33,16 @@ struct CacheView {
 };
 
 // Decode workspace split into its three arrays.
+// Most quantized splits per sequence a decode call may use (the merge keeps
+// every split's running max and sum of up to 8 heads in LDS).
+constexpr int kMaxDecodeSplits = 128;
+
 struct DecodeWork {
-  float* o;   // [B][Hq][S][D] unnormalized partial outputs
-  float* m;   // [B][Hq][S] running maxima
-  float* l;   // [B][Hq][S] running sums
-  int S;      // split slots per (b, q head)
-  int L;      // tokens per split
+  uint32_t* count;  // [B][Hkv] partials finished in this call (zero between calls)
+  float* o;         // [B][Hq][S][D] unnormalized partial outputs
+  float* m;         // [B][Hq][S] running maxima (log2 domain)
+  float* l;         // [B][Hq][S] running sums
+  int S;            // split slots per (b, q head): S - 1 quantized splits + 1
 };
 
 hipError_t launch_append(const CacheView& cv, int32_t* seq_lens, const void* k_new,
@@ -46,5 +50,9 @@ hipError_t launch_append(const CacheView& cv, int32_t* seq_lens, const void* k_n
 
 hipError_t launch_decode(const CacheView& cv, const int32_t* seq_lens, const void* q,
                          float sm_scale, float* out, const DecodeWork& work, hipStream_t stream);
+
+// Decode workgroups the current device holds at once (compute units times
+// the kernel's occupancy per unit); 0 when it cannot be queried.
+int decode_resident_workgroups(const CacheView& cv);
 
 }  // namespace kvq

@@ -28,7 +28,8 @@ class GpuCache:
         self.buf = torch.zeros(self.layout.total_bytes, dtype=torch.uint8, device=device)
         self.seq_lens = torch.zeros(cfg.batch, dtype=torch.int32, device=device)
         self.split_tokens = split_tokens
-        self.ws = torch.empty(kvq.kvq_decode_workspace_bytes(cfg, split_tokens), dtype=torch.uint8,
+        # zero-filled: the workspace's arrival counters must start at zero
+        self.ws = torch.zeros(kvq.kvq_decode_workspace_bytes(cfg, split_tokens), dtype=torch.uint8,
                               device=device)
 
     def append(self, k, v, append_lens=None):
@@ -38,7 +39,7 @@ class GpuCache:
 
     def decode(self, q, sm_scale, split_tokens=None):
         st = self.split_tokens if split_tokens is None else split_tokens
-        ws = self.ws if st == self.split_tokens else torch.empty(
+        ws = self.ws if st == self.split_tokens else torch.zeros(
             kvq.kvq_decode_workspace_bytes(self.cfg, st), dtype=torch.uint8, device=self.buf.device)
         out = torch.empty((self.cfg.batch, self.cfg.n_q_heads, self.cfg.head_dim), dtype=torch.float32,
                           device=self.buf.device)

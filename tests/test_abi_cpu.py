@@ -150,12 +150,30 @@ def test_decode_argument_errors_need_no_gpu():
 
 
 def test_workspace_grows_with_split_count():
+    """Workspace = [B][Hkv] uint32 arrival counters, then partial (o, m, l)
+    rows for every split slot; at most 128 quantized splits per sequence."""
     cfg = _cfg(WORKLOADS[4])
     small = kvq.kvq_decode_workspace_bytes(cfg, 4096)
-    big = kvq.kvq_decode_workspace_bytes(cfg, 64)
+    big = kvq.kvq_decode_workspace_bytes(cfg, 512)
     assert big > small > 0
-    rows = cfg.batch * cfg.n_q_heads * (cfg.max_tokens // 64 + 1)
-    assert big >= rows * (cfg.head_dim + 2) * 4
+    rows = cfg.batch * cfg.n_q_heads * (-(-cfg.max_tokens // 512) + 1)
+    assert big >= cfg.batch * cfg.n_kv_heads * 4 + rows * (cfg.head_dim + 2) * 4
+    # 64-token splits of this cache would be > 128 splits
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_decode_workspace_bytes(cfg, 64)
+    assert e.value.status == kvq.ERR_UNSUPPORTED
+    # the library's own choice is sized for min(128, max_tokens // 256)
+    # quantized splits (+1 residual slot), whatever device runs it
+    def ws(c, nsplit):
+        def a256(x):
+            return -(-x // 256) * 256
+        rows = c.batch * c.n_q_heads * (nsplit + 1)
+        return a256(c.batch * c.n_kv_heads * 4) + a256(rows * c.head_dim * 4) + 2 * a256(rows * 4)
+    for w in (WORKLOADS[1], WORKLOADS[2], WORKLOADS[4]):
+        c = _cfg(w)
+        assert kvq.kvq_decode_workspace_bytes(c, 0) == ws(c, min(128, max(1, c.max_tokens // 256)))
+    short = _cfg(WORKLOADS[1], max_tokens=200)
+    assert kvq.kvq_decode_workspace_bytes(short, 0) == ws(short, 1)
 
 
 @pytest.mark.parametrize("d", [64, 128])
