@@ -104,6 +104,42 @@ def append_bytes(w, lens_before, t):
     return total
 
 
+def workload_key(w):
+    """File-name key of a workload's profile summaries under profiles/."""
+    fmt = w.fmt if w.fmt != "kivi" else f"kivi{w.bits}_g{w.group}_r{w.residual}"
+    ctx = w.context if not w.ragged else f"{w.context_min}-{w.context}"
+    return f"{fmt}_b{w.batch}_hkv{w.n_kv_heads}_hq{w.n_q_heads}_d{w.head_dim}_n{ctx}"
+
+
+DECODE_SOURCES = ("quantized_kv_cache_06_amd/csrc/kvq_decode.hip", "quantized_kv_cache_06_amd/csrc/kvq_device.h",
+                  "quantized_kv_cache_06_amd/csrc/kvq_internal.h", "include/kvq.h")
+
+
+def profiled_traffic(w):
+    """HBM bytes per decode launch from the committed rocprofv3 counter
+    summary of this workload (FETCH_SIZE and WRITE_SIZE per dispatch, scaled
+    by what they read for a plain 1 GiB copy), or None when there is none or
+    the decode kernel's sources have changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"decode_split_{workload_key(w)}.hbm_counters.md")
+    if not os.path.exists(path):
+        return None, None
+    rec = None
+    with open(path) as f:
+        for line in f:
+            if line.startswith('{"kernel": "decode_split"'):
+                rec = json.loads(line)
+    if rec is None:
+        return None, None
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(ROOT, name), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != rec["kernel_source_sha256"]:
+        return None, os.path.relpath(path, ROOT) + " (stale: kernel sources changed)"
+    return float(rec["traffic_bytes_per_launch"]), os.path.relpath(path, ROOT)
+
+
 def cpu_baseline(w, k_host, v_host, q_host, lens, seconds):
     """Time the CPU oracle (as it is) on whole sequences of copy 0: append
     every token, then decode, until about `seconds` of work is done."""
@@ -294,6 +330,7 @@ def main():
     value = (dec_bytes_total + app_bytes_total) / (total_ms * 1e-3) / 1e9
     ms_per_step = total_ms / args.steps
 
+    traffic, traffic_src = profiled_traffic(w) if args.split == 0 else (None, None)
     result = {
         "metric": "decode-attn effective HBM GB/s (% of peak) + appended KV tokens/s, 1 GPU",
         "value": round(value, 2),
@@ -323,9 +360,12 @@ def main():
         "wall_s_timed": round(wall, 3),
         "decode_calls_timed": rounds * copies,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": round(traffic) if traffic is not None else None,
                      "kernel": "decode_split (one launch per decode call, merge fused)",
-                     "bytes_per_launch": round(dec_bytes_per_call, 1)},
+                     "bytes_per_launch": round(dec_bytes_per_call, 1),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE, WRITE_SIZE scaled by a 1 GiB copy)",
+                     "traffic_source": traffic_src},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, k_host, v_host, qs[0].float().cpu().numpy(), lens0.numpy(),
