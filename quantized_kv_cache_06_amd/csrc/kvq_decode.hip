@@ -54,7 +54,8 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kTile = 32;        // tokens per wave iteration (two 16-token score tiles)
-constexpr int kResidChunk = 256; // tokens per residual chunk (one per thread)
+constexpr int kResidChunk = 256;
+constexpr float kLazyLog2 = 8.0f;  // headroom of the lazy softmax rescale (log2 units) // tokens per residual chunk (one per thread)
 constexpr int kMaxSplits = kMaxDecodeSplits;  // quantized splits per sequence (S - 1 <= this)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr uint32_t kMagic128 = 0x43004300u;  // two bf16 128.0
@@ -110,6 +111,35 @@ __device__ __forceinline__ uint32_t f16_sub1024(uint32_t w) {
   return __builtin_bit_cast(uint32_t, y);
 }
 
+// (x & m) | c in one instruction (a three-input bitwise op; its truth table
+// is f(0xF0, 0xCC, 0xAA) = (0xF0 & 0xCC) | 0xAA).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(x, m, c, 0xEA);
+}
+
+// -1.0 in a register the compiler cannot see through, so that x - f16 below
+// stays a multiply-add with an f16 operand (one v_fma_mix instruction)
+// instead of a convert and a subtract.
+__device__ __forceinline__ float opaque_minus_one() {
+  float v;
+  asm volatile("v_mov_b32 %0, 0xbf800000" : "=v"(v));
+  return v;
+}
+// f16 pair (x0 - hi.lo, x1 - hi.hi), each difference exact in fp32 and
+// rounded once to f16: the lo term of the hi/lo split of (x0, x1) whose hi
+// term is hi = pack_f16(x0, x1). m1 = opaque_minus_one().
+__device__ __forceinline__ uint32_t f16_residual(uint32_t hi, float x0, float x1, float m1) {
+  const f16x2_t h = __builtin_bit_cast(f16x2_t, hi);
+  return pack_f16(__builtin_fmaf(float(h[0]), m1, x0), __builtin_fmaf(float(h[1]), m1, x1));
+}
+
+// Within each 16-lane row: the lanes of the banks in `banks` (bit b = lanes
+// 4b..4b+3) take src from the lane 8 places along; the others keep old.
+template <int BANKS>
+__device__ __forceinline__ uint32_t swap8_into(uint32_t old, uint32_t src) {
+  return uint32_t(__builtin_amdgcn_update_dpp(int(old), int(src), 0x128, 0xf, BANKS, false));
+}
+
 // Two floats to a bf16 pair, round to nearest even (x0 in the low half).
 __device__ __forceinline__ uint32_t pack_bf16(float x0, float x1) {
   const f32x2 v = {x0, x1};
@@ -134,6 +164,10 @@ __device__ __forceinline__ Split2 split_pair(float x0, float x1) {
 __device__ __forceinline__ float add_ror8(float x) {
   const int y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false);
   return x + __builtin_bit_cast(float, y);
+}
+__device__ __forceinline__ float max_ror8(float x) {  // max with the lane 8 places along the row
+  const int y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false);
+  return fmaxf(x, __builtin_bit_cast(float, y));
 }
 __device__ __forceinline__ float max_rows(float x) {  // max over lanes l, l^16, l^32, l^48
   x = fmaxf(x, __shfl_xor(x, 16, kWave));
@@ -277,6 +311,8 @@ __device__ __forceinline__ void load_elems(const void* p, size_t i, float* x) {
 // Key bytes. 8-bit codes: bf16, exact. KIVI codes: f16, each element exactly
 // code * 2^kfactor_log2(kk, i): the nibble (or 2-bit field) is masked in
 // place under the f16 pattern of 1024 and 1024 is subtracted, which is exact.
+// (Subnormal f16 codes would avoid the subtraction, but the matrix cores do
+// not accumulate products of subnormal inputs exactly.)
 template <int BITS>
 __device__ __forceinline__ constexpr int kfactor_log2(int kk, int i) {
   if constexpr (BITS == 4) {
@@ -298,10 +334,10 @@ __device__ __forceinline__ u32x4 key_operand(const uint32_t* kw, int kk) {
   } else if constexpr (BITS == 4) {
     // pairs (nibble j, nibble j+4): j = 0, 2 at bits 0-3 (x1), j = 1, 3 at bits 4-7 (x16)
     const uint32_t w = kw[kk], w8 = w >> 8;
-    a[0] = f16_sub1024((w & 0x000F000Fu) | kMagic1024);
-    a[1] = f16_sub1024((w & 0x00F000F0u) | kMagic1024);
-    a[2] = f16_sub1024((w8 & 0x000F000Fu) | kMagic1024);
-    a[3] = f16_sub1024((w8 & 0x00F000F0u) | kMagic1024);
+    a[0] = f16_sub1024(and_or(w, 0x000F000Fu, kMagic1024));
+    a[1] = f16_sub1024(and_or(w, 0x00F000F0u, kMagic1024));
+    a[2] = f16_sub1024(and_or(w8, 0x000F000Fu, kMagic1024));
+    a[3] = f16_sub1024(and_or(w8, 0x00F000F0u, kMagic1024));
   } else {
     // pairs (code j, code j+8), j = 4*(kk&1) + e: fields j <= 4 at bits 2j
     // (x4^j), fields 5..7 shifted down by 10 (x4^(j-5))
@@ -311,7 +347,7 @@ __device__ __forceinline__ u32x4 key_operand(const uint32_t* kw, int kk) {
       const int j = 4 * (kk & 1) + e;
       const uint32_t src = j <= 4 ? w : w10;
       const int sh = j <= 4 ? 2 * j : 2 * (j - 5);
-      a[e] = f16_sub1024((src & (0x00030003u << sh)) | kMagic1024);
+      a[e] = f16_sub1024(and_or(src, 0x00030003u << sh, kMagic1024));
     }
   }
   return a;
@@ -332,12 +368,12 @@ __device__ __forceinline__ u32x4 value_operand(const uint32_t* vw, int mt, int r
   } else if constexpr (BITS == 4) {
     const uint32_t w = vw[mt];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) a[j] = ((w >> (4 * j)) & 0x000F000Fu) | kMagic128;
+    for (int j = 0; j < 4; ++j) a[j] = and_or(w >> (4 * j), 0x000F000Fu, kMagic128);
   } else {
     const uint32_t w = vw[mt];
     const int sh = 8 * (r & 1);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) a[j] = ((w >> (sh + 2 * j)) & 0x00030003u) | kMagic128;
+    for (int j = 0; j < 4; ++j) a[j] = and_or(w >> (sh + 2 * j), 0x00030003u, kMagic128);
   }
   return a;
 }
@@ -509,7 +545,8 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   float zb[NVG];
 #pragma unroll
   for (int j = 0; j < NVG; ++j) zb[j] = 0.0f;
-  float kbias = 0.0f, kscale = 1.0f;
+  float kbias = 0.0f, kscale = 1.0f;  // KIVI: score = (acc * kscale + kbias), log2 domain
+  int kes = 0;                        // KIVI: exponent that scaled the open group's Key scales
 
   const uint8_t* kbase = cv.k_codes + pair * size_t(cv.cap) * KB + (KSPLIT ? 16 * r : LKB * r);
   const uint8_t* vbase = cv.v_codes + pair * size_t(cv.cap / TB) * D * VWB;
@@ -596,12 +633,45 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   }
   if (nk > 0) static_for<NPF>([&](auto uc) { load_tile(ring[decltype(uc)::value], decltype(uc)::value); });
 
-  // ---- query, part 2: KIVI stages q in LDS; the others build the operand
+  // ---- query, part 2: KIVI stages q in LDS and keeps its share of the
+  // normalized query (below); the others build the operand
+  // KIVI Key-group fold layout: lane (m, r) computes both f16 terms of the
+  // operand pairs of head hh, row group r, for the NKW k-steps from kk0 (the
+  // hi lanes the first half, the lo lanes the second); the two lanes of a
+  // (head, row group) then swap halves. qn = q * 2^(eq - kfactor) for those
+  // elements, eq putting the head's largest |q * 2^-kfactor| in [64, 128).
+  constexpr int NKW = NKK / 2;
+  float qn[NKW][4][2];
+  int eq = 0, fbase = 0;
+  const float m1 = KIVI ? opaque_minus_one() : -1.0f;
   if constexpr (KIVI) {
     const int e0 = tid * EPT, j = e0 / D, c = e0 % D;
 #pragma unroll
     for (int i = 0; i < EPT; ++i) sm.q[j][c + i] = j < g ? qx[i] : 0.0f;
     __syncthreads();
+    const int kk0 = lo_col ? NKW : 0;
+    fbase = CPL * r + cperm<BITS>(kk0, 0);  // the lane's elements sit at fbase + cperm(kw, i)
+    float mx = 0.0f;
+#pragma unroll
+    for (int kw = 0; kw < NKW; ++kw)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int i = 2 * e + h2;
+          const float v = __builtin_amdgcn_ldexpf(sm.q[hh][fbase + cperm<BITS>(kw, i)],
+                                                  -kfactor_log2<BITS>(kk0 + kw, i));
+          qn[kw][e][h2] = v;
+          mx = fmaxf(mx, fabsf(v));
+        }
+    mx = max_rows(max_ror8(mx));
+    eq = mx > 0.0f ? 7 - __builtin_amdgcn_frexp_expf(mx) : 0;
+#pragma unroll
+    for (int kw = 0; kw < NKW; ++kw)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) qn[kw][e][h2] = __builtin_amdgcn_ldexpf(qn[kw][e][h2], eq);
   } else {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
@@ -627,68 +697,58 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
       for (int j = 0; j < NVG; ++j) mdst[j] = sl.mw[j];
       if constexpr (KIVI) {
         if (grp_open) {
+          // Key scales (lanes 0-31; >= 0) scaled by 2^kes so that the
+          // group's largest lies in [64, 128); zero-points as they are
+          float ms = 0.0f;
+#pragma unroll
+          for (int j = 0; j < KGL; ++j) ms = fmaxf(ms, sl.gw[j]);
+#pragma unroll
+          for (int o = 1; o < 32; o <<= 1) ms = fmaxf(ms, __shfl_xor(ms, o, kWave));
+          ms = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, ms)));
+          kes = ms > 0.0f ? 7 - __builtin_amdgcn_frexp_expf(ms) : 0;
           float* gdst = sm.kgrp[wave][part] + qi * KGL;
 #pragma unroll
-          for (int j = 0; j < KGL; ++j) gdst[j] = sl.gw[j];
+          for (int j = 0; j < KGL; ++j) gdst[j] = part ? sl.gw[j] : __builtin_amdgcn_ldexpf(sl.gw[j], kes);
         }
       }
     }
     wave_lds_sync();
 
     // ---- KIVI: fold this group's per-channel Key scales into the query ----
-    // x_c = q_c * s_c is scaled by 2^ke (per head) so its largest magnitude
-    // is below 2^15, divided by the key operand's power-of-two factor, and
-    // split into f16 hi + lo (about 22 significant bits).
+    // x_c = qn_c * s'_c (|x| < 2^14) split into f16 hi + lo (about 22
+    // significant bits); the score of a token is then
+    //   acc * 2^(-eq - kes) + sum_c q_c z_c,
+    // acc the matrix-core sum of x against the Key codes (times 2^kfactor).
     if constexpr (KIVI) {
       if (grp_open) {
-        const float* qr = &sm.q[hh][CPL * r];
-        const float* ksr = &sm.kgrp[wave][0][CPL * r];
-        const float* kzr = &sm.kgrp[wave][1][CPL * r];
-        float xq[NKK][8];
-        float qzs = 0.0f, amax = 0.0f;
+        const float* ksr = &sm.kgrp[wave][0][fbase];
+        const float* kzr = &sm.kgrp[wave][1][fbase];
+        const float* qr = &sm.q[hh][fbase];
+        uint32_t xh[NKW][4], xl[NKW][4];
+        float qzs = 0.0f;
 #pragma unroll
-        for (int u = 0; u < NKK / 2; ++u) {  // 16 channels (two k-steps) at a time
-          float ks[16], kz[16], qv[16];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(ksr + 16 * u + 4 * v);
-            const f32x4 z = *reinterpret_cast<const f32x4*>(kzr + 16 * u + 4 * v);
-            const f32x4 x = *reinterpret_cast<const f32x4*>(qr + 16 * u + 4 * v);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              ks[4 * v + i] = a[i];
-              kz[4 * v + i] = z[i];
-              qv[4 * v + i] = x[i];
-            }
-          }
-#pragma unroll
-          for (int i = 0; i < 16; ++i) qzs += qv[i] * kz[i];
-#pragma unroll
-          for (int kh = 0; kh < 2; ++kh) {
-            const int kk = 2 * u + kh;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const int c = cperm<BITS>(kk, i) - 16 * u;
-              xq[kk][i] = qv[c] * ks[c];
-              amax = fmaxf(amax, fabsf(xq[kk][i]));
-            }
-          }
-        }
-        amax = max_rows(amax);
-        const int ke = amax > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(amax) : 0;
-        kscale = __builtin_amdgcn_ldexpf(1.0f, -ke);
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
+        for (int kw = 0; kw < NKW; ++kw)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float x0 = __builtin_amdgcn_ldexpf(xq[kk][2 * e], ke - kfactor_log2<BITS>(kk, 2 * e));
-            const float x1 = __builtin_amdgcn_ldexpf(xq[kk][2 * e + 1], ke - kfactor_log2<BITS>(kk, 2 * e + 1));
-            const uint32_t hi = pack_f16(x0, x1);
-            const uint32_t lo = pack_f16(x0 - f16_lo(hi), x1 - f16_hi(hi));
-            bq[kk][e] = lo_col ? lo : hi;
+            const int oa = cperm<BITS>(kw, 2 * e), ob = cperm<BITS>(kw, 2 * e + 1);
+            const float x0 = qn[kw][e][0] * ksr[oa];
+            const float x1 = qn[kw][e][1] * ksr[ob];
+            xh[kw][e] = pack_f16(x0, x1);
+            xl[kw][e] = f16_residual(xh[kw][e], x0, x1, m1);
+            qzs = fmaf(qr[oa], kzr[oa], qzs);
+            qzs = fmaf(qr[ob], kzr[ob], qzs);
           }
-        }
-        kbias = sum_rows(qzs);
+        // k-steps [0, NKW): hi lanes keep their own hi term, lo lanes take
+        // the hi lane's lo term; [NKW, 2 NKW): the other way round
+#pragma unroll
+        for (int kw = 0; kw < NKW; ++kw)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            bq[kw][e] = swap8_into<0xc>(xh[kw][e], xl[kw][e]);
+            bq[NKW + kw][e] = swap8_into<0x3>(xl[kw][e], xh[kw][e]);
+          }
+        kbias = sum_rows(add_ror8(qzs)) * sm_log2;
+        kscale = __builtin_amdgcn_ldexpf(sm_log2, -eq - kes);
       }
     }
 
@@ -720,7 +780,7 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float x = add_ror8(acc[t][j]);
-        if constexpr (KIVI) x = (x * kscale + kbias) * sm_log2;
+        if constexpr (KIVI) x = fmaf(x, kscale, kbias);
         else x = x * ks[t][j] * sm_log2;
         if (tok<BITS>(t, r, j) >= valid) x = -INFINITY;
         sc[t][j] = x;
@@ -728,25 +788,29 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
       }
     }
     tmax = max_rows(tmax);
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.0f;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float p = __builtin_amdgcn_exp2f(sc[t][j] - m_new);
-        sc[t][j] = p;
-        psum += p;
-      }
-    l_run = l_run * alpha + psum;
-    if (__any(alpha != 1.0f)) {
+    // Lazy rescale: the running maximum moves only when a score exceeds it
+    // by more than kLazyLog2, so the accumulators are rescaled on few tiles
+    // and every probability stays below 2^kLazyLog2.
+    if (__any(tmax > m_run + kLazyLog2)) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < NMT; ++i) o[i] *= alpha;
 #pragma unroll
       for (int j = 0; j < NVG; ++j) zb[j] *= alpha;
     }
+    float psum = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p = __builtin_amdgcn_exp2f(sc[t][j] - m_run);
+        sc[t][j] = p;
+        psum += p;
+      }
+    l_run += psum;
 
     // ---- values ----
     if constexpr (!KIVI) {
@@ -763,36 +827,60 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
         o[mt] = mfma_bf16(a, bp, o[mt]);
       }
     } else {
-      // per-token Value scale and zero of each channel group: 4 consecutive
-      // tokens per score tile, NVG values each
-      float vsf[2][4 * NVG], vzf[2][4 * NVG];
+      // The hi and lo lanes of a column pair hold the same probabilities.
+      // Each takes two of the four operand pairs (pair k = tokens (0, k) and
+      // (1, k) of the score tiles: the hi lane k = 0, 1, the lo lane k = 2,
+      // 3), splits them into both terms, and the two lanes swap halves.
+      const int ja = lo_col ? 2 : 0;
+      float ps[2][2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) ps[t][u] = lo_col ? sc[t][2 + u] : sc[t][u];
+      // per-token Value scale and zero of each channel group, for the lane's
+      // two tokens of each score tile
+      float vsf[2][2 * NVG], vzf[2][2 * NVG];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
+        const int off = (tok<BITS>(t, r, 0) + ja) * NVG;
+        if constexpr (NVG == 1) {
+          const f32x2 a = *reinterpret_cast<const f32x2*>(meta0 + off);
+          const f32x2 z = *reinterpret_cast<const f32x2*>(meta1 + off);
+          vsf[t][0] = a[0]; vsf[t][1] = a[1];
+          vzf[t][0] = z[0]; vzf[t][1] = z[1];
+        } else {
 #pragma unroll
-        for (int v = 0; v < NVG; ++v) {
-          const f32x4 a = *reinterpret_cast<const f32x4*>(meta0 + tok<BITS>(t, r, 0) * NVG + 4 * v);
-          const f32x4 z = *reinterpret_cast<const f32x4*>(meta1 + tok<BITS>(t, r, 0) * NVG + 4 * v);
+          for (int v = 0; v < NVG / 2; ++v) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(meta0 + off + 4 * v);
+            const f32x4 z = *reinterpret_cast<const f32x4*>(meta1 + off + 4 * v);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            vsf[t][4 * v + i] = a[i];
-            vzf[t][4 * v + i] = z[i];
+            for (int i = 0; i < 4; ++i) {
+              vsf[t][4 * v + i] = a[i];
+              vzf[t][4 * v + i] = z[i];
+            }
           }
         }
       }
 #pragma unroll
       for (int jg = 0; jg < NVG; ++jg) {
-        float pv[2][4];
+        float pv[2][2];
         float zs = 0.0f;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float vsc = vsf[t][j * NVG + jg];
-            pv[t][j] = sc[t][j] * vsc;
-            zs += sc[t][j] * (vzf[t][j * NVG + jg] + kCenter * vsc);
+          for (int u = 0; u < 2; ++u) {
+            const float vsc = vsf[t][u * NVG + jg];
+            pv[t][u] = ps[t][u] * vsc;
+            zs = fmaf(ps[t][u], fmaf(kCenter, vsc, vzf[t][u * NVG + jg]), zs);
           }
         zb[jg] += zs;
-        const u32x4 bp = prob_operand<BITS>(pv, lo_col);
+        const Split2 s0 = split_pair(pv[0][0], pv[1][0]);  // pair ja
+        const Split2 s1 = split_pair(pv[0][1], pv[1][1]);  // pair ja + 1
+        u32x4 bp;
+        bp[0] = swap8_into<0xc>(s0.hi, s0.lo);
+        bp[1] = swap8_into<0xc>(s1.hi, s1.lo);
+        bp[2] = swap8_into<0x3>(s0.lo, s0.hi);
+        bp[3] = swap8_into<0x3>(s1.lo, s1.hi);
 #pragma unroll
         for (int mt = jg * MPG; mt < (jg + 1) * MPG; ++mt) {
           o[mt] = mfma_bf16(value_operand<FMT, BITS>(vc, mt, r), bp, o[mt]);
@@ -820,7 +908,7 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   const float l_tot = sum_rows(l_run);
   float zt[NVG];
 #pragma unroll
-  for (int j = 0; j < NVG; ++j) zt[j] = sum_rows(zb[j]);
+  for (int j = 0; j < NVG; ++j) zt[j] = sum_rows(add_ror8(zb[j]));  // hi and lo lanes hold disjoint tokens
   if (lane < 8) {
     sm.m[wave][lane] = m_run;
     sm.l[wave][lane] = l_tot;
