@@ -74,6 +74,11 @@ constexpr uint32_t kMagic128 = 0x43004300u;  // two bf16 128.0
 #ifndef KVQ_DECODE_NPF
 #define KVQ_DECODE_NPF 2
 #endif
+// Workgroups per compute unit the register allocation must allow (0 = the
+// per-kernel default of min_wg_per_cu below).
+#ifndef KVQ_DECODE_MIN_WG_PER_CU
+#define KVQ_DECODE_MIN_WG_PER_CU 0
+#endif
 constexpr bool kStreamNT = KVQ_DECODE_NT != 0;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -115,6 +120,16 @@ __device__ __forceinline__ uint32_t f16_sub1024(uint32_t w) {
 // is f(0xF0, 0xCC, 0xAA) = (0xF0 & 0xCC) | 0xAA).
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
   return __builtin_amdgcn_bitop3_b32(x, m, c, 0xEA);
+}
+
+// m ? a : b for a lane mask m (all ones or all zeros) as one bitwise op.
+// Unlike a plain conditional between two elements of a register array, it
+// cannot be rewritten into an array access with a lane-dependent index
+// (which would move the array to scratch memory, whose loads wait behind
+// every outstanding global load).
+__device__ __forceinline__ float select_bits(uint32_t m, float a, float b) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_bitop3_b32(__builtin_bit_cast(uint32_t, a),
+                                                               __builtin_bit_cast(uint32_t, b), m, 0xE4));
 }
 
 // -1.0 in a register the compiler cannot see through, so that x - f16 below
@@ -832,11 +847,12 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
       // (1, k) of the score tiles: the hi lane k = 0, 1, the lo lane k = 2,
       // 3), splits them into both terms, and the two lanes swap halves.
       const int ja = lo_col ? 2 : 0;
+      const uint32_t lo_mask = lo_col ? 0xffffffffu : 0u;
       float ps[2][2];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) ps[t][u] = lo_col ? sc[t][2 + u] : sc[t][u];
+        for (int u = 0; u < 2; ++u) ps[t][u] = select_bits(lo_mask, sc[t][2 + u], sc[t][u]);
       // per-token Value scale and zero of each channel group, for the lane's
       // two tokens of each score tile
       float vsf[2][2 * NVG], vzf[2][2 * NVG];
@@ -1046,8 +1062,17 @@ __device__ __forceinline__ void split_residual(const CacheView& cv, int b, int h
 // g query heads by the log-sum-exp rule, writes the normalized output and
 // resets the counter to zero. Slots with no tokens return at once; an empty
 // sequence gets zeros from slot 0.
+// Three resident workgroups per compute unit (12 waves, at most 168
+// registers per lane) measure fastest: more loads in flight per unit. KIVI
+// INT4 with groups of 32 at d = 128 needs a few more registers and keeps two.
+template <int FMT, int BITS, int D, int G>
+constexpr int min_wg_per_cu() {
+  if constexpr (KVQ_DECODE_MIN_WG_PER_CU > 0) return KVQ_DECODE_MIN_WG_PER_CU;
+  return (FMT == KVQ_FMT_KIVI && BITS == 4 && D == 128 && G == 32) ? 2 : 3;
+}
+
 template <int FMT, int BITS, int D, int G, bool BF16>
-__global__ __launch_bounds__(kThreads) void decode_split(CacheView cv, const int32_t* __restrict__ seq_lens,
+__global__ __launch_bounds__(kThreads, (min_wg_per_cu<FMT, BITS, D, G>())) void decode_split(CacheView cv, const int32_t* __restrict__ seq_lens,
                                                         const void* __restrict__ q, float sm_log2, float* __restrict__ out,
                                                         DecodeWork wk) {
   constexpr bool KIVI = FMT == KVQ_FMT_KIVI;
