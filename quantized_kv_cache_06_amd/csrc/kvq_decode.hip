@@ -477,6 +477,29 @@ __device__ __forceinline__ float get_partial(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Buffer resource over n bytes at p (raw addressing, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, int(n), 0x00020000);
+}
+// 16-byte partial loads and stores with the same device-scope coherence as
+// put_partial / get_partial (cache policy sc1).
+constexpr int kCoherent = 16;
+__device__ __forceinline__ f32x4 get_partial4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCoherent);
+}
+__device__ __forceinline__ void put_partial4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, kCoherent);
+}
+
+// x, as a value the compiler cannot relate to earlier expressions of x
+// (emits no instruction). Used after the main loop so that addresses the
+// epilogue shares with the prologue are recomputed instead of being held in
+// registers across the loop.
+__device__ __forceinline__ int fresh(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Orders this wave's LDS writes before its later LDS reads by other lanes.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -939,23 +962,29 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
     }
   }
   __syncthreads();
-  for (int e = tid; e < g * D; e += kThreads) {
-    const int j = e / D, c = e % D;
+  // thread (j, c4): head j, channels [4 c4, 4 c4 + 4); one 16-byte store
+  constexpr int C4 = D / 4;
+  const int tm = fresh(tid);
+  const int j = tm / C4, c4 = tm % C4;
+  if (j < g) {
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.m[w][j]);
-    float ov = 0.0f, L = 0.0f;
+    f32x4 ov = {0.0f, 0.0f, 0.0f, 0.0f};
+    float L = 0.0f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
         const float f = __builtin_amdgcn_exp2f(sm.m[w][j] - M);
-        ov += sm.o[w][j][c] * f;
+        ov += *reinterpret_cast<const f32x4*>(&sm.o[w][j][4 * c4]) * f;
         L += sm.l[w][j] * f;
       }
     }
     const size_t row = partial_row(cv, wk, b, h, j, s);
-    put_partial(&wk.o[row * D + c], ov);
-    if (c == 0) {
+    const size_t row0 = partial_row(cv, wk, b, h, 0, 0);
+    put_partial4(buffer_rsrc(wk.o + row0 * D, uint32_t(g * wk.S * D * 4)), uint32_t(((row - row0) * D + 4 * c4) * 4),
+                 ov);
+    if (c4 == 0) {
       put_partial(&wk.m[row], M);
       put_partial(&wk.l[row], L);
     }
@@ -1120,17 +1149,35 @@ __global__ __launch_bounds__(kThreads, (min_wg_per_cu<FMT, BITS, D, G>())) void 
   __syncthreads();
   if (ticket != uint32_t(nact - 1)) return;
 
-  // Merge: gather every split's (max, sum) of the g heads into LDS with one
-  // parallel batch of loads, turn them into weights exp2(m - M) and 1 / L per
-  // head, then sum the weighted partial outputs eight splits at a time.
+  // Merge. Thread (j, c4) owns channels [4 c4, 4 c4 + 4) of head j and
+  // loads its partial outputs of up to kMergeBatch splits at a time with
+  // 16-byte coherent loads; the first batch is issued together with the
+  // gather of every split's (max, sum) into LDS, so a call with at most
+  // kMergeBatch splits merges in one round trip. The (max, sum) table turns
+  // into weights exp2(m - M) and 1 / L per head.
   // nact <= kMaxSplits + 1 (the host caps the split count).
+  constexpr int kMergeBatch = 16;
+  constexpr int C4 = D / 4;
   float* wgt = smem;                     // [g][nact] maxima, then weights
   float* lsm = smem + 8 * (kMaxSplits + 1);  // [g][nact] sums
   float* inv = lsm + 8 * (kMaxSplits + 1);   // [g] 1 / L
   auto slot = [&](int k) { return k < nsq ? k : wk.S - 1; };
+  const int tm = fresh(tid);
+  const int j = tm / C4, c4 = tm % C4;
+  const bool mine = j < g;
+  const size_t row0 = partial_row(cv, wk, b, h, 0, 0);
+  const __amdgpu_buffer_rsrc_t orsrc = buffer_rsrc(wk.o + row0 * D, uint32_t(g * wk.S * D * 4));
+  const uint32_t obase = uint32_t((size_t(min(j, g - 1)) * wk.S * D + 4 * c4) * 4);
+  f32x4 ov[kMergeBatch];
+  auto load_batch = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u)
+      ov[u] = get_partial4(orsrc, obase + uint32_t(slot(min(k0 + u, nact - 1)) * D * 4));
+  };
+  load_batch(0);
   for (int e = tid; e < g * nact; e += kThreads) {
-    const int j = e / nact, k = e % nact;
-    const size_t r = (size_t(b) * cv.Hq + size_t(h) * g + j) * wk.S + slot(k);
+    const int jj = e / nact, k = e % nact;
+    const size_t r = row0 + size_t(jj) * wk.S + slot(k);
     wgt[e] = get_partial(&wk.m[r]);
     lsm[e] = get_partial(&wk.l[r]);
   }
@@ -1147,20 +1194,17 @@ __global__ __launch_bounds__(kThreads, (min_wg_per_cu<FMT, BITS, D, G>())) void 
     inv[tid] = L > 0.0f ? 1.0f / L : 0.0f;
   }
   __syncthreads();
-  for (int e = tid; e < g * D; e += kThreads) {
-    const int j = e / D, c = e % D;
-    const size_t row = (size_t(b) * cv.Hq + size_t(h) * g + j) * wk.S;
-    float acc = 0.0f;
-    for (int k0 = 0; k0 < nact; k0 += 8) {
-      float ov[8];
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k0 = 0; k0 < nact; k0 += kMergeBatch) {
+    if (k0 > 0) load_batch(k0);
+    if (mine) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) ov[u] = get_partial(&wk.o[(row + slot(min(k0 + u, nact - 1))) * D + c]);
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (k0 + u < nact) acc = fmaf(ov[u], wgt[j * nact + k0 + u], acc);
+      for (int u = 0; u < kMergeBatch; ++u)
+        if (k0 + u < nact) acc += ov[u] * wgt[j * nact + k0 + u];
     }
-    out[(size_t(b) * cv.Hq + size_t(h) * g + j) * D + c] = acc * inv[j];
   }
+  if (mine)
+    *reinterpret_cast<f32x4*>(&out[(size_t(b) * cv.Hq + size_t(h) * g + j) * D + 4 * c4]) = acc * inv[j];
   if (tid == 0) __hip_atomic_store(&wk.count[pair], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
