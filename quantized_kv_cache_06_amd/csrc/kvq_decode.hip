@@ -54,8 +54,8 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kTile = 32;        // tokens per wave iteration (two 16-token score tiles)
-constexpr int kResidChunk = 256;
-constexpr float kLazyLog2 = 8.0f;  // headroom of the lazy softmax rescale (log2 units) // tokens per residual chunk (one per thread)
+constexpr int kResidChunk = 64;   // KIVI residual tokens per chunk (one per lane in its softmax)
+constexpr float kLazyLog2 = 8.0f;  // headroom of the lazy softmax rescale (log2 units)
 constexpr int kMaxSplits = kMaxDecodeSplits;  // quantized splits per sequence (S - 1 <= this)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr uint32_t kMagic128 = 0x43004300u;  // two bf16 128.0
@@ -445,7 +445,7 @@ struct SmemQuant {
 template <int D>
 struct SmemResid {
   float q[8][D];
-  float sc[8][kResidChunk];   // scores, then probabilities; reused for the final reduction
+  float sc[8][kResidChunk];   // scores, then probabilities
   float st_m[8], st_l[8], st_a[8];
 };
 template <int D>
@@ -992,63 +992,80 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
 }
 
 // ---------------------------------------------------------------------------
-// KIVI residual ring (tokens [nq, n), full precision): one workgroup on the
-// vector ALU, one thread per token for the scores, threads over (channel,
-// token part) for the values. Writes partial slot s.
+// KIVI residual ring (tokens [nq, n), full precision), in chunks of 64
+// tokens on the vector ALU. Every load of a chunk is issued before any is
+// used, so a chunk costs one memory round trip: the scores take four lanes
+// per token (a quarter of the row each, 16-byte loads, summed by
+// shuffles); the values take lane (channel pair, token part), the parts
+// summed by shuffles at the end. Writes partial slot s.
 // ---------------------------------------------------------------------------
 template <int D, bool BF16>
 __device__ __forceinline__ void split_residual(const CacheView& cv, int b, int h, int s, int nq, int n,
                                                const void* __restrict__ q, float sm_log2, const DecodeWork& wk,
                                                SmemResid<D>& sm) {
   constexpr int NH = 8;
-  constexpr int P = kThreads / D;  // token parts in the value phase
+  constexpr int T = kResidChunk;
+  constexpr int QPT = kThreads / T;       // lanes per token in the score phase
+  constexpr int CPT = D / QPT;            // their channels: 32 (d = 128) or 16 (d = 64)
+  constexpr int NP = kThreads / (D / 2);  // token parts in the value phase: 4 (d = 128) or 8 (d = 64)
+  constexpr int TPP = T / NP;             // tokens per part and chunk
+  static_assert(T == kWave && QPT * T == kThreads && NP * (D / 2) == kThreads, "residual layout");
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int g = cv.g, C = cv.C;
   const size_t pair = pair_index(cv, b, h);
+  const size_t ring = pair * size_t(C);
   for (int e = tid; e < NH * D; e += kThreads) {
     const int j = e / D, c = e % D;
     sm.q[j][c] = j < g ? load_elem<BF16>(q, (size_t(b) * cv.Hq + size_t(h) * g + j) * D + c) : 0.0f;
   }
+  for (int e = tid; e < NH * T; e += kThreads) sm.sc[e / T][e % T] = 0.0f;  // heads >= g stay 0
   if (tid < NH) {
     sm.st_m[tid] = -INFINITY;
     sm.st_l[tid] = 0.0f;
     sm.st_a[tid] = 1.0f;
   }
-  const int c = tid % D, part = tid / D;
-  float acc[NH];
+  const int ti = tid / QPT, cq = (tid % QPT) * CPT;  // scores: token ti, channels [cq, cq + CPT)
+  const int part = tid % NP, cp = tid / NP;          // values: channels 2 cp, 2 cp + 1
+  float acc[NH][2];
 #pragma unroll
-  for (int j = 0; j < NH; ++j) acc[j] = 0.0f;
+  for (int j = 0; j < NH; ++j) acc[j][0] = acc[j][1] = 0.0f;
   __syncthreads();
-  for (int cs = nq; cs < n; cs += kResidChunk) {
-    const int nt = min(kResidChunk, n - cs);
-    if (tid < nt) {
-      const size_t rbase = (pair * C + ((cs + tid) % C)) * D;
-      float sco[NH];
+  for (int cs = nq; cs < n; cs += T) {
+    const int nt = min(T, n - cs);
+    // the chunk's loads (ring slots are in bounds for any token index; the
+    // values of tokens past the chunk are zeroed below)
+    float kx[CPT];
+    load_elems<BF16, CPT>(cv.k_resid, (ring + size_t((cs + ti) % C)) * D + cq, kx);
+    float vx[TPP][2];
 #pragma unroll
-      for (int j = 0; j < NH; ++j) sco[j] = 0.0f;
-      for (int ch = 0; ch < D; ++ch) {
-        const float x = load_elem<BF16>(cv.k_resid, rbase + ch);
+    for (int u = 0; u < TPP; ++u)
+      load_elems<BF16, 2>(cv.v_resid, (ring + size_t((cs + part + NP * u) % C)) * D + 2 * cp, vx[u]);
+    float sco[NH];
 #pragma unroll
-        for (int j = 0; j < NH; ++j) sco[j] = fmaf(sm.q[j][ch], x, sco[j]);
-      }
+    for (int j = 0; j < NH; ++j) sco[j] = 0.0f;
 #pragma unroll
-      for (int j = 0; j < NH; ++j) sm.sc[j][tid] = sco[j] * sm_log2;
+    for (int k = 0; k < CPT; ++k)
+#pragma unroll
+      for (int j = 0; j < NH; ++j) sco[j] = fmaf(sm.q[j][cq + k], kx[k], sco[j]);
+#pragma unroll
+    for (int o = 1; o < QPT; o <<= 1)
+#pragma unroll
+      for (int j = 0; j < NH; ++j) sco[j] += __shfl_xor(sco[j], o, kWave);
+    if (tid % QPT == 0 && ti < nt) {
+#pragma unroll
+      for (int j = 0; j < g && j < NH; ++j) sm.sc[j][ti] = sco[j] * sm_log2;
     }
     __syncthreads();
+    // online softmax of each head over the chunk, one token per lane
     for (int j = wave; j < g; j += kWaves) {
-      float mx = -INFINITY;
-      for (int i = lane; i < nt; i += kWave) mx = fmaxf(mx, sm.sc[j][i]);
-      mx = wave_max(mx);
+      const float sc = lane < nt ? sm.sc[j][lane] : -INFINITY;
+      const float mx = wave_max(sc);
       const float m_old = sm.st_m[j];
       const float m_new = fmaxf(m_old, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_old - m_new);
-      float sum = 0.0f;
-      for (int i = lane; i < nt; i += kWave) {
-        const float p = __builtin_amdgcn_exp2f(sm.sc[j][i] - m_new);
-        sm.sc[j][i] = p;
-        sum += p;
-      }
-      sum = wave_sum(sum);
+      const float p = lane < nt ? __builtin_amdgcn_exp2f(sc - m_new) : 0.0f;
+      sm.sc[j][lane] = p;
+      const float sum = wave_sum(p);
       if (lane == 0) {
         sm.st_m[j] = m_new;
         sm.st_l[j] = sm.st_l[j] * alpha + sum;
@@ -1057,24 +1074,37 @@ __device__ __forceinline__ void split_residual(const CacheView& cv, int b, int h
     }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < NH; ++j) acc[j] *= sm.st_a[j];
-    for (int i = part; i < nt; i += P) {
-      const float v = load_elem<BF16>(cv.v_resid, (pair * C + ((cs + i) % C)) * D + c);
-#pragma unroll
-      for (int j = 0; j < NH; ++j) acc[j] = fmaf(sm.sc[j][i], v, acc[j]);
+    for (int j = 0; j < NH; ++j) {
+      const float a = sm.st_a[j];
+      acc[j][0] *= a;
+      acc[j][1] *= a;
     }
-    __syncthreads();
-  }
-  float* red = &sm.sc[0][0];  // P * NH * D <= NH * kResidChunk floats
 #pragma unroll
-  for (int j = 0; j < NH; ++j) red[(part * NH + j) * D + c] = acc[j];
-  __syncthreads();
+    for (int u = 0; u < TPP; ++u) {
+      const int i = part + NP * u;
+      const bool in = i < nt;
+      const float v0 = in ? vx[u][0] : 0.0f, v1 = in ? vx[u][1] : 0.0f;
+#pragma unroll
+      for (int j = 0; j < NH; ++j) {
+        const float p = sm.sc[j][i];
+        acc[j][0] = fmaf(p, v0, acc[j][0]);
+        acc[j][1] = fmaf(p, v1, acc[j][1]);
+      }
+    }
+    __syncthreads();  // probability reads done before the next chunk's scores
+  }
+#pragma unroll
+  for (int o = 1; o < NP; o <<= 1)
+#pragma unroll
+    for (int j = 0; j < NH; ++j) {
+      acc[j][0] += __shfl_xor(acc[j][0], o, kWave);
+      acc[j][1] += __shfl_xor(acc[j][1], o, kWave);
+    }
   if (part == 0) {
     for (int j = 0; j < g; ++j) {
-      float o = 0.0f;
-#pragma unroll
-      for (int p = 0; p < P; ++p) o += red[(p * NH + j) * D + c];
-      put_partial(&wk.o[partial_row(cv, wk, b, h, j, s) * D + c], o);
+      const size_t row = partial_row(cv, wk, b, h, j, s) * D + 2 * cp;
+      put_partial(&wk.o[row], acc[j][0]);
+      put_partial(&wk.o[row + 1], acc[j][1]);
     }
   }
   if (tid < g) {
