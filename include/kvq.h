@@ -208,9 +208,11 @@ int32_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t split_tokens, 
  *               on one workspace race.
  *  split_tokens the longest split, a positive multiple of 64 giving at most
  *               128 splits of max_tokens: n = ceil(max_tokens /
- *               split_tokens). 0 = the library's choice: n fills about one
- *               round of the device's resident workgroups (four rounds for
- *               KIVI), within the bound kvq_decode_workspace_bytes gives.
+ *               split_tokens). 0 = the library's choice: for FP8 and INT8,
+ *               about two workgroups per compute unit in one round; for
+ *               KIVI, about four rounds of the device's resident
+ *               workgroups; within the bound kvq_decode_workspace_bytes
+ *               gives.
  * Errors: KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE,
  * KVQ_ERR_HIP. */
 int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache, const int32_t* seq_lens,

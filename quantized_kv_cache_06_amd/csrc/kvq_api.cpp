@@ -122,17 +122,18 @@ int auto_split_bound(const kvq_config* c) {
   return int(n);
 }
 
-// Automatic split count for a device that holds `resident` decode
-// workgroups at once: enough splits that the B * Hkv * n workgroups fill
-// about kRounds waves of residency, within [1, auto_split_bound()]. The
-// per-token formats stream at the memory bound, where one full round is
-// fastest (each further round adds a prologue and a tail); KIVI's decode is
-// bound by vector-ALU work, where about four rounds let workgroups in
-// different phases (loads, group folds, epilogue) share a compute unit.
-int auto_split(const kvq_config* c, int64_t resident) {
-  const int64_t rounds = c->format == KVQ_FMT_KIVI ? 4 : 1;
+// Automatic split count for a device with `cus` compute units that holds
+// `resident` decode workgroups at once, within [1, auto_split_bound()].
+// The per-token formats stream at the memory bound in one round of two
+// workgroups per compute unit: a third co-resident workgroup gets the least
+// of the unit's memory issue (the oldest waves are served first) and ends
+// the launch late, and each further round adds a prologue and a tail.
+// KIVI's decode is bound by vector-ALU work, where about four rounds of
+// residency let workgroups in different phases (loads, group folds,
+// epilogue) share a compute unit.
+int auto_split(const kvq_config* c, int64_t resident, int64_t cus) {
   const int64_t pairs = int64_t(c->batch) * c->n_kv_heads;
-  int64_t n = rounds * resident / pairs;
+  int64_t n = c->format == KVQ_FMT_KIVI ? 4 * resident / pairs : 2 * cus / pairs;
   const int bound = auto_split_bound(c);
   if (n < 1) n = 1;
   if (n > bound) n = bound;
@@ -237,8 +238,9 @@ int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache, const int
   const kvq::CacheView v = make_view(cfg, lay, cache);
   if (split_tokens == 0) {
     const int resident = kvq::decode_resident_workgroups(v);
-    if (resident <= 0) return KVQ_ERR_HIP;
-    n = auto_split(cfg, resident);
+    const int cus = kvq::decode_compute_units();
+    if (resident <= 0 || cus <= 0) return KVQ_ERR_HIP;
+    n = auto_split(cfg, resident, cus);
   }
   const int S = n + 1;
   const uint64_t rows = uint64_t(cfg->batch) * cfg->n_q_heads * S;

@@ -1294,6 +1294,13 @@ hipError_t launch_decode(const CacheView& cv, const int32_t* seq_lens, const voi
   return hipGetLastError();
 }
 
+int decode_compute_units() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return cus;
+}
+
 int decode_resident_workgroups(const CacheView& cv) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;

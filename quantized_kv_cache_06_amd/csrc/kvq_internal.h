@@ -55,4 +55,7 @@ hipError_t launch_decode(const CacheView& cv, const int32_t* seq_lens, const voi
 // the kernel's occupancy per unit); 0 when it cannot be queried.
 int decode_resident_workgroups(const CacheView& cv);
 
+// Compute units of the current device; 0 when it cannot be queried.
+int decode_compute_units();
+
 }  // namespace kvq
