@@ -177,6 +177,30 @@ def test_edge_cases_empty_single_residual_only_and_overflow():
             T.assert_cache_matches(contents, b, h, seqs[b][h], w)
 
 
+@pytest.mark.parametrize("d,dtype,hq", [(128, "bf16", 16), (64, "f32", 6)])
+def test_kivi_residual_chunk_boundaries(d, dtype, hq):
+    """The residual ring is decoded in chunks of 64 tokens: residual-only
+    sequences of 63, 64, 65, 127 and 129 tokens, 191 (three chunks), and
+    sequences with quantized groups whose ring has wrapped (257, 300 tokens;
+    the ring holds R + G = 192). Cache contents bit-exact, attention in
+    tolerance; d = 64 with fp32 inputs and a GQA group of 3 query heads."""
+    w = SMALL[5].scaled(batch=8, head_dim=d, dtype=dtype, n_q_heads=hq, context=300, context_min=300)
+    _log(f"[residual chunk boundaries d={d} {dtype} g={hq // w.n_kv_heads}]")
+    cache = T.GpuCache(T.config(w, 300))
+    sm = O.default_sm_scale(w.head_dim)
+    q = queries(w, device="cuda")
+    k, v = kv_tokens(w, 300, device="cuda")
+    lens = torch.tensor([63, 64, 65, 127, 129, 191, 257, 300], dtype=torch.int32)
+    cache.append(k, v, lens)
+    seqs = _oracle_all(w, k, v, lens)
+    contents = T.CacheContents(cache)
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            T.assert_cache_matches(contents, b, h, seqs[b][h], w)
+    for split in (0, 64):
+        _check_decode(w, cache, seqs, q, sm, split, f"resid-chunks d={d}")
+
+
 def test_fp8_encoder_all_bf16_values_and_midpoints():
     """Every bf16 value in [-448, 448] plus E4M3 midpoints +-1 ulp through the
     per-token FP8 kernel: rows anchored at 448 have scale exactly 1, so the
