@@ -540,7 +540,8 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   constexpr int NPF = (KIVI && G == 32 && KVQ_DECODE_NPF > 2) ? 2 : KVQ_DECODE_NPF;  // ring slots (register budget)
   static_assert(KGL == 2 || KGL == 4, "group load width");
 
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: tile indices stay scalar
   const int m = lane & 15, r = lane >> 4;
   const int hh = m & 7;            // head within the GQA group for this column
   const bool lo_col = m >= 8;      // column holds the lo term
@@ -586,8 +587,15 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   float kbias = 0.0f, kscale = 1.0f;  // KIVI: score = (acc * kscale + kbias), log2 domain
   int kes = 0;                        // KIVI: exponent that scaled the open group's Key scales
 
-  const uint8_t* kbase = cv.k_codes + pair * size_t(cv.cap) * KB + (KSPLIT ? 16 * r : LKB * r);
-  const uint8_t* vbase = cv.v_codes + pair * size_t(cv.cap / TB) * D * VWB;
+  // Code loads: a scalar base that advances with the tile plus a per-lane
+  // byte offset fixed for the split, so no per-lane address arithmetic is
+  // done per tile.
+  const uint8_t* kpair = cv.k_codes + pair * size_t(cv.cap) * KB;
+  const uint8_t* vpair = cv.v_codes + pair * size_t(cv.cap / TB) * D * VWB;
+  uint32_t koff[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) koff[t] = uint32_t(tok<BITS>(t, m >> 2, m & 3) * KB + (KSPLIT ? 16 * r : LKB * r));
+  const uint32_t voff = uint32_t((size_t(BITS == 2 ? (r >> 1) : r) * D + VW * m) * VWB);
   float* meta0 = sm.meta[wave][0];
   float* meta1 = sm.meta[wave][1];
 
@@ -606,10 +614,11 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   // that the number of loads in flight does not depend on the path taken and
   // the waits before each slot's use stay exact.
   auto load_tile = [&](Slot& sl, int ti) {
-    const int T0 = t0 + tile_of(min(ti, nk - 1)) * kTile;
+    const int T0 = __builtin_amdgcn_readfirstlane(t0 + tile_of(min(ti, nk - 1)) * kTile);
+    const uint8_t* ktile = kpair + size_t(T0) * KB;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const uint8_t* row = kbase + size_t(T0 + tok<BITS>(t, m >> 2, m & 3)) * KB;
+      const uint8_t* row = ktile + koff[t];
       if constexpr (KSPLIT) {
         load_bytes<16, kStreamNT>(row, sl.kw[t]);
         load_bytes<16, kStreamNT>(row + 64, sl.kw[t] + 4);
@@ -617,8 +626,7 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
         load_bytes<LKB, kStreamNT>(row, sl.kw[t]);
       }
     }
-    const int blk = T0 / TB + (BITS == 2 ? (r >> 1) : r);
-    const uint8_t* vb = vbase + (size_t(blk) * D + VW * m) * VWB;
+    const uint8_t* vb = vpair + size_t(T0 / TB) * D * VWB + voff;
 #pragma unroll
     for (int p = 0; p < NVL; ++p) load_bytes<16, kStreamNT>(vb + size_t(p) * 16 * VW * VWB, sl.vw + 4 * p);
     // metadata: lanes 0-31 the Key (or Value scale) half, lanes 32-63 the
