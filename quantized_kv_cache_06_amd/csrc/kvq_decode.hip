@@ -60,10 +60,15 @@ constexpr int kMaxSplits = kMaxDecodeSplits;  // quantized splits per sequence (
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr uint32_t kMagic128 = 0x43004300u;  // two bf16 128.0
 // Tuning knobs (compile-time; the defaults are the measured best on MI355X):
-// non-temporal loads for the streamed cache codes, the 64-byte Key pieces of
-// 8-bit codes at d = 128, and the prefetch ring depth.
+// non-temporal loads for the streamed cache codes and for the per-token
+// scales and zero-points (each byte is read once per call; KIVI's Key group
+// parameters, re-read by every tile of a group, stay temporal), the 64-byte
+// Key pieces of 8-bit codes at d = 128, and the prefetch ring depth.
 #ifndef KVQ_DECODE_NT
-#define KVQ_DECODE_NT 0
+#define KVQ_DECODE_NT 1
+#endif
+#ifndef KVQ_DECODE_NT_META
+#define KVQ_DECODE_NT_META 1
 #endif
 #ifndef KVQ_DECODE_KSPLIT
 #define KVQ_DECODE_KSPLIT 1
@@ -80,6 +85,7 @@ constexpr uint32_t kMagic128 = 0x43004300u;  // two bf16 128.0
 #define KVQ_DECODE_MIN_WG_PER_CU 0
 #endif
 constexpr bool kStreamNT = KVQ_DECODE_NT != 0;
+constexpr bool kMetaNT = KVQ_DECODE_NT_META != 0;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -633,17 +639,18 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
     // Value (or Value zero) half, NVG floats per lane
     const int part = lane >> 5, qi = lane & 31;
     if constexpr (!KIVI) {
-      sl.mw[0] = (part ? cv.v_scale : cv.k_scale)[pair * cv.cap + T0 + qi];
+      sl.mw[0] = load_vec<float, kMetaNT>(
+          reinterpret_cast<const uint8_t*>((part ? cv.v_scale : cv.k_scale) + (pair * cv.cap + T0 + qi)));
     } else {
       const float* src = (part ? cv.v_zero : cv.v_scale) + (pair * cv.cap + T0 + qi) * NVG;
       if constexpr (NVG == 4) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(src);
+        const f32x4 x = load_vec<f32x4, kMetaNT>(reinterpret_cast<const uint8_t*>(src));
         sl.mw[0] = x[0]; sl.mw[1] = x[1]; sl.mw[2] = x[2]; sl.mw[3] = x[3];
       } else if constexpr (NVG == 2) {
-        const f32x2 x = *reinterpret_cast<const f32x2*>(src);
+        const f32x2 x = load_vec<f32x2, kMetaNT>(reinterpret_cast<const uint8_t*>(src));
         sl.mw[0] = x[0]; sl.mw[1] = x[1];
       } else {
-        sl.mw[0] = src[0];
+        sl.mw[0] = load_vec<float, kMetaNT>(reinterpret_cast<const uint8_t*>(src));
       }
       // the group parameters of the tile's group (used when it opens one)
       const float* gsrc = (part ? cv.k_zero : cv.k_scale) + (pair * (cv.cap / GG) + T0 / GG) * D + qi * KGL;
