@@ -619,7 +619,12 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   // clamped to its last tile, whose bytes are then re-read from cache) so
   // that the number of loads in flight does not depend on the path taken and
   // the waits before each slot's use stay exact.
-  auto load_tile = [&](Slot& sl, int ti) {
+  // uc: the ring slot (compile time). With NPF a multiple of TPG a slot
+  // only ever holds the same tile of its group, so only the slots of a
+  // group's first tile load the Key group parameters.
+  auto load_tile = [&](Slot& sl, int ti, auto uc) {
+    constexpr int U = decltype(uc)::value;
+    constexpr bool kGroupLoad = NPF % TPG != 0 || U % TPG == 0;
     const int T0 = __builtin_amdgcn_readfirstlane(t0 + tile_of(min(ti, nk - 1)) * kTile);
     const uint8_t* ktile = kpair + size_t(T0) * KB;
 #pragma unroll
@@ -653,13 +658,15 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
         sl.mw[0] = load_vec<float, kMetaNT>(reinterpret_cast<const uint8_t*>(src));
       }
       // the group parameters of the tile's group (used when it opens one)
-      const float* gsrc = (part ? cv.k_zero : cv.k_scale) + (pair * (cv.cap / GG) + T0 / GG) * D + qi * KGL;
-      if constexpr (KGL == 4) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(gsrc);
-        sl.gw[0] = x[0]; sl.gw[1] = x[1]; sl.gw[2] = x[2]; sl.gw[3] = x[3];
-      } else {
-        const f32x2 x = *reinterpret_cast<const f32x2*>(gsrc);
-        sl.gw[0] = x[0]; sl.gw[1] = x[1];
+      if constexpr (kGroupLoad) {
+        const float* gsrc = (part ? cv.k_zero : cv.k_scale) + (pair * (cv.cap / GG) + T0 / GG) * D + qi * KGL;
+        if constexpr (KGL == 4) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(gsrc);
+          sl.gw[0] = x[0]; sl.gw[1] = x[1]; sl.gw[2] = x[2]; sl.gw[3] = x[3];
+        } else {
+          const f32x2 x = *reinterpret_cast<const f32x2*>(gsrc);
+          sl.gw[0] = x[0]; sl.gw[1] = x[1];
+        }
       }
     }
   };
@@ -684,7 +691,7 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
       load_elems<BF16, CPL>(q, qrow + CPL * r, qx);
     }
   }
-  if (nk > 0) static_for<NPF>([&](auto uc) { load_tile(ring[decltype(uc)::value], decltype(uc)::value); });
+  if (nk > 0) static_for<NPF>([&](auto uc) { load_tile(ring[decltype(uc)::value], decltype(uc)::value, uc); });
 
   // ---- query, part 2: KIVI stages q in LDS and keeps its share of the
   // normalized query (below); the others build the operand
@@ -953,7 +960,7 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
         constexpr int U = decltype(uc)::value;
         const int ti = base + U;
         if (ti < nk) process(ring[U], ti);
-        load_tile(ring[U], ti + NPF);
+        load_tile(ring[U], ti + NPF, uc);
       });
     }
   }
