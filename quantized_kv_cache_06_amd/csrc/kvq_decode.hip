@@ -68,7 +68,7 @@ constexpr uint32_t kMagic128 = 0x43004300u;  // two bf16 128.0
 #define KVQ_DECODE_NT 1
 #endif
 #ifndef KVQ_DECODE_NT_META
-#define KVQ_DECODE_NT_META 1
+#define KVQ_DECODE_NT_META 0
 #endif
 #ifndef KVQ_DECODE_KSPLIT
 #define KVQ_DECODE_KSPLIT 1
@@ -86,6 +86,7 @@ constexpr uint32_t kMagic128 = 0x43004300u;  // two bf16 128.0
 #endif
 constexpr bool kStreamNT = KVQ_DECODE_NT != 0;
 constexpr bool kMetaNT = KVQ_DECODE_NT_META != 0;
+constexpr int kCodeAux = kStreamNT ? 2 : 0;  // cache policy of the code loads (2: non-temporal)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -487,6 +488,23 @@ __device__ __forceinline__ float get_partial(const float* p) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t n) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, int(n), 0x00020000);
 }
+// NB bytes (4, 8, 16 or 32) from buffer r at vector offset vo plus scalar
+// offset so. Bytes outside the buffer's range read as 0 and are not fetched.
+template <int NB, int AUX>
+__device__ __forceinline__ void buffer_bytes(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so, uint32_t* w) {
+  if constexpr (NB == 32) {
+    buffer_bytes<16, AUX>(r, vo, so, w);
+    buffer_bytes<16, AUX>(r, vo + 16, so, w + 4);
+  } else if constexpr (NB == 16) {
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, AUX);
+    w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
+  } else if constexpr (NB == 8) {
+    const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, AUX);
+    w[0] = a[0]; w[1] = a[1];
+  } else {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, vo, so, AUX);
+  }
+}
 // 16-byte partial loads and stores with the same device-scope coherence as
 // put_partial / get_partial (cache policy sc1).
 constexpr int kCoherent = 16;
@@ -602,6 +620,12 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
 #pragma unroll
   for (int t = 0; t < 2; ++t) koff[t] = uint32_t(tok<BITS>(t, m >> 2, m & 3) * KB + (KSPLIT ? 16 * r : LKB * r));
   const uint32_t voff = uint32_t((size_t(BITS == 2 ? (r >> 1) : r) * D + VW * m) * VWB);
+  // the pair's code regions as buffers; a tile past the wave's run loads
+  // through an empty buffer (reads 0, fetches nothing), so the loads in
+  // flight stay the same on every path without re-reading bytes
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(kpair, uint32_t(size_t(cv.cap) * KB));
+  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(vpair, uint32_t(size_t(cv.cap / TB) * D * VWB));
+  const __amdgpu_buffer_rsrc_t none = buffer_rsrc(kpair, 0u);
   float* meta0 = sm.meta[wave][0];
   float* meta1 = sm.meta[wave][1];
 
@@ -626,20 +650,22 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
     constexpr int U = decltype(uc)::value;
     constexpr bool kGroupLoad = NPF % TPG != 0 || U % TPG == 0;
     const int T0 = __builtin_amdgcn_readfirstlane(t0 + tile_of(min(ti, nk - 1)) * kTile);
-    const uint8_t* ktile = kpair + size_t(T0) * KB;
+    const bool live = ti < nk;  // uniform
+    const __amdgpu_buffer_rsrc_t kr = live ? krs : none;
+    const __amdgpu_buffer_rsrc_t vr = live ? vrs : none;
+    const uint32_t ks = uint32_t(T0) * KB;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const uint8_t* row = ktile + koff[t];
       if constexpr (KSPLIT) {
-        load_bytes<16, kStreamNT>(row, sl.kw[t]);
-        load_bytes<16, kStreamNT>(row + 64, sl.kw[t] + 4);
+        buffer_bytes<16, kCodeAux>(kr, koff[t], ks, sl.kw[t]);
+        buffer_bytes<16, kCodeAux>(kr, koff[t] + 64, ks, sl.kw[t] + 4);
       } else {
-        load_bytes<LKB, kStreamNT>(row, sl.kw[t]);
+        buffer_bytes<LKB, kCodeAux>(kr, koff[t], ks, sl.kw[t]);
       }
     }
-    const uint8_t* vb = vpair + size_t(T0 / TB) * D * VWB + voff;
+    const uint32_t vs = uint32_t(T0 / TB) * D * VWB;
 #pragma unroll
-    for (int p = 0; p < NVL; ++p) load_bytes<16, kStreamNT>(vb + size_t(p) * 16 * VW * VWB, sl.vw + 4 * p);
+    for (int p = 0; p < NVL; ++p) buffer_bytes<16, kCodeAux>(vr, voff + uint32_t(p * 16 * VW * VWB), vs, sl.vw + 4 * p);
     // metadata: lanes 0-31 the Key (or Value scale) half, lanes 32-63 the
     // Value (or Value zero) half, NVG floats per lane
     const int part = lane >> 5, qi = lane & 31;
