@@ -460,11 +460,9 @@ constexpr size_t smem_floats_split() {
   return (sizeof(SmemQuant<D>) > sizeof(SmemResid<D>) ? sizeof(SmemQuant<D>) : sizeof(SmemResid<D>)) /
          sizeof(float);
 }
-// ... and the merge's (max, sum) table of up to 8 heads x (kMaxSplits + 1) slots
 template <int D>
 constexpr size_t smem_floats() {
-  constexpr size_t merge = 2 * 8 * (kMaxSplits + 1) + 8;
-  return smem_floats_split<D>() > merge ? smem_floats_split<D>() : merge;
+  return smem_floats_split<D>();
 }
 
 // Row of one partial state (unnormalized output, log2-domain maximum and
@@ -1227,62 +1225,59 @@ __global__ __launch_bounds__(kThreads, (min_wg_per_cu<FMT, BITS, D, G>())) void 
   __syncthreads();
   if (ticket != uint32_t(nact - 1)) return;
 
-  // Merge. Thread (j, c4) owns channels [4 c4, 4 c4 + 4) of head j and
-  // loads its partial outputs of up to kMergeBatch splits at a time with
-  // 16-byte coherent loads; the first batch is issued together with the
-  // gather of every split's (max, sum) into LDS, so a call with at most
-  // kMergeBatch splits merges in one round trip. The (max, sum) table turns
-  // into weights exp2(m - M) and 1 / L per head.
-  // nact <= kMaxSplits + 1 (the host caps the split count).
+  // Merge by the log-sum-exp rule. Thread (j, c4) owns channels [4 c4,
+  // 4 c4 + 4) of head j. For up to kMergeBatch pieces at a time it loads,
+  // in one batch of coherent loads, its 16 bytes of every piece's partial
+  // output and the piece's (max, sum) of head j, and folds them into a
+  // running (max, sum, output); at most kMergeBatch pieces merge in one
+  // round trip, with no barrier. nact <= kMaxSplits + 1.
   constexpr int kMergeBatch = 16;
   constexpr int C4 = D / 4;
-  float* wgt = smem;                     // [g][nact] maxima, then weights
-  float* lsm = smem + 8 * (kMaxSplits + 1);  // [g][nact] sums
-  float* inv = lsm + 8 * (kMaxSplits + 1);   // [g] 1 / L
   auto slot = [&](int k) { return k < nsq ? k : wk.S - 1; };
   const int tm = fresh(tid);
   const int j = tm / C4, c4 = tm % C4;
-  const bool mine = j < g;
+  const int jc = min(j, g - 1);
   const size_t row0 = partial_row(cv, wk, b, h, 0, 0);
+  const size_t mrow = row0 + size_t(jc) * wk.S;
   const __amdgpu_buffer_rsrc_t orsrc = buffer_rsrc(wk.o + row0 * D, uint32_t(g * wk.S * D * 4));
-  const uint32_t obase = uint32_t((size_t(min(j, g - 1)) * wk.S * D + 4 * c4) * 4);
-  f32x4 ov[kMergeBatch];
-  auto load_batch = [&](int k0) {
-#pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u)
-      ov[u] = get_partial4(orsrc, obase + uint32_t(slot(min(k0 + u, nact - 1)) * D * 4));
-  };
-  load_batch(0);
-  for (int e = tid; e < g * nact; e += kThreads) {
-    const int jj = e / nact, k = e % nact;
-    const size_t r = row0 + size_t(jj) * wk.S + slot(k);
-    wgt[e] = get_partial(&wk.m[r]);
-    lsm[e] = get_partial(&wk.l[r]);
-  }
-  __syncthreads();
-  if (tid < g) {
-    float M = -INFINITY;
-    for (int k = 0; k < nact; ++k) M = fmaxf(M, wgt[tid * nact + k]);
-    float L = 0.0f;
-    for (int k = 0; k < nact; ++k) {
-      const float w = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(wgt[tid * nact + k] - M);
-      wgt[tid * nact + k] = w;
-      L = fmaf(lsm[tid * nact + k], w, L);
-    }
-    inv[tid] = L > 0.0f ? 1.0f / L : 0.0f;
-  }
-  __syncthreads();
+  const uint32_t obase = uint32_t((size_t(jc) * wk.S * D + 4 * c4) * 4);
+  float M = -INFINITY, L = 0.0f;
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int k0 = 0; k0 < nact; k0 += kMergeBatch) {
-    if (k0 > 0) load_batch(k0);
-    if (mine) {
+    f32x4 ov[kMergeBatch];
+    float mv[kMergeBatch], lv[kMergeBatch];
 #pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u)
-        if (k0 + u < nact) acc += ov[u] * wgt[j * nact + k0 + u];
+    for (int u = 0; u < kMergeBatch; ++u) {
+      if (k0 + u < nact) {
+        const int sl = slot(k0 + u);
+        ov[u] = get_partial4(orsrc, obase + uint32_t(sl * D * 4));
+        mv[u] = get_partial(&wk.m[mrow + sl]);
+        lv[u] = get_partial(&wk.l[mrow + sl]);
+      } else {
+        ov[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        mv[u] = -INFINITY;
+        lv[u] = 0.0f;
+      }
+    }
+    float mn = M;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) mn = fmaxf(mn, mv[u]);
+    if (mn != -INFINITY) {
+      const float a = __builtin_amdgcn_exp2f(M - mn);  // 0 while nothing is merged yet
+      acc *= a;
+      L *= a;
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const float w = __builtin_amdgcn_exp2f(mv[u] - mn);  // 0 for empty pieces
+        acc += ov[u] * w;
+        L = fmaf(lv[u], w, L);
+      }
+      M = mn;
     }
   }
-  if (mine)
-    *reinterpret_cast<f32x4*>(&out[(size_t(b) * cv.Hq + size_t(h) * g + j) * D + 4 * c4]) = acc * inv[j];
+  if (j < g)
+    *reinterpret_cast<f32x4*>(&out[(size_t(b) * cv.Hq + size_t(h) * g + j) * D + 4 * c4]) =
+        acc * (L > 0.0f ? 1.0f / L : 0.0f);
   if (tid == 0) __hip_atomic_store(&wk.count[pair], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
