@@ -2,7 +2,8 @@
 
 A step is one decode iteration over every cache copy ("layer"): append one
 new K/V token per sequence (quantize, or residual write + group flush) and
-run decode attention over the whole cache. Workload 2 (FP8 E4M3 per-token,
+run decode attention over the whole cache, as one fused launch per layer
+(kvq_append_decode; --unfused times the two separate calls instead). Workload 2 (FP8 E4M3 per-token,
 batch 16, 8 KV heads, 32 query heads, head_dim 128, 4096 tokens) is the
 default; its 139 MB cache fits in the 256 MB Infinity Cache, so the step
 rotates over enough independent copies to touch >= 2 GB. Workload 5 runs its
@@ -44,6 +45,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--decode-rounds", type=int, default=20, help="passes over all copies in the decode-only timing")
+    p.add_argument("--unfused", action="store_true",
+                   help="time the step as kvq_quantize_append + kvq_decode_attention (two calls per layer)")
     p.add_argument("--stream-ref", type=float, default=0.0,
                    help="instead of the hot path: time torch's copy and sum over this many GiB (the "
                         "attainable streaming bandwidth, and the plain copy used to scale HBM counters)")
@@ -112,6 +115,7 @@ def workload_key(w):
 
 
 DECODE_SOURCES = ("quantized_kv_cache_06_amd/csrc/kvq_decode.hip", "quantized_kv_cache_06_amd/csrc/kvq_device.h",
+                  "quantized_kv_cache_06_amd/csrc/kvq_quant.h",
                   "quantized_kv_cache_06_amd/csrc/kvq_internal.h", "include/kvq.h")
 
 
@@ -276,8 +280,12 @@ def main():
 
     def step(s):
         for c in range(copies):
-            kvq.kvq_quantize_append(cfg, caches[c], seq_lens[c], new_k[c][s], new_v[c][s], 1)
-            decode(c)
+            if args.unfused:
+                kvq.kvq_quantize_append(cfg, caches[c], seq_lens[c], new_k[c][s], new_v[c][s], 1)
+                decode(c)
+            else:
+                kvq.kvq_append_decode(cfg, caches[c], seq_lens[c], new_k[c][s], new_v[c][s], qs[c], sm, outs[c],
+                                      ws_list[0], ws_bytes, args.split)
 
     for s in range(args.warmup):
         step(s)
@@ -353,6 +361,9 @@ def main():
         "decode_gbps": round(achieved, 2),
         "decode_pct_of_peak": round(100 * achieved / HBM_PEAK_GBPS, 2),
         "decode_us_per_call": round(dec_avg_ms * 1e3, 2),
+        "step": "one launch per layer (append + decode fused)" if not args.unfused else
+                "two calls per layer (append, then decode)",
+        "step_us_per_layer": round(total_ms * 1e3 / (args.steps * copies), 2),
         "decode_tokens_per_s_per_layer": round(w.batch * copies * args.steps / (total_ms * 1e-3), 1),
         "append_tokens_per_s_streaming": round(w.batch * copies * args.steps / (total_ms * 1e-3), 1),
         "append_bulk_tokens_per_s": round(bulk_tokens / (bulk_ms * 1e-3), 1),

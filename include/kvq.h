@@ -179,10 +179,10 @@ int32_t kvq_quantize_append(const kvq_config* cfg, void* cache, int32_t* seq_len
  * the device. For split_tokens > 0 it holds n = ceil(max_tokens /
  * split_tokens) splits; for 0 it holds n = min(128, max(1, max_tokens /
  * 256)) splits, the most the library's choice can take on any device. The
- * workspace starts with batch * n_kv_heads uint32 arrival counters (see
- * kvq_decode_attention for the zero-fill rule), then per (sequence, query
- * head) n + 1 partial rows of head_dim + 2 fp32, each array 256-byte
- * aligned. Errors: KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED (split_tokens not a
+ * workspace starts with batch * (n_kv_heads + 1) uint32 arrival counters
+ * (see kvq_decode_attention for the zero-fill rule), then per (sequence,
+ * query head) n + 1 partial rows of head_dim + 2 fp32, each array 256-byte
+ * aligned. kvq_append_decode takes the same workspace. Errors: KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED (split_tokens not a
  * positive multiple of 64, or more than 128 splits of max_tokens). */
 int32_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t split_tokens, uint64_t* bytes);
 
@@ -200,8 +200,8 @@ int32_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t split_tokens, 
  *  sm_scale     softmax scale applied to the dot products (1/sqrt(d) is usual).
  *  out          device fp32 [B][Hq][d], written.
  *  workspace    device scratch of at least kvq_decode_workspace_bytes(cfg,
- *               split_tokens) bytes. Its first batch * n_kv_heads uint32
- *               (the arrival counters) must be zero on entry: zero-fill the
+ *               split_tokens) bytes. Its first batch * (n_kv_heads + 1)
+ *               uint32 (the arrival counters) must be zero on entry: zero-fill the
  *               workspace once after allocating it (or when batch or
  *               n_kv_heads change); every call leaves them zero when it
  *               completes. The rest is scratch. Calls that overlap in time
@@ -218,6 +218,38 @@ int32_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t split_tokens, 
 int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache, const int32_t* seq_lens,
                              const void* q, float sm_scale, float* out, void* workspace,
                              uint64_t workspace_bytes, int32_t split_tokens, void* stream);
+
+/* One decode step in one launch: appends one new K/V token to every
+ * sequence and then attends over the grown cache. The result equals
+ * kvq_quantize_append(cfg, cache, seq_lens, k_new, v_new, 1, NULL, stream)
+ * followed by kvq_decode_attention(cfg, cache, seq_lens, q, ...) on the
+ * same stream: the same codes, scales, zero-points, residual rows and
+ * seq_lens bit for bit, and the same attention up to fp32 rounding order.
+ * Sources: [N4N] "Step 5: Integrate with your inference engine" (the
+ * attention forward pass appends the step's K, V and then reads the cache);
+ * [LLMS] "Serving Economics and Latency Trade-Offs" (scale computation and
+ * bit-packing add latency unless fused into a kernel; said there of
+ * prefill, applied here to the one-token decode append).
+ *  cache        device, one layer's cache; modified (the new token, and for
+ *               KIVI a group that it completes, as the append stores them).
+ *  seq_lens     device int32 [B]; a sequence with 0 <= seq_lens[b] <
+ *               max_tokens takes the token and its length is advanced by
+ *               one inside the launch; any other sequence is left unchanged
+ *               and attention reads it as kvq_decode_attention does.
+ *  k_new,v_new  device [B][Hkv][1][d] in cfg->in_dtype: the new token.
+ *  q, sm_scale, out, workspace, workspace_bytes, split_tokens: as in
+ *               kvq_decode_attention (the same workspace size and zero-fill
+ *               rule). q must not alias cache, k_new or v_new.
+ * FP8/INT8: the new token is quantized by the slot that also attends to
+ * it. KIVI: the residual-window workgroup writes the token to its ring slot
+ * (or, with a zero window, straight into the group it completes) and, when a
+ * group completes, quantizes and packs it and attends over its dequantized
+ * codes. Calls that overlap in time on one cache or one workspace race.
+ * Errors: KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE,
+ * KVQ_ERR_HIP. */
+int32_t kvq_append_decode(const kvq_config* cfg, void* cache, int32_t* seq_lens, const void* k_new,
+                          const void* v_new, const void* q, float sm_scale, float* out, void* workspace,
+                          uint64_t workspace_bytes, int32_t split_tokens, void* stream);
 
 #ifdef __cplusplus
 }

@@ -16,7 +16,7 @@ __all__ = [
     "FMT_FP8_E4M3", "FMT_INT8", "FMT_KIVI", "DT_F32", "DT_BF16",
     "KvqConfig", "KvqLayout", "KvqError", "LIB_PATH", "lib", "make_config",
     "kvq_status_string", "kvq_version", "kvq_get_layout", "kvq_quantize_append",
-    "kvq_decode_workspace_bytes", "kvq_decode_attention",
+    "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_append_decode",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -72,6 +72,9 @@ def lib() -> ctypes.CDLL:
         L.kvq_decode_attention.argtypes = [cfgp, P, P, P, ctypes.c_float, P, P, ctypes.c_uint64,
                                            ctypes.c_int32, P]
         L.kvq_decode_attention.restype = ctypes.c_int32
+        L.kvq_append_decode.argtypes = [cfgp, P, P, P, P, P, ctypes.c_float, P, P, ctypes.c_uint64,
+                                        ctypes.c_int32, P]
+        L.kvq_append_decode.restype = ctypes.c_int32
         _lib = L
     return _lib
 
@@ -164,3 +167,23 @@ def kvq_decode_attention(cfg: KvqConfig, cache, seq_lens, q, sm_scale: float, ou
         _addr(workspace, workspace_bytes, "workspace"), int(workspace_bytes), int(split_tokens),
         _stream(stream))
     _check(st, "kvq_decode_attention")
+
+
+def kvq_append_decode(cfg: KvqConfig, cache, seq_lens, k_new, v_new, q, sm_scale: float, out, workspace,
+                      workspace_bytes: Optional[int] = None, split_tokens: int = 0, stream=None) -> None:
+    """One decode step in one launch: append the one new K/V token per
+    sequence (k_new, v_new shaped [B, Hkv, 1, d]) and attend over the grown
+    cache; seq_lens advances on the device. Same workspace rules as
+    kvq_decode_attention."""
+    lay = kvq_get_layout(cfg)
+    if workspace_bytes is None:
+        workspace_bytes = (workspace.numel() * workspace.element_size()
+                           if not isinstance(workspace, int) else kvq_decode_workspace_bytes(cfg, split_tokens))
+    n_q = cfg.batch * cfg.n_q_heads * cfg.head_dim
+    n_in = cfg.batch * cfg.n_kv_heads * cfg.head_dim * _elem(cfg)
+    st = lib().kvq_append_decode(
+        ctypes.byref(cfg), _addr(cache, lay.total_bytes, "cache"), _addr(seq_lens, 4 * cfg.batch, "seq_lens"),
+        _addr(k_new, n_in, "k_new"), _addr(v_new, n_in, "v_new"), _addr(q, n_q * _elem(cfg), "q"),
+        ctypes.c_float(sm_scale), _addr(out, n_q * 4, "out"), _addr(workspace, workspace_bytes, "workspace"),
+        int(workspace_bytes), int(split_tokens), _stream(stream))
+    _check(st, "kvq_append_decode")

@@ -155,13 +155,62 @@ int32_t split_bound(const kvq_config* c, int32_t split_tokens, int* n) {
   return KVQ_OK;
 }
 
-// Workspace: [B][Hkv] uint32 arrival counters first (they must read zero on
-// entry; each call leaves them zero), then the partial states o, m, l.
-uint64_t counter_bytes(const kvq_config* c) { return align256(uint64_t(c->batch) * c->n_kv_heads * 4); }
+// Workspace: [B][Hkv] uint32 arrival counters and [B] per-sequence counters
+// (fused calls) first (they must read zero on entry; each call leaves them
+// zero), then the partial states o, m, l.
+uint64_t counter_bytes(const kvq_config* c) {
+  return align256((uint64_t(c->batch) * c->n_kv_heads + uint64_t(c->batch)) * 4);
+}
 
 uint64_t workspace_bytes(const kvq_config* c, int S) {
   const uint64_t rows = uint64_t(c->batch) * c->n_q_heads * S;
   return counter_bytes(c) + align256(rows * c->head_dim * 4) + align256(rows * 4) + align256(rows * 4);
+}
+
+}  // namespace
+
+namespace {
+
+// Shared by kvq_decode_attention and kvq_append_decode: checks the decode
+// arguments, plans the splits, lays out the workspace and launches.
+int32_t decode_call(const kvq_config* cfg, const void* cache, const int32_t* seq_lens, const void* q, float sm_scale,
+                    float* out, void* workspace, uint64_t ws_bytes, int32_t split_tokens, const kvq::AppendIn* app,
+                    void* stream) {
+  const int32_t st = validate(cfg);
+  if (st != KVQ_OK) return st;
+  if (!cache || !seq_lens || !q || !out || !workspace) return KVQ_ERR_INVALID;
+  if (!aligned16(cache) || !aligned16(q) || !aligned16(out) || !aligned16(workspace) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3))
+    return KVQ_ERR_INVALID;
+  if (app && (!app->k || !app->v || !aligned16(app->k) || !aligned16(app->v))) return KVQ_ERR_INVALID;
+  if (!(sm_scale == sm_scale) || sm_scale > 3.0e38f || sm_scale < -3.0e38f) return KVQ_ERR_INVALID;
+  int n;
+  const int32_t sp = split_bound(cfg, split_tokens, &n);
+  if (sp != KVQ_OK) return sp;
+  if (ws_bytes < workspace_bytes(cfg, n + 1)) return KVQ_ERR_WORKSPACE;
+  kvq_layout lay;
+  make_layout(cfg, &lay);
+  const kvq::CacheView v = make_view(cfg, lay, cache);
+  if (split_tokens == 0) {
+    const int resident = kvq::decode_resident_workgroups(v);
+    const int cus = kvq::decode_compute_units();
+    if (resident <= 0 || cus <= 0) return KVQ_ERR_HIP;
+    n = auto_split(cfg, resident, cus);
+  }
+  const int S = n + 1;
+  const uint64_t rows = uint64_t(cfg->batch) * cfg->n_q_heads * S;
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  kvq::DecodeWork work;
+  work.count = reinterpret_cast<uint32_t*>(w);
+  work.bcount = work.count + uint64_t(cfg->batch) * cfg->n_kv_heads;
+  w += counter_bytes(cfg);
+  work.o = reinterpret_cast<float*>(w);
+  work.m = reinterpret_cast<float*>(w + align256(rows * cfg->head_dim * 4));
+  work.l = reinterpret_cast<float*>(w + align256(rows * cfg->head_dim * 4) + align256(rows * 4));
+  work.S = S;
+  const hipError_t e =
+      kvq::launch_decode(v, seq_lens, q, sm_scale, out, work, app, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
 }  // namespace
@@ -222,38 +271,15 @@ int32_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t split_tokens, 
 int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache, const int32_t* seq_lens, const void* q,
                              float sm_scale, float* out, void* workspace, uint64_t ws_bytes,
                              int32_t split_tokens, void* stream) {
-  const int32_t st = validate(cfg);
-  if (st != KVQ_OK) return st;
-  if (!cache || !seq_lens || !q || !out || !workspace) return KVQ_ERR_INVALID;
-  if (!aligned16(cache) || !aligned16(q) || !aligned16(out) || !aligned16(workspace) ||
-      (reinterpret_cast<uintptr_t>(seq_lens) & 3))
-    return KVQ_ERR_INVALID;
-  if (!(sm_scale == sm_scale) || sm_scale > 3.0e38f || sm_scale < -3.0e38f) return KVQ_ERR_INVALID;
-  int n;
-  const int32_t sp = split_bound(cfg, split_tokens, &n);
-  if (sp != KVQ_OK) return sp;
-  if (ws_bytes < workspace_bytes(cfg, n + 1)) return KVQ_ERR_WORKSPACE;
-  kvq_layout lay;
-  make_layout(cfg, &lay);
-  const kvq::CacheView v = make_view(cfg, lay, cache);
-  if (split_tokens == 0) {
-    const int resident = kvq::decode_resident_workgroups(v);
-    const int cus = kvq::decode_compute_units();
-    if (resident <= 0 || cus <= 0) return KVQ_ERR_HIP;
-    n = auto_split(cfg, resident, cus);
-  }
-  const int S = n + 1;
-  const uint64_t rows = uint64_t(cfg->batch) * cfg->n_q_heads * S;
-  uint8_t* w = static_cast<uint8_t*>(workspace);
-  kvq::DecodeWork work;
-  work.count = reinterpret_cast<uint32_t*>(w);
-  w += counter_bytes(cfg);
-  work.o = reinterpret_cast<float*>(w);
-  work.m = reinterpret_cast<float*>(w + align256(rows * cfg->head_dim * 4));
-  work.l = reinterpret_cast<float*>(w + align256(rows * cfg->head_dim * 4) + align256(rows * 4));
-  work.S = S;
-  const hipError_t e = kvq::launch_decode(v, seq_lens, q, sm_scale, out, work, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+  return decode_call(cfg, cache, seq_lens, q, sm_scale, out, workspace, ws_bytes, split_tokens, nullptr, stream);
+}
+
+int32_t kvq_append_decode(const kvq_config* cfg, void* cache, int32_t* seq_lens, const void* k_new,
+                          const void* v_new, const void* q, float sm_scale, float* out, void* workspace,
+                          uint64_t ws_bytes, int32_t split_tokens, void* stream) {
+  if (!k_new || !v_new || !seq_lens) return KVQ_ERR_INVALID;
+  const kvq::AppendIn app{seq_lens, k_new, v_new};
+  return decode_call(cfg, cache, seq_lens, q, sm_scale, out, workspace, ws_bytes, split_tokens, &app, stream);
 }
 
 }  // extern "C"

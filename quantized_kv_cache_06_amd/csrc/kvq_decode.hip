@@ -46,7 +46,7 @@
 
 #include <type_traits>
 
-#include "kvq_device.h"
+#include "kvq_quant.h"
 
 namespace kvq {
 namespace {
@@ -440,9 +440,12 @@ __device__ __forceinline__ u32x4 mask_tokens8(u32x4 a, int r, int valid) {
 template <int D>
 struct SmemQuant {
   float q[8][D];              // query of the GQA group (KIVI)
-  float o[kWaves][8][D];      // each wave's unnormalized output
-  float m[kWaves][8];
-  float l[kWaves][8];
+  // each wave's unnormalized output, maximum and sum; piece kWaves is the
+  // new token of a fused FP8/INT8 step
+  float o[kWaves + 1][8][D];
+  float m[kWaves + 1][8];
+  float l[kWaves + 1][8];
+  float xn[2][D];             // the new token's dequantized Key and Value rows
   // per-wave staging of a tile's metadata: per-token scales (8-bit
   // formats: [K | V][32 tokens]); KIVI: Value [scale | zero][32 * D/32]
   // and Key group [scale | zero][D]
@@ -455,14 +458,19 @@ struct SmemResid {
   float sc[8][kResidChunk];   // scores, then probabilities
   float st_m[8], st_l[8], st_a[8];
 };
-template <int D>
-constexpr size_t smem_floats_split() {
-  return (sizeof(SmemQuant<D>) > sizeof(SmemResid<D>) ? sizeof(SmemQuant<D>) : sizeof(SmemResid<D>)) /
-         sizeof(float);
-}
-template <int D>
+// The KIVI residual path of the fused append + decode step also flushes a
+// completed group (staged in LDS) before attending over it.
+template <int D, int G>
+struct SmemResidFused : SmemResid<D> {
+  FlushSmem<G, D> f;
+};
+template <int D, int G, bool FUSED>
+using SmemResidT = std::conditional_t<FUSED && (G > 0), SmemResidFused<D, (G > 0 ? G : 32)>, SmemResid<D>>;
+template <int D, int G, bool FUSED>
 constexpr size_t smem_floats() {
-  return smem_floats_split<D>();
+  return (sizeof(SmemQuant<D>) > sizeof(SmemResidT<D, G, FUSED>) ? sizeof(SmemQuant<D>)
+                                                                   : sizeof(SmemResidT<D, G, FUSED>)) /
+         sizeof(float);
 }
 
 // Row of one partial state (unnormalized output, log2-domain maximum and
@@ -530,6 +538,57 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // ---------------------------------------------------------------------------
+// Fused append + decode, FP8/INT8: the sequence's new token t (its length
+// before the call) is quantized by the append's own steps (wave 0 the Key
+// row, wave 1 the Value row) and stored at position t; it enters attention
+// as one more piece of the workgroup's wave merge: maximum = its score, sum
+// = 1, output = its dequantized Value row. Every load (the two new rows and
+// the query) is issued before the first barrier. Workgroup-collective.
+template <int FMT, int D, bool BF16>
+__device__ __forceinline__ void new_token_piece(const CacheView& cv, int b, int h, int t, const AppendIn& ap,
+                                                const void* __restrict__ q, float sm_log2, SmemQuant<D>& sm) {
+  constexpr int CPL = D / kWave;
+  constexpr int CPT = D / 32;  // channels per thread in the dot products (32 threads per head)
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int g = cv.g;
+  const size_t pair = pair_index(cv, b, h);
+  const int j = tid / 32, part = tid % 32;
+  float qx[CPT];
+  load_elems<BF16, CPT>(q, (size_t(b) * cv.Hq + size_t(h) * g + min(j, g - 1)) * D + part * CPT, qx);
+  if (wave < 2) {
+    float x[CPL];
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) x[e] = load_elem<BF16>(wave ? ap.v : ap.k, pair * D + lane * CPL + e);
+    float sc;
+    const uint32_t codes = quantize_token_lane<FMT, CPL>(x, &sc);
+    store_token_codes<CPL>(cv, pair, t, wave == 1, lane, codes, sc);
+    float c[2];  // the codes as values, exactly
+    if constexpr (FMT == KVQ_FMT_FP8_E4M3) {
+      const uint32_t w = fp8x2_bf16<0>(codes);
+      c[0] = bf_lo(w);
+      c[1] = bf_hi(w);
+    } else {
+      c[0] = float(int8_t(uint8_t(codes)));
+      c[1] = float(int8_t(uint8_t(codes >> 8)));
+    }
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) sm.xn[wave][lane * CPL + e] = c[e] * sc;
+  }
+  __syncthreads();
+  float dot = 0.0f;
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) dot = fmaf(qx[k], sm.xn[0][part * CPT + k], dot);
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) dot += __shfl_xor(dot, o, kWave);
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) sm.o[kWaves][j][part * CPT + k] = sm.xn[1][part * CPT + k];
+  if (part == 0) {
+    sm.m[kWaves][j] = j < g ? dot * sm_log2 : -INFINITY;
+    sm.l[kWaves][j] = 1.0f;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Quantized tokens [t0, t1) of one split: 4 waves on the matrix cores.
 // Every global load of a tile (codes, scales, zero-points, and the Key
 // group parameters when the tile opens a group) is issued one tile ahead in
@@ -537,10 +596,12 @@ __device__ __forceinline__ void wave_lds_sync() {
 // computes the current one; metadata is re-laid out through the wave's own
 // LDS area.
 // ---------------------------------------------------------------------------
-template <int FMT, int BITS, int D, int G, bool BF16>
+// With FUSED and t_new >= 0 (FP8/INT8), the fused step's new token t_new
+// joins the wave merge as a fifth piece (new_token_piece).
+template <int FMT, int BITS, int D, int G, bool BF16, bool FUSED>
 __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int h, int s, int t0, int t1,
                                                 const void* __restrict__ q, float sm_log2, const DecodeWork& wk,
-                                                SmemQuant<D>& sm) {
+                                                SmemQuant<D>& sm, int t_new, const AppendIn& ap) {
   constexpr bool KIVI = FMT == KVQ_FMT_KIVI;
   constexpr int CPL = D / 4;                  // channels per row group (score MFMA)
   // 8-bit codes at d = 128: row group r holds channels [16r, 16r+16) and
@@ -989,7 +1050,14 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
     }
   }
 
-  // ---- merge the 4 waves through LDS ----
+  // ---- the fused step's new token: a fifth piece ----
+  bool has_new = false;
+  if constexpr (FUSED && !KIVI) {
+    has_new = t_new >= 0;  // uniform
+    if (has_new) new_token_piece<FMT, D, BF16>(cv, b, h, t_new, ap, q, sm_log2, sm);
+  }
+
+  // ---- merge the 4 waves (and the new token) through LDS ----
   const float l_tot = sum_rows(l_run);
   float zt[NVG];
 #pragma unroll
@@ -1013,14 +1081,17 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   const int tm = fresh(tid);
   const int j = tm / C4, c4 = tm % C4;
   if (j < g) {
+    const int npiece = kWaves + (has_new ? 1 : 0);
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.m[w][j]);
+    for (int w = 0; w < kWaves + 1; ++w)
+      if (w < npiece) M = fmaxf(M, sm.m[w][j]);
     f32x4 ov = {0.0f, 0.0f, 0.0f, 0.0f};
     float L = 0.0f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < kWaves + 1; ++w) {
+        if (w >= npiece) break;
         const float f = __builtin_amdgcn_exp2f(sm.m[w][j] - M);
         ov += *reinterpret_cast<const f32x4*>(&sm.o[w][j][4 * c4]) * f;
         L += sm.l[w][j] * f;
@@ -1044,11 +1115,18 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
 // per token (a quarter of the row each, 16-byte loads, summed by
 // shuffles); the values take lane (channel pair, token part), the parts
 // summed by shuffles at the end. Writes partial slot s.
+//
+// Fused append + decode (FUSED, app): token n - 1 is the new input token.
+// It is written to its ring slot when it stays in the residual window, and
+// read from the input row. When it completes a group (the flush rule now
+// admits tokens [nq, nq + G)), that group is quantized here by the append's
+// own steps, and attention reads it as the dequantized codes, code * s + z,
+// exactly as an attention call after the append would.
 // ---------------------------------------------------------------------------
-template <int D, bool BF16>
+template <int D, bool BF16, int BITS, int G, bool FUSED>
 __device__ __forceinline__ void split_residual(const CacheView& cv, int b, int h, int s, int nq, int n,
                                                const void* __restrict__ q, float sm_log2, const DecodeWork& wk,
-                                               SmemResid<D>& sm) {
+                                               SmemResidT<D, G, FUSED>& sm, const AppendIn& ap, bool app) {
   constexpr int NH = 8;
   constexpr int T = kResidChunk;
   constexpr int QPT = kThreads / T;       // lanes per token in the score phase
@@ -1075,24 +1153,11 @@ __device__ __forceinline__ void split_residual(const CacheView& cv, int b, int h
   float acc[NH][2];
 #pragma unroll
   for (int j = 0; j < NH; ++j) acc[j][0] = acc[j][1] = 0.0f;
-  __syncthreads();
-  for (int cs = nq; cs < n; cs += T) {
-    const int nt = min(T, n - cs);
-    // the chunk's loads (ring slots are in bounds for any token index; the
-    // values of tokens past the chunk are zeroed below)
-    float kx[CPT];
-    load_elems<BF16, CPT>(cv.k_resid, (ring + size_t((cs + ti) % C)) * D + cq, kx);
-    float vx[TPP][2];
-#pragma unroll
-    for (int u = 0; u < TPP; ++u)
-      load_elems<BF16, 2>(cv.v_resid, (ring + size_t((cs + part + NP * u) % C)) * D + 2 * cp, vx[u]);
-    float sco[NH];
-#pragma unroll
-    for (int j = 0; j < NH; ++j) sco[j] = 0.0f;
-#pragma unroll
-    for (int k = 0; k < CPT; ++k)
-#pragma unroll
-      for (int j = 0; j < NH; ++j) sco[j] = fmaf(sm.q[j][cq + k], kx[k], sco[j]);
+
+  // Steps of one chunk of nt tokens: the lane's partial dot products (token
+  // ti) to scores, the online softmax update of every head, and the
+  // weighted Value sum (the lane's tokens part + NP u, channels 2 cp, 2 cp+1).
+  auto put_scores = [&](float (&sco)[NH], int nt) {
 #pragma unroll
     for (int o = 1; o < QPT; o <<= 1)
 #pragma unroll
@@ -1102,7 +1167,8 @@ __device__ __forceinline__ void split_residual(const CacheView& cv, int b, int h
       for (int j = 0; j < g && j < NH; ++j) sm.sc[j][ti] = sco[j] * sm_log2;
     }
     __syncthreads();
-    // online softmax of each head over the chunk, one token per lane
+  };
+  auto softmax_step = [&](int nt) {
     for (int j = wave; j < g; j += kWaves) {
       const float sc = lane < nt ? sm.sc[j][lane] : -INFINITY;
       const float mx = wave_max(sc);
@@ -1125,6 +1191,8 @@ __device__ __forceinline__ void split_residual(const CacheView& cv, int b, int h
       acc[j][0] *= a;
       acc[j][1] *= a;
     }
+  };
+  auto value_step = [&](const float (&vx)[TPP][2], int nt) {
 #pragma unroll
     for (int u = 0; u < TPP; ++u) {
       const int i = part + NP * u;
@@ -1138,6 +1206,97 @@ __device__ __forceinline__ void split_residual(const CacheView& cv, int b, int h
       }
     }
     __syncthreads();  // probability reads done before the next chunk's scores
+  };
+
+  int cs0 = nq;  // first token read from the ring
+  if constexpr (FUSED) {
+    if (app) {
+      const int t_new = n - 1;
+      const int nq1 = kivi_quantized(n, G, cv.R);
+      if (t_new >= nq1) {
+        // the new token stays in the residual window: its ring slot held a
+        // token older than nq, no longer read
+        constexpr int VPR = D * (BF16 ? 2 : 4) / 16;  // 16-byte vectors per row
+        if (tid < 2 * VPR) {
+          const int v = tid % VPR;
+          const uint8_t* src = static_cast<const uint8_t*>(tid < VPR ? ap.k : ap.v) + (pair * VPR + v) * 16;
+          uint8_t* dst = (tid < VPR ? cv.k_resid : cv.v_resid) + ((ring + size_t(t_new % C)) * VPR + v) * 16;
+          *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+        }
+      }
+      if (nq1 > nq) {
+        // the group [nq, nq + G) completes: flush it, then attend over it
+        constexpr float QMAX = float((1 << BITS) - 1);
+        static_assert(G <= T, "a group fits one chunk");
+        const int grp = nq / G;
+        FlushSmem<G, D>& f = sm.f;
+        flush_stage<BF16, G, D>(f, cv, pair, grp, t_new, ap.k, 1, cv.k_resid);
+        flush_key<BITS, G, D>(f, cv, pair, grp);
+        // the staged tile becomes the dequantized Key rows, code * s + z
+        for (int e = tid; e < G * D; e += kThreads) {
+          const int i = e / D, c = e % D;
+          f.xs[i][c] = float(asym_code(f.xs[i][c], f.sk[c], f.zk[c], QMAX)) * f.sk[c] + f.zk[c];
+        }
+        __syncthreads();
+        float sco[NH];
+#pragma unroll
+        for (int j = 0; j < NH; ++j) sco[j] = 0.0f;
+        if (ti < G) {
+#pragma unroll
+          for (int k = 0; k < CPT; ++k)
+#pragma unroll
+            for (int j = 0; j < NH; ++j) sco[j] = fmaf(sm.q[j][cq + k], f.xs[ti][cq + k], sco[j]);
+        }
+        put_scores(sco, G);
+        softmax_step(G);
+        flush_stage<BF16, G, D>(f, cv, pair, grp, t_new, ap.v, 1, cv.v_resid);
+        flush_value<BITS, G, D>(f, cv, pair, grp);
+        for (int e = tid; e < G * D; e += kThreads) {
+          const int i = e / D, c = e % D;
+          const float sv = f.sv[i][c / G], zv = f.zv[i][c / G];
+          f.xs[i][c] = float(asym_code(f.xs[i][c], sv, zv, QMAX)) * sv + zv;
+        }
+        __syncthreads();
+        float vx[TPP][2];
+#pragma unroll
+        for (int u = 0; u < TPP; ++u) {
+          const int i = min(part + NP * u, G - 1);
+          vx[u][0] = f.xs[i][2 * cp];
+          vx[u][1] = f.xs[i][2 * cp + 1];
+        }
+        value_step(vx, G);
+        cs0 = nq1;
+      }
+    }
+  }
+  __syncthreads();
+  // token t's row: its ring slot, or for the new token of a fused step the
+  // input row
+  auto row = [&](const uint8_t* ringp, const void* inp, int t) -> const void* {
+    if constexpr (FUSED) {
+      if (app && t == n - 1) return static_cast<const uint8_t*>(inp) + pair * D * (BF16 ? 2 : 4);
+    }
+    return ringp + (ring + size_t(t % C)) * D * (BF16 ? 2 : 4);
+  };
+  for (int cs = cs0; cs < n; cs += T) {
+    const int nt = min(T, n - cs);
+    // the chunk's loads (ring slots are in bounds for any token index; the
+    // values of tokens past the chunk are zeroed below)
+    float kx[CPT];
+    load_elems<BF16, CPT>(row(cv.k_resid, ap.k, cs + ti), cq, kx);
+    float vx[TPP][2];
+#pragma unroll
+    for (int u = 0; u < TPP; ++u) load_elems<BF16, 2>(row(cv.v_resid, ap.v, cs + part + NP * u), 2 * cp, vx[u]);
+    float sco[NH];
+#pragma unroll
+    for (int j = 0; j < NH; ++j) sco[j] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k)
+#pragma unroll
+      for (int j = 0; j < NH; ++j) sco[j] = fmaf(sm.q[j][cq + k], kx[k], sco[j]);
+    put_scores(sco, nt);
+    softmax_step(nt);
+    value_step(vx, nt);
   }
 #pragma unroll
   for (int o = 1; o < NP; o <<= 1)
@@ -1148,15 +1307,15 @@ __device__ __forceinline__ void split_residual(const CacheView& cv, int b, int h
     }
   if (part == 0) {
     for (int j = 0; j < g; ++j) {
-      const size_t row = partial_row(cv, wk, b, h, j, s) * D + 2 * cp;
-      put_partial(&wk.o[row], acc[j][0]);
-      put_partial(&wk.o[row + 1], acc[j][1]);
+      const size_t prow = partial_row(cv, wk, b, h, j, s) * D + 2 * cp;
+      put_partial(&wk.o[prow], acc[j][0]);
+      put_partial(&wk.o[prow + 1], acc[j][1]);
     }
   }
   if (tid < g) {
-    const size_t row = partial_row(cv, wk, b, h, tid, s);
-    put_partial(&wk.m[row], sm.st_m[tid]);
-    put_partial(&wk.l[row], sm.st_l[tid]);
+    const size_t prow = partial_row(cv, wk, b, h, tid, s);
+    put_partial(&wk.m[prow], sm.st_m[tid]);
+    put_partial(&wk.l[prow], sm.st_l[tid]);
   }
 }
 
@@ -1176,45 +1335,64 @@ constexpr int min_wg_per_cu() {
   return (FMT == KVQ_FMT_KIVI && BITS == 4 && D == 128 && G == 32) ? 2 : 3;
 }
 
-template <int FMT, int BITS, int D, int G, bool BF16>
-__global__ __launch_bounds__(kThreads, (min_wg_per_cu<FMT, BITS, D, G>())) void decode_split(CacheView cv, const int32_t* __restrict__ seq_lens,
+template <int FMT, int BITS, int D, int G, bool BF16, bool FUSED>
+__global__ __launch_bounds__(kThreads, (min_wg_per_cu<FMT, BITS, D, G>())) void decode_split(CacheView cv, const int32_t* seq_lens,
                                                         const void* __restrict__ q, float sm_log2, float* __restrict__ out,
-                                                        DecodeWork wk) {
+                                                        DecodeWork wk, AppendIn ap) {
   constexpr bool KIVI = FMT == KVQ_FMT_KIVI;
-  __shared__ float smem[smem_floats<D>()];
+  __shared__ float smem[smem_floats<D, G, FUSED>()];
   __shared__ uint32_t ticket;
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int g = cv.g;
-  const int n = min(max(seq_lens[b], 0), cv.max_tokens);
-  const int nq = KIVI ? kivi_quantized(n, G, cv.R) : n;
+  // Tokens in the cache, and for a fused step whether this sequence takes
+  // the new token (the append's rule: a valid length with room for one more;
+  // otherwise the sequence is left unchanged and attention reads it as is).
+  const int raw = seq_lens[b];
+  bool app = false;
+  if constexpr (FUSED) app = raw >= 0 && raw < cv.max_tokens;
+  const int n_cache = min(max(raw, 0), cv.max_tokens);
+  const int n = n_cache + (app ? 1 : 0);  // tokens attended
+  // quantized tokens the splits read (KIVI: the new token, and a group it
+  // completes, are handled by the residual slot)
+  const int nq = KIVI ? kivi_quantized(n_cache, G, cv.R) : n_cache;
   // This sequence's quantized tokens spread evenly over the S - 1 split
   // slots, in whole tiles (whole groups for KIVI, so that a Key group never
   // straddles two splits).
   constexpr int kUnit = KIVI ? G : kTile;
   const int per = (nq + wk.S - 2) / (wk.S - 1);
   const int len = (per + kUnit - 1) / kUnit * kUnit;
-  const int nsq = len > 0 ? (nq + len - 1) / len : 0;
-  const bool resid = KIVI && n > nq;
-  const int nact = nsq + (resid ? 1 : 0);
+  int nsq = len > 0 ? (nq + len - 1) / len : 0;
+  // FP8/INT8 fused step: split 0 also takes the new token (for an empty
+  // sequence, split 0 holds it alone)
+  const int t_new = (FUSED && !KIVI && app) ? n_cache : -1;
+  if (t_new >= 0 && nsq == 0) nsq = 1;
+  // slot S-1: the KIVI residual window
+  const bool extra = KIVI && n > nq;
+  const int nact = nsq + (extra ? 1 : 0);
+  // A fused step advances seq_lens[b] inside this launch, so every
+  // workgroup of the sequence (also one with no tokens) takes a ticket: the
+  // last merge of the sequence then knows that all of them have read it.
+  const bool every = FUSED && app;
   if (nact == 0) {
     if (s == 0)
       for (int e = tid; e < g * D; e += kThreads) out[(size_t(b) * cv.Hq + size_t(h) * g) * D + e] = 0.0f;
     return;
   }
   if (s == wk.S - 1) {
-    if constexpr (KIVI) {
-      if (!resid) return;
-      split_residual<D, BF16>(cv, b, h, s, nq, n, q, sm_log2, wk, *reinterpret_cast<SmemResid<D>*>(smem));
-    } else {
-      return;
+    if (!extra) {
+      if (!every) return;
+    } else if constexpr (KIVI) {
+      split_residual<D, BF16, BITS, G, FUSED>(cv, b, h, s, nq, n, q, sm_log2, wk,
+                                              *reinterpret_cast<SmemResidT<D, G, FUSED>*>(smem), ap, app);
     }
+  } else if (s >= nsq) {
+    if (!every) return;
   } else {
-    if (s >= nsq) return;
     const int t0 = s * len;
     const int t1 = min(t0 + len, nq);
-    split_quantized<FMT, BITS, D, G, BF16>(cv, b, h, s, t0, t1, q, sm_log2, wk,
-                                           *reinterpret_cast<SmemQuant<D>*>(smem));
+    split_quantized<FMT, BITS, D, G, BF16, FUSED>(cv, b, h, s, t0, t1, q, sm_log2, wk,
+                                                  *reinterpret_cast<SmemQuant<D>*>(smem), s == 0 ? t_new : -1, ap);
   }
 
   // ---- arrival: the last workgroup of this (sequence, kv head) merges ----
@@ -1223,7 +1401,7 @@ __global__ __launch_bounds__(kThreads, (min_wg_per_cu<FMT, BITS, D, G>())) void 
   __syncthreads();                 // ... for every thread, before the ticket is taken
   if (tid == 0) ticket = __hip_atomic_fetch_add(&wk.count[pair], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  if (ticket != uint32_t(nact - 1)) return;
+  if (ticket != uint32_t(every ? int(gridDim.x) - 1 : nact - 1)) return;
 
   // Merge by the log-sum-exp rule. Thread (j, c4) owns channels [4 c4,
   // 4 c4 + 4) of head j. For up to kMergeBatch pieces at a time it loads,
@@ -1278,7 +1456,18 @@ __global__ __launch_bounds__(kThreads, (min_wg_per_cu<FMT, BITS, D, G>())) void 
   if (j < g)
     *reinterpret_cast<f32x4*>(&out[(size_t(b) * cv.Hq + size_t(h) * g + j) * D + 4 * c4]) =
         acc * (L > 0.0f ? 1.0f / L : 0.0f);
-  if (tid == 0) __hip_atomic_store(&wk.count[pair], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) {
+    __hip_atomic_store(&wk.count[pair], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (every) {
+      // the last (sequence, kv head) merge of sequence b: every workgroup of
+      // the sequence has read seq_lens[b]
+      const uint32_t done = __hip_atomic_fetch_add(&wk.bcount[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (done == uint32_t(cv.Hkv - 1)) {
+        __hip_atomic_store(&wk.bcount[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ap.seq_lens[b] = n;
+      }
+    }
+  }
 }
 
 // One kernel instantiation per (format, bits, head_dim, group, input type).
@@ -1325,14 +1514,19 @@ void visit_variant(const CacheView& cv, F&& f) {
 }  // namespace
 
 hipError_t launch_decode(const CacheView& cv, const int32_t* seq_lens, const void* q, float sm_scale, float* out,
-                         const DecodeWork& work, hipStream_t stream) {
+                         const DecodeWork& work, const AppendIn* app, hipStream_t stream) {
   const float sm_log2 = sm_scale * kLog2e;
+  const AppendIn ap = app ? *app : AppendIn{nullptr, nullptr, nullptr};
   visit_variant(cv, [&](auto v) {
     using V = decltype(v);
-    // the residual slot S-1 exists only for KIVI
+    // slot S-1 (the KIVI residual window)
     const dim3 grid(V::FMT == KVQ_FMT_KIVI ? work.S : work.S - 1, cv.Hkv, cv.B);
-    decode_split<V::FMT, V::BITS, V::D, V::G, V::BF16><<<grid, kThreads, 0, stream>>>(cv, seq_lens, q, sm_log2, out,
-                                                                                       work);
+    if (app)
+      decode_split<V::FMT, V::BITS, V::D, V::G, V::BF16, true><<<grid, kThreads, 0, stream>>>(
+          cv, ap.seq_lens, q, sm_log2, out, work, ap);
+    else
+      decode_split<V::FMT, V::BITS, V::D, V::G, V::BF16, false><<<grid, kThreads, 0, stream>>>(
+          cv, seq_lens, q, sm_log2, out, work, ap);
   });
   return hipGetLastError();
 }
@@ -1351,8 +1545,8 @@ int decode_resident_workgroups(const CacheView& cv) {
   hipError_t e = hipSuccess;
   visit_variant(cv, [&](auto v) {
     using V = decltype(v);
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split<V::FMT, V::BITS, V::D, V::G, V::BF16>,
-                                                     kThreads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, decode_split<V::FMT, V::BITS, V::D, V::G, V::BF16, false>, kThreads, 0);
   });
   if (e != hipSuccess) return 0;
   return cus * per_cu;

@@ -39,6 +39,7 @@ constexpr int kMaxDecodeSplits = 128;
 
 struct DecodeWork {
   uint32_t* count;  // [B][Hkv] partials finished in this call (zero between calls)
+  uint32_t* bcount; // [B] (sequence, kv head) merges finished in a fused call (zero between calls)
   float* o;         // [B][Hq][S][D] unnormalized partial outputs
   float* m;         // [B][Hq][S] running maxima (log2 domain)
   float* l;         // [B][Hq][S] running sums
@@ -48,8 +49,20 @@ struct DecodeWork {
 hipError_t launch_append(const CacheView& cv, int32_t* seq_lens, const void* k_new,
                          const void* v_new, int T, const int32_t* append_lens, hipStream_t stream);
 
+// The one new token per sequence of a fused append + decode call: K and V
+// rows [B][Hkv][1][D] in the input dtype; seq_lens is advanced in place.
+struct AppendIn {
+  int32_t* seq_lens;
+  const void* k;
+  const void* v;
+};
+
+// Decode attention; with app != nullptr, the fused step that first appends
+// app's token to every sequence (as launch_append with T = 1 would) and then
+// attends over the grown cache, in one launch.
 hipError_t launch_decode(const CacheView& cv, const int32_t* seq_lens, const void* q,
-                         float sm_scale, float* out, const DecodeWork& work, hipStream_t stream);
+                         float sm_scale, float* out, const DecodeWork& work, const AppendIn* app,
+                         hipStream_t stream);
 
 // Decode workgroups the current device holds at once (compute units times
 // the kernel's occupancy per unit); 0 when it cannot be queried.

@@ -1,0 +1,231 @@
+// Append-time quantization steps shared by the append kernels and the fused
+// append + decode kernel, so that both store the same codes, scales and
+// zero-points bit for bit.
+//
+// Operations (cited by page title and section):
+//  - per-token FP8 E4M3 / INT8: "KV Cache Quantization" (infra.bea.ai) §4
+//    "FP8 KV Cache" (scale from the maximum absolute value, stored with the
+//    data); "KV Cache Quantization in Production LLM Serving" (llms.blog)
+//    "1. FP8 KV Cache" (OCP E4M3) and "2. INT8 and INT4 Uniform Group-Wise
+//    Quantization" ([-127, 127]); n4n.ai "Step 3: Implement quantization
+//    hooks" (x / scale, round half to even, clamp).
+//  - KIVI group flush: infra.bea.ai §3 (Key per channel over a group of
+//    tokens, Value per token over groups of channels, "Residual Cache for
+//    Streaming"); llms.blog "3. KIVI" (tokens leaving the residual window
+//    are quantized and packed).
+//
+// Arithmetic is fp32 with true IEEE division and round-half-even (rintf);
+// the formulas hold no product that could fuse into an add, and every
+// function also disables contraction, so the result does not depend on the
+// flags of the file that includes it.
+#pragma once
+
+#include "kvq_device.h"
+
+namespace kvq {
+
+constexpr int kQuantThreads = 256;  // workgroup size the group-flush steps assume
+
+// ---------------------------------------------------------------------------
+// Per-token FP8 E4M3 / INT8: one wave quantizes one token row, CPL = D / 64
+// channels per lane (channel lane * CPL + j in x[j]).
+// ---------------------------------------------------------------------------
+// Returns the lane's CPL code bytes (channel lane * CPL + j in byte j) and
+// sets *scale to the row's scale. Wave-collective.
+template <int FMT, int CPL>
+__device__ __forceinline__ uint32_t quantize_token_lane(const float (&x)[CPL], float* scale) {
+#pragma clang fp contract(off)
+  float a = 0.0f;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) a = fmaxf(a, fabsf(x[j]));
+  a = wave_max(a);
+  const float s = a / (FMT == KVQ_FMT_FP8_E4M3 ? 448.0f : 127.0f);
+  uint32_t codes = 0;
+  if constexpr (FMT == KVQ_FMT_INT8) {
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      float qv = 0.0f;
+      if (s > 0.0f) qv = fminf(fmaxf(rintf(x[j] / s), -127.0f), 127.0f);
+      codes |= (uint32_t(int32_t(qv)) & 0xffu) << (8 * j);
+    }
+  } else {
+    float y[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      if (s > 0.0f) y[j] = fminf(fmaxf(x[j] / s, -448.0f), 448.0f);
+    }
+    // OCP E4M3, round to nearest even; inputs are already within +-448.
+    codes = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false)) & (CPL == 2 ? 0xffffu : 0xffu);
+  }
+  *scale = s;
+  return codes;
+}
+
+// Stores one lane's code bytes and (lane 0) the scale of token t of pair
+// `pair`: Key rows token-major, Value codes in 8-token blocks with one
+// 8-byte word per (permuted) channel slot.
+template <int CPL>
+__device__ __forceinline__ void store_token_codes(const CacheView& cv, size_t pair, int t, bool value, int lane,
+                                                  uint32_t codes, float s) {
+  constexpr int D = CPL * kWave;
+  if (!value) {
+    uint8_t* dst = cv.k_codes + (pair * cv.cap + t) * D + lane * CPL;
+    if constexpr (CPL == 2) *reinterpret_cast<uint16_t*>(dst) = uint16_t(codes);
+    else *dst = uint8_t(codes);
+    if (lane == 0) cv.k_scale[pair * cv.cap + t] = s;
+  } else {
+    uint8_t* blk = cv.v_codes + (pair * (cv.cap / 8) + t / 8) * (size_t(D) * 8) + (t & 7);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) blk[size_t(value_slot<2>(lane * CPL + j)) * 8] = uint8_t(codes >> (8 * j));
+    if (lane == 0) cv.v_scale[pair * cv.cap + t] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// KIVI group flush, one workgroup of kQuantThreads threads per group. The G
+// tokens are staged in LDS as fp32; Key statistics run down each channel,
+// Value statistics along each token's channel groups.
+// ---------------------------------------------------------------------------
+template <int G, int D>
+struct FlushSmem {
+  float xs[G][D + 1];
+  float red_mn[kQuantThreads], red_mx[kQuantThreads];
+  float sk[D], zk[D];              // Key scale, zero-point per channel
+  float sv[G][D / G], zv[G][D / G];  // Value scale, zero-point per token and channel group
+};
+
+// Asymmetric code of one element: clamp(rint((x - mn) / s), 0, qmax), or 0
+// for a degenerate group (s == 0).
+__device__ __forceinline__ uint32_t asym_code(float x, float s, float mn, float qmax) {
+#pragma clang fp contract(off)
+  if (!(s > 0.0f)) return 0u;
+  const float qv = fminf(fmaxf(rintf((x - mn) / s), 0.0f), qmax);
+  return uint32_t(qv);
+}
+
+// Stages tokens [grp*G, grp*G + G) of one pair: a token below n (already in
+// the cache) comes from its residual ring slot, token t >= n from row t - n
+// of the pair's T new input rows. No barrier.
+template <bool BF16, int G, int D>
+__device__ __forceinline__ void flush_stage(FlushSmem<G, D>& f, const CacheView& cv, size_t pair, int grp, int n,
+                                            const void* in, int T, const uint8_t* ring) {
+  for (int e = threadIdx.x; e < G * D; e += kQuantThreads) {
+    const int i = e / D, c = e % D;
+    const int t = grp * G + i;
+    f.xs[i][c] = t < n ? load_elem<BF16>(ring, (pair * cv.C + (t % cv.C)) * D + c)
+                       : load_elem<BF16>(in, (pair * T + (t - n)) * D + c);
+  }
+}
+
+// Key half of a flush from the staged tile: per-channel scale and
+// zero-point (stored, and kept in f.sk / f.zk) and the packed codes.
+// Starts and ends with a barrier.
+template <int BITS, int G, int D>
+__device__ __forceinline__ void flush_key(FlushSmem<G, D>& f, const CacheView& cv, size_t pair, int grp) {
+#pragma clang fp contract(off)
+  constexpr float QMAX = float((1 << BITS) - 1);
+  constexpr int P = kQuantThreads / D;  // threads per channel
+  const int tid = threadIdx.x;
+  __syncthreads();
+  {
+    const int c = tid % D, part = tid / D;
+    float mn = INFINITY, mx = -INFINITY;
+    for (int i = part; i < G; i += P) {
+      const float x = f.xs[i][c];
+      mn = fminf(mn, x);
+      mx = fmaxf(mx, x);
+    }
+    f.red_mn[tid] = mn;
+    f.red_mx[tid] = mx;
+  }
+  __syncthreads();
+  if (tid < D) {
+    float mn = f.red_mn[tid], mx = f.red_mx[tid];
+#pragma unroll
+    for (int p = 1; p < P; ++p) {
+      mn = fminf(mn, f.red_mn[p * D + tid]);
+      mx = fmaxf(mx, f.red_mx[p * D + tid]);
+    }
+    const float s = (mx - mn) / QMAX + 0.0f;
+    const float z = mn + 0.0f;
+    f.sk[tid] = s;
+    f.zk[tid] = z;
+    const size_t si = (pair * (cv.cap / G) + grp) * D + tid;
+    cv.k_scale[si] = s;
+    cv.k_zero[si] = z;
+  }
+  __syncthreads();
+  {
+    constexpr int CW = 32 / BITS;  // channels per 32-bit word
+    constexpr int W = D / CW;      // words per token row
+    uint32_t* rows = reinterpret_cast<uint32_t*>(cv.k_codes + (pair * cv.cap + size_t(grp) * G) * (D * BITS / 8));
+    for (int w = tid; w < G * W; w += kQuantThreads) {
+      const int i = w / W, c0 = (w % W) * CW;
+      uint32_t word = 0;
+#pragma unroll
+      for (int j = 0; j < CW; ++j)
+        word |= asym_code(f.xs[i][c0 + j], f.sk[c0 + j], f.zk[c0 + j], QMAX) << (j * BITS);
+      rows[w] = word;
+    }
+  }
+  __syncthreads();
+}
+
+// Value half of a flush from the staged tile: per-token, per-channel-group
+// scale and zero-point (stored, and kept in f.sv / f.zv) and the codes in
+// blocks of TB tokens (8 for INT4, 16 for INT2), one 32-bit word per
+// permuted channel slot. Starts and ends with a barrier.
+template <int BITS, int G, int D>
+__device__ __forceinline__ void flush_value(FlushSmem<G, D>& f, const CacheView& cv, size_t pair, int grp) {
+#pragma clang fp contract(off)
+  constexpr float QMAX = float((1 << BITS) - 1);
+  constexpr int NVG = D / G;              // Value channel groups per token
+  constexpr int TP = kQuantThreads / D;   // threads per (token, channel group)
+  constexpr int CPT = G / TP;             // channels per thread in a Value group
+  static_assert(G * NVG == D, "value groups tile head_dim");
+  const int tid = threadIdx.x;
+  __syncthreads();
+  {
+    const int pr = tid / TP, part = tid % TP;
+    const int i = pr / NVG, j = pr % NVG;
+    float mn = INFINITY, mx = -INFINITY;
+    for (int k = 0; k < CPT; ++k) {
+      const float x = f.xs[i][j * G + part * CPT + k];
+      mn = fminf(mn, x);
+      mx = fmaxf(mx, x);
+    }
+#pragma unroll
+    for (int o = 1; o < TP; o <<= 1) {
+      mn = fminf(mn, __shfl_xor(mn, o, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+    }
+    if (part == 0) {
+      const float s = (mx - mn) / QMAX + 0.0f;
+      const float z = mn + 0.0f;
+      f.sv[i][j] = s;
+      f.zv[i][j] = z;
+      const size_t vi = (pair * cv.cap + size_t(grp) * G + i) * NVG + j;
+      cv.v_scale[vi] = s;
+      cv.v_zero[vi] = z;
+    }
+  }
+  __syncthreads();
+  {
+    constexpr int TB = BITS == 2 ? 16 : 8;
+    constexpr int NB = G / TB;
+    uint32_t* blocks = reinterpret_cast<uint32_t*>(cv.v_codes) + (pair * (cv.cap / TB) + size_t(grp) * NB) * D;
+    for (int w = tid; w < NB * D; w += kQuantThreads) {
+      const int blk = w / D, c = w % D, j = c / G;
+      uint32_t word = 0;
+#pragma unroll
+      for (int k = 0; k < TB; ++k) {
+        const int i = blk * TB + k;
+        word |= asym_code(f.xs[i][c], f.sv[i][j], f.zv[i][j], QMAX) << (k * BITS);
+      }
+      blocks[blk * D + value_slot<4>(c)] = word;
+    }
+  }
+  __syncthreads();
+}
+
+}  // namespace kvq

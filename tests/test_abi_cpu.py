@@ -27,7 +27,8 @@ def _declared_functions():
 def test_library_exports_every_declared_function():
     names = _declared_functions()
     assert set(names) >= {"kvq_get_layout", "kvq_quantize_append", "kvq_decode_attention",
-                          "kvq_decode_workspace_bytes", "kvq_status_string", "kvq_version"}
+                          "kvq_decode_workspace_bytes", "kvq_status_string", "kvq_version",
+                          "kvq_append_decode"}
     lib = ctypes.CDLL(kvq.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -149,15 +150,37 @@ def test_decode_argument_errors_need_no_gpu():
     assert L.kvq_decode_attention(ctypes.byref(bad), P, P, P, f, P, P, need, 0, None) == kvq.ERR_UNSUPPORTED
 
 
+def test_append_decode_argument_errors_need_no_gpu():
+    L = kvq.lib()
+    cfg = _cfg(WORKLOADS[1])
+    need = kvq.kvq_decode_workspace_bytes(cfg, 0)
+    P = FAKE
+    f = ctypes.c_float(0.125)
+    ok = (P, P, P, P, P, f, P, P, need, 0, None)
+
+    def call(*args):
+        return L.kvq_append_decode(ctypes.byref(cfg), *args)
+    assert call(None, *ok[1:]) == kvq.ERR_INVALID                      # cache
+    assert call(P, None, *ok[2:]) == kvq.ERR_INVALID                   # seq_lens
+    assert call(P, P, None, *ok[3:]) == kvq.ERR_INVALID                # k_new
+    assert call(P, P, P, None, *ok[4:]) == kvq.ERR_INVALID             # v_new
+    assert call(P, P, P + 8, *ok[3:]) == kvq.ERR_INVALID               # misaligned k_new
+    assert call(P, P, P, P, None, *ok[5:]) == kvq.ERR_INVALID          # q
+    assert call(*ok[:5], ctypes.c_float(float("inf")), *ok[6:]) == kvq.ERR_INVALID
+    assert call(*ok[:8], need - 1, 0, None) == kvq.ERR_WORKSPACE
+    assert call(*ok[:8], need, 96, None) == kvq.ERR_UNSUPPORTED        # split not a multiple of 64
+    assert L.kvq_append_decode(None, *ok) == kvq.ERR_INVALID
+
+
 def test_workspace_grows_with_split_count():
-    """Workspace = [B][Hkv] uint32 arrival counters, then partial (o, m, l)
+    """Workspace = [B][Hkv] + [B] uint32 arrival counters, then partial (o, m, l)
     rows for every split slot; at most 128 quantized splits per sequence."""
     cfg = _cfg(WORKLOADS[4])
     small = kvq.kvq_decode_workspace_bytes(cfg, 4096)
     big = kvq.kvq_decode_workspace_bytes(cfg, 512)
     assert big > small > 0
     rows = cfg.batch * cfg.n_q_heads * (-(-cfg.max_tokens // 512) + 1)
-    assert big >= cfg.batch * cfg.n_kv_heads * 4 + rows * (cfg.head_dim + 2) * 4
+    assert big >= cfg.batch * (cfg.n_kv_heads + 1) * 4 + rows * (cfg.head_dim + 2) * 4
     # 64-token splits of this cache would be > 128 splits
     with pytest.raises(kvq.KvqError) as e:
         kvq.kvq_decode_workspace_bytes(cfg, 64)
@@ -168,7 +191,7 @@ def test_workspace_grows_with_split_count():
         def a256(x):
             return -(-x // 256) * 256
         rows = c.batch * c.n_q_heads * (nsplit + 1)
-        return a256(c.batch * c.n_kv_heads * 4) + a256(rows * c.head_dim * 4) + 2 * a256(rows * 4)
+        return a256(c.batch * (c.n_kv_heads + 1) * 4) + a256(rows * c.head_dim * 4) + 2 * a256(rows * 4)
     for w in (WORKLOADS[1], WORKLOADS[2], WORKLOADS[4]):
         c = _cfg(w)
         assert kvq.kvq_decode_workspace_bytes(c, 0) == ws(c, min(128, max(1, c.max_tokens // 256)))
