@@ -131,8 +131,10 @@ def profiled_traffic(w):
     rec = None
     with open(path) as f:
         for line in f:
-            if line.startswith('{"kernel": "decode_split"'):
-                rec = json.loads(line)
+            if line.startswith('{"kernel": '):
+                r = json.loads(line)
+                if r["kernel"] == "decode_split":  # the plain decode call (not the fused step)
+                    rec = r
     if rec is None:
         return None, None
     h = hashlib.sha256()
