@@ -150,6 +150,29 @@ def quantize_fp8_per_token(x):
     return e4m3_encode(y), s.astype(F32)
 
 
+# ---------------------------------------------------------------------------
+# Unquantized 16-bit cache  [BEA §1 table: BF16 at 2 bytes per element, the
+# baseline the quantized formats are measured against; LLMS intro: the
+# 16-bit memory-per-token formula]
+# ---------------------------------------------------------------------------
+def round_bf16(x) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) of float32 values, rounded to nearest,
+    ties to even: bfloat16 keeps the upper 16 bits of the binary32 pattern,
+    so the lower 16 bits decide the rounding (below half: truncate, above:
+    round up, exactly half: round to the even upper part). Finite inputs."""
+    u = np.asarray(x, dtype=F32).view(np.uint32).astype(np.uint64)
+    upper, lower = u >> np.uint64(16), u & np.uint64(0xFFFF)
+    up = (lower > 0x8000) | ((lower == 0x8000) & ((upper & np.uint64(1)) == 1))
+    return (upper + up.astype(np.uint64)).astype(np.uint16)
+
+
+def bf16_value(bits) -> np.ndarray:
+    """Value (float64) of bfloat16 bit patterns: the pattern shifted into the
+    upper half of a binary32, widened exactly."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(F32).astype(F64)
+
+
 def dequantize_int8(codes, s):
     return np.asarray(codes, F64) * np.asarray(s, F64)[..., None]
 
@@ -256,14 +279,16 @@ def unpack_codes(packed, bits: int) -> np.ndarray:
 class SequenceCache:
     """State of one sequence's cache for one KV head.
 
-    fmt: "fp8", "int8" or "kivi". Inputs are float32 rows (bf16 inputs are
-    widened exactly by the caller). For KIVI, flushed groups are kept as
-    lists of arrays, the residual as float32 rows in arrival order.
+    fmt: "fp8", "int8", "kivi" or "bf16" (the unquantized 16-bit cache:
+    codes are the bfloat16 patterns of the inputs, no scales). Inputs are
+    float32 rows (bf16 inputs are widened exactly by the caller). For KIVI,
+    flushed groups are kept as lists of arrays, the residual as float32 rows
+    in arrival order.
     """
 
     def __init__(self, fmt: str, head_dim: int, bits: int = 8, group: int = 0,
                  residual: int = 0):
-        if fmt not in ("fp8", "int8", "kivi"):
+        if fmt not in ("fp8", "int8", "kivi", "bf16"):
             raise ValueError(fmt)
         self.fmt, self.d, self.bits, self.group, self.residual = fmt, head_dim, bits, group, residual
         self.n = 0
@@ -286,6 +311,9 @@ class SequenceCache:
                 q, s = quantize_int8_per_token(x)
                 codes.append(q)
                 scales.append(s)
+        elif self.fmt == "bf16":
+            self.k_codes.append(round_bf16(k))
+            self.v_codes.append(round_bf16(v))
         elif self.fmt == "fp8":
             for x, codes, scales in ((k, self.k_codes, self.k_scale), (v, self.v_codes, self.v_scale)):
                 q, s = quantize_fp8_per_token(x)
@@ -319,10 +347,12 @@ class SequenceCache:
         return self.n
 
     def key_codes(self):
-        return np.concatenate(self.k_codes) if self.k_codes else np.zeros((0, self.d), np.uint8)
+        dt = np.uint16 if self.fmt == "bf16" else np.uint8
+        return np.concatenate(self.k_codes) if self.k_codes else np.zeros((0, self.d), dt)
 
     def value_codes(self):
-        return np.concatenate(self.v_codes) if self.v_codes else np.zeros((0, self.d), np.uint8)
+        dt = np.uint16 if self.fmt == "bf16" else np.uint8
+        return np.concatenate(self.v_codes) if self.v_codes else np.zeros((0, self.d), dt)
 
     def dequantized(self):
         """(K, V) as float64 [n, d]: quantized tokens first, then the residual
@@ -334,6 +364,9 @@ class SequenceCache:
                   for c, s, z in zip(self.v_codes, self.v_scale, self.v_zero)]
             ks.append(self.resid_k.astype(F64))
             vs.append(self.resid_v.astype(F64))
+        elif self.fmt == "bf16":
+            ks = [bf16_value(c) for c in self.k_codes]
+            vs = [bf16_value(c) for c in self.v_codes]
         else:
             deq = dequantize_int8 if self.fmt == "int8" else dequantize_fp8
             ks = [deq(c, s) for c, s in zip(self.k_codes, self.k_scale)]

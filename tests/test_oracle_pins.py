@@ -408,3 +408,57 @@ def test_kivi_dequantized_cache_orders_quantized_then_residual():
     assert s.n_quantized == 64
     np.testing.assert_array_equal(K[64:], k[64:].astype(np.float64))   # residual untouched
     assert np.max(np.abs(K[:64] - k[:64])) < 0.5
+
+
+# --- the unquantized 16-bit cache (the baseline the quantized formats save bytes against) ---
+def test_round_bf16_matches_torch_cast_on_every_tie_and_neighbour():
+    """round_bf16 against torch's CPU float32 -> bfloat16 cast (a library
+    routine): every pattern whose low 16 bits are a tie (0x8000) or one ulp
+    either side of it, over a spread of upper halves of both parities, plus
+    random finite values."""
+    rng = np.random.default_rng(7)
+    upper = np.concatenate([np.arange(0x0000, 0x0100), np.arange(0x3F00, 0x4100),
+                            rng.integers(0, 0x7F7F, 4000)]).astype(np.uint32)
+    upper = np.concatenate([upper, upper | 0x8000])          # both signs
+    lows = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], dtype=np.uint32)
+    pats = (upper[:, None] << 16 | lows[None, :]).reshape(-1)
+    pats = pats[(pats & 0x7F800000) != 0x7F800000]            # finite only
+    x = pats.view(np.float32)
+    x = np.concatenate([x, rng.standard_normal(20000).astype(np.float32) * 100])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(O.round_bf16(x), ref)
+
+
+def test_round_bf16_ties_go_to_even():
+    # 1 + 2^-8 lies halfway between bf16 neighbours 1 and 1 + 2^-7: even is 1.0
+    assert O.round_bf16(np.float32(1.0 + 2.0 ** -8)) == 0x3F80
+    # 1 + 3 * 2^-8 lies halfway between 1 + 2^-7 (odd) and 1 + 2^-6: up
+    assert O.round_bf16(np.float32(1.0 + 3 * 2.0 ** -8)) == 0x3F82
+    assert O.round_bf16(np.float32(-0.0)) == 0x8000
+
+
+def test_bf16_value_is_exact_and_bf16_cache_round_trips():
+    """bf16 inputs are stored bit-unchanged and read back exactly; the 16-bit
+    cache's decode attention equals attention over the bf16 values."""
+    rng = np.random.default_rng(3)
+    bits = rng.integers(0, 0x7F00, (40, 64)).astype(np.uint16)
+    bits |= (rng.integers(0, 2, bits.shape) << 15).astype(np.uint16)
+    x = O.bf16_value(bits).astype(np.float32)
+    np.testing.assert_array_equal(O.round_bf16(x), bits)
+    s = O.SequenceCache("bf16", 64)
+    s.append(x[:20], -x[:20])
+    s.append(x[20:], -x[20:])
+    K, V = s.dequantized()
+    np.testing.assert_array_equal(K, x.astype(np.float64))
+    np.testing.assert_array_equal(V, -x.astype(np.float64))
+    assert s.n == 40 and s.key_codes().dtype == np.uint16
+    q = rng.standard_normal(64)
+    ref = O.attention_one_head(q, x.astype(np.float64), -x.astype(np.float64), np.float32(0.125))
+    got = O.decode_attention([s], q[None, :], np.float32(0.125))[0]
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_bf16_cache_halves_nothing_the_memory_table_says_2_bytes():
+    # [BEA] §1: BF16 is the 2-byte row of the table (320 KB per token for the
+    # 80-layer, 8-KV-head, d = 128 model); the bf16 cache stores exactly that
+    assert O.kv_bytes_per_token(80, 8, 128, 2) == 327680
