@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--decode-rounds", type=int, default=20, help="passes over all copies in the decode-only timing")
+    p.add_argument("--cache-format", choices=("native", "bf16"), default="native",
+                   help="bf16: the same workload shapes and inputs with the unquantized 16-bit cache "
+                        "(the baseline the quantized formats save bytes against)")
     p.add_argument("--unfused", action="store_true",
                    help="time the step as kvq_quantize_append + kvq_decode_attention (two calls per layer)")
     p.add_argument("--stream-ref", type=float, default=0.0,
@@ -56,6 +59,8 @@ def parse():
 def bytes_per_token_head(w):
     """Algorithmic bytes of one quantized token for one KV head (K + V)."""
     d = w.head_dim
+    if w.fmt == "bf16":
+        return 2 * d * 2
     if w.fmt in ("fp8", "int8"):
         return 2 * d + 2 * 4
     codes = 2 * d * w.bits // 8
@@ -94,7 +99,7 @@ def append_bytes(w, lens_before, t):
     for n in lens_before:
         n = int(n)
         per_head = 2 * t * d * elem                       # read new K and V
-        if w.fmt in ("fp8", "int8"):
+        if w.fmt != "kivi":
             per_head += t * bytes_per_token_head(w)       # codes + scales written
         else:
             q0, q1 = nq_of(w, n), nq_of(w, n + t)
@@ -220,11 +225,13 @@ def main():
         return
 
     w = WORKLOADS[args.config]
+    if args.cache_format == "bf16":
+        w = w.scaled(fmt="bf16", bits=16, group=0, residual=0)
     dev = torch.device("cuda:0")
     lens0 = context_lengths(w)
     n_max = int(lens0.max())
-    grow = args.warmup + args.steps + 1
-    fmt = {"fp8": kvq.FMT_FP8_E4M3, "int8": kvq.FMT_INT8, "kivi": kvq.FMT_KIVI}[w.fmt]
+    grow = args.warmup + 2 * args.steps + 1  # warm-up steps, an untimed and a timed replay of the steps
+    fmt = {"fp8": kvq.FMT_FP8_E4M3, "int8": kvq.FMT_INT8, "kivi": kvq.FMT_KIVI, "bf16": kvq.FMT_BF16}[w.fmt]
     cfg = kvq.make_config(fmt, w.bits, w.group, w.residual, w.batch, w.n_kv_heads, w.n_q_heads, w.head_dim,
                           n_max + grow, kvq.DT_BF16 if w.dtype == "bf16" else kvq.DT_F32)
     lay = kvq.kvq_get_layout(cfg)
@@ -233,7 +240,18 @@ def main():
     elif w.layers > 1:
         copies = w.layers
     else:
-        copies = max(1, math.ceil(args.min_bytes / lay.total_bytes))
+        # enough copies to span min_bytes, at most 64 (the tiny workload's
+        # 0.1 MB cache would otherwise need ~20000 copies and graphs of
+        # hundreds of thousands of launches)
+        copies = min(64, max(1, math.ceil(args.min_bytes / lay.total_bytes)))
+    # the bf16 cache of the long-context workload is 8.6 GB per layer at
+    # capacity: keep the copies within 250 GB of the 288 GB of HBM (the 80
+    # layers of every quantized workload fit)
+    fit = max(2, int(250e9 // lay.total_bytes))
+    if copies > fit:
+        print(f"bench: {copies} cache copies of {lay.total_bytes / 1e9:.1f} GB do not fit; using {fit}",
+              file=sys.stderr)
+        copies = fit
     ws_bytes = kvq.kvq_decode_workspace_bytes(cfg, args.split)
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)  # arrival counters start at zero
     stream = torch.cuda.current_stream()
@@ -302,6 +320,11 @@ def main():
         for s in range(args.warmup, steps_total):
             step(s)
     torch.cuda.synchronize()
+    # an untimed replay first (the first launch of a graph also uploads it);
+    # it appends the same new tokens once more, which the capacity allows
+    steps_graph.replay()
+    torch.cuda.synchronize()
+    lens_start += args.steps
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t_start.record()
@@ -352,12 +375,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"fp8": "e4m3", "int8": "i8"}.get(w.fmt, f"u{w.bits}") + " codes, bf16 MFMA (hi+lo), f32 accumulate",
+        "dtype": {"fp8": "e4m3", "int8": "i8", "bf16": "bf16"}.get(w.fmt, f"u{w.bits}") +
+                 " codes, bf16 MFMA (hi+lo), f32 accumulate",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "n_kv_heads": w.n_kv_heads, "n_q_heads": w.n_q_heads,
                    "head_dim": w.head_dim, "context": w.context if not w.ragged else
                    f"ragged {w.context_min}..{w.context}", "group": w.group, "residual": w.residual,
-                   "input_dtype": w.dtype, "cache_copies": copies, "split_tokens": args.split,
+                   "input_dtype": w.dtype, "cache_format": w.fmt, "cache_copies": copies,
+                   "split_tokens": args.split,
                    "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "decode_gbps": round(achieved, 2),

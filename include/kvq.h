@@ -80,7 +80,8 @@ typedef enum kvq_status {
 typedef enum kvq_format {
   KVQ_FMT_FP8_E4M3 = 1,    /* per-token OCP FP8 E4M3, fp32 scale per token   */
   KVQ_FMT_INT8 = 2,        /* per-token symmetric INT8, fp32 scale per token */
-  KVQ_FMT_KIVI = 3         /* KIVI asymmetric INT4/INT2 + residual window    */
+  KVQ_FMT_KIVI = 3,        /* KIVI asymmetric INT4/INT2 + residual window    */
+  KVQ_FMT_BF16 = 4         /* unquantized bfloat16 cache (the 16-bit baseline) */
 } kvq_format;
 
 typedef enum kvq_dtype {
@@ -89,12 +90,17 @@ typedef enum kvq_dtype {
 } kvq_dtype;
 
 /* Shape and format of one layer's cache. Supported: head_dim 64 or 128;
- * n_q_heads = g * n_kv_heads with g in 1..8; bits 8 for FP8/INT8 (group and
- * residual must be 0), bits 4 or 2 for KIVI with group 32 or 64 dividing
- * head_dim and 0 <= residual <= 4096; 1 <= max_tokens <= 2^24. */
+ * n_q_heads = g * n_kv_heads with g in 1..8; bits 8 for FP8/INT8 and 16 for
+ * BF16 (group and residual must be 0), bits 4 or 2 for KIVI with group 32
+ * or 64 dividing head_dim and 0 <= residual <= 4096; 1 <= max_tokens <= 2^24.
+ * KVQ_FMT_BF16 is the unquantized 16-bit cache of [BEA] §1's table (2 bytes
+ * per element): it stores each input rounded to bfloat16 (to nearest, ties
+ * to even; bf16 inputs bit-unchanged) with no scales, and decodes through
+ * the same attention kernel, as the point of comparison for the formats
+ * that store fewer bytes. */
 typedef struct kvq_config {
   int32_t format;      /* kvq_format                                         */
-  int32_t bits;        /* code width: 8 (FP8, INT8), 4 or 2 (KIVI)           */
+  int32_t bits;        /* code width: 8 (FP8, INT8), 4 or 2 (KIVI), 16 (BF16) */
   int32_t group;       /* KIVI G: tokens per Key group = channels per Value group */
   int32_t residual;    /* KIVI R: most recent tokens always kept unquantized */
   int32_t batch;       /* B sequences                                        */
@@ -111,16 +117,20 @@ typedef struct kvq_config {
  *
  *  k_codes  [B][Hkv][cap][row_bytes]       token-major; within a row, code of
  *           channel c sits in byte c*bits/8 at bit (c % (8/bits))*bits
- *           (low bits first; one byte per channel for FP8/INT8).
- *  v_codes  [B][Hkv][cap/TB][d][TB*bits/8] tokens in blocks of TB = 8 (8-bit
- *           codes, INT4) or TB = 16 (INT2); for each block, d little-endian
- *           words of TB*bits bits (8 bytes for 8-bit codes, else 4) whose bits
- *           [i*bits, (i+1)*bits) hold token TB*blk+i of one channel (8-bit:
- *           byte i). Word slots are permuted within chunks of 16*W channels,
- *           W = 16 / word bytes (2 or 4): slot W*m + x of a chunk holds the
- *           word of channel 16*x + m of that chunk, so a 16-byte load at slot
- *           W*m returns channel m of W consecutive 16-channel tiles.
+ *           (low bits first; one byte per channel for FP8/INT8; BF16: the
+ *           bfloat16 of channel c in bytes 2c, 2c+1).
+ *  v_codes  [B][Hkv][cap/TB][d][TB*bits/8] tokens in blocks of TB = 8 (BF16,
+ *           8-bit codes, INT4) or TB = 16 (INT2); for each block, d
+ *           little-endian words of TB*bits bits (16 bytes for BF16, 8 for
+ *           8-bit codes, else 4) whose bits [i*bits, (i+1)*bits) hold token
+ *           TB*blk+i of one channel (8-bit: byte i; BF16: bytes 2i, 2i+1).
+ *           Word slots are permuted within chunks of 16*W channels, W = 16 /
+ *           word bytes (1, 2 or 4): slot W*m + x of a chunk holds the word of
+ *           channel 16*x + m of that chunk, so a 16-byte load at slot W*m
+ *           returns channel m of W consecutive 16-channel tiles (W = 1, BF16:
+ *           no permutation).
  *  FP8/INT8: k_scale, v_scale [B][Hkv][cap] fp32; k_zero, v_zero unused (0).
+ *  BF16:    no scale or zero-point arrays (offsets 0).
  *  KIVI:    k_scale, k_zero [B][Hkv][cap/G][d] fp32 (per group, per channel);
  *           v_scale, v_zero [B][Hkv][cap][d/G] fp32 (per token, per channel
  *           group); k_resid, v_resid [B][Hkv][resid_slots][d] in in_dtype,
@@ -132,7 +142,7 @@ typedef struct kvq_layout {
   uint64_t k_scale_off, v_scale_off;
   uint64_t k_zero_off, v_zero_off;
   uint64_t k_resid_off, v_resid_off;
-  int32_t token_capacity;  /* cap: max_tokens rounded up to 32 (FP8/INT8) or to G (KIVI) */
+  int32_t token_capacity;  /* cap: max_tokens rounded up to 32 (FP8/INT8/BF16) or to G (KIVI) */
   int32_t resid_slots;     /* KIVI ring slots = residual + group; 0 otherwise */
   int32_t row_bytes;       /* head_dim * bits / 8                             */
   int32_t elem_bytes;      /* bytes of one in_dtype element (4 or 2)          */

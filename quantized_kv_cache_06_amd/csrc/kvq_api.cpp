@@ -32,6 +32,9 @@ int32_t validate(const kvq_config* c) {
     case KVQ_FMT_INT8:
       if (c->bits != 8 || c->group != 0 || c->residual != 0) return KVQ_ERR_INVALID;
       break;
+    case KVQ_FMT_BF16:
+      if (c->bits != 16 || c->group != 0 || c->residual != 0) return KVQ_ERR_INVALID;
+      break;
     case KVQ_FMT_KIVI:
       if (c->bits != 4 && c->bits != 2) return KVQ_ERR_INVALID;
       if (c->group <= 0 || c->residual < 0) return KVQ_ERR_INVALID;
@@ -63,7 +66,9 @@ void make_layout(const kvq_config* c, kvq_layout* L) {
   };
   L->k_codes_off = region(pairs * cap * L->row_bytes);
   L->v_codes_off = region(pairs * cap * L->row_bytes);
-  if (!kivi) {
+  if (c->format == KVQ_FMT_BF16) {
+    // no scales: the codes are the values
+  } else if (!kivi) {
     L->k_scale_off = region(pairs * cap * 4);
     L->v_scale_off = region(pairs * cap * 4);
   } else {
@@ -100,8 +105,9 @@ kvq::CacheView make_view(const kvq_config* c, const kvq_layout& L, const void* c
   v.row_bytes = L.row_bytes;
   v.k_codes = base + L.k_codes_off;
   v.v_codes = base + L.v_codes_off;
-  v.k_scale = reinterpret_cast<float*>(base + L.k_scale_off);
-  v.v_scale = reinterpret_cast<float*>(base + L.v_scale_off);
+  const bool scaled = c->format != KVQ_FMT_BF16;
+  v.k_scale = scaled ? reinterpret_cast<float*>(base + L.k_scale_off) : nullptr;
+  v.v_scale = scaled ? reinterpret_cast<float*>(base + L.v_scale_off) : nullptr;
   v.k_zero = kivi ? reinterpret_cast<float*>(base + L.k_zero_off) : nullptr;
   v.v_zero = kivi ? reinterpret_cast<float*>(base + L.v_zero_off) : nullptr;
   v.k_resid = kivi ? base + L.k_resid_off : nullptr;

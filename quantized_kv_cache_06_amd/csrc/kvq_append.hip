@@ -40,7 +40,8 @@ __device__ __forceinline__ bool append_range(const CacheView& cv, const int32_t*
 }
 
 // ---------------------------------------------------------------------------
-// Per-token FP8 E4M3 / INT8: one wave per token row, D/64 channels per lane.
+// Per-token FP8 E4M3 / INT8 (and the unquantized BF16 cache): one wave per
+// token row, D/64 channels per lane.
 // ---------------------------------------------------------------------------
 template <int FMT, int D, bool BF16>
 __global__ __launch_bounds__(kThreads) void append_per_token(CacheView cv, const int32_t* __restrict__ seq_lens,
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void append_per_token(CacheView cv, const
       for (int j = 0; j < CPL; ++j) x[j] = load_elem<BF16>(src, in_base + j);
       float s;
       const uint32_t codes = quantize_token_lane<FMT, CPL>(x, &s);
-      store_token_codes<CPL>(cv, pair, t, which != 0, lane, codes, s);
+      store_token_codes<FMT, CPL>(cv, pair, t, which != 0, lane, codes, s);
     }
   }
 }
@@ -183,6 +184,9 @@ hipError_t launch_append(const CacheView& cv, int32_t* seq_lens, const void* k_n
     if (cv.fmt == KVQ_FMT_FP8_E4M3) {
       if (cv.bf16) per_token_d<KVQ_FMT_FP8_E4M3, true>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
       else per_token_d<KVQ_FMT_FP8_E4M3, false>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
+    } else if (cv.fmt == KVQ_FMT_BF16) {
+      if (cv.bf16) per_token_d<KVQ_FMT_BF16, true>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
+      else per_token_d<KVQ_FMT_BF16, false>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
     } else {
       if (cv.bf16) per_token_d<KVQ_FMT_INT8, true>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
       else per_token_d<KVQ_FMT_INT8, false>(cv, seq_lens, k_new, v_new, T, append_lens, stream);

@@ -238,7 +238,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 // D/4, and element i of k-step kk is the following one of them.
 template <int BITS>
 __device__ __forceinline__ constexpr int cperm(int kk, int i) {
-  if constexpr (BITS == 8) return 8 * kk + i;
+  if constexpr (BITS >= 8) return 8 * kk + i;
   else if constexpr (BITS == 4) return 8 * kk + (i >> 1) + 4 * (i & 1);
   else return 16 * (kk >> 1) + 4 * (kk & 1) + (i >> 1) + 8 * (i & 1);
 }
@@ -348,7 +348,13 @@ __device__ __forceinline__ constexpr int kfactor_log2(int kk, int i) {
 template <int FMT, int BITS>
 __device__ __forceinline__ u32x4 key_operand(const uint32_t* kw, int kk) {
   u32x4 a;
-  if constexpr (BITS == 8) {
+  if constexpr (BITS == 16) {
+    // bf16 rows: 16-byte piece kk holds the k-step's 8 channels as they are
+    a[0] = kw[4 * kk];
+    a[1] = kw[4 * kk + 1];
+    a[2] = kw[4 * kk + 2];
+    a[3] = kw[4 * kk + 3];
+  } else if constexpr (BITS == 8) {
     a[0] = byte_pair_bf16<FMT, 0>(kw[2 * kk]);
     a[1] = byte_pair_bf16<FMT, 1>(kw[2 * kk]);
     a[2] = byte_pair_bf16<FMT, 0>(kw[2 * kk + 1]);
@@ -380,7 +386,13 @@ __device__ __forceinline__ u32x4 key_operand(const uint32_t* kw, int kk) {
 template <int FMT, int BITS>
 __device__ __forceinline__ u32x4 value_operand(const uint32_t* vw, int mt, int r) {
   u32x4 a;
-  if constexpr (BITS == 8) {
+  if constexpr (BITS == 16) {
+    // bf16: 16-byte load mt holds channel tile mt's 8 tokens as they are
+    a[0] = vw[4 * mt];
+    a[1] = vw[4 * mt + 1];
+    a[2] = vw[4 * mt + 2];
+    a[3] = vw[4 * mt + 3];
+  } else if constexpr (BITS == 8) {
     // 16-byte load p holds the 8-byte words of channel tiles 2p, 2p+1
     const uint32_t* w = vw + 4 * (mt >> 1) + 2 * (mt & 1);
     a[0] = byte_pair_bf16<FMT, 0>(w[0]);
@@ -409,7 +421,7 @@ __device__ __forceinline__ u32x4 prob_operand(const float (&p)[2][4], bool lo) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     float x0, x1;
-    if constexpr (BITS == 8) {
+    if constexpr (BITS >= 8) {
       x0 = p[k >> 1][2 * (k & 1)];
       x1 = p[k >> 1][2 * (k & 1) + 1];
     } else {
@@ -561,9 +573,12 @@ __device__ __forceinline__ void new_token_piece(const CacheView& cv, int b, int 
     for (int e = 0; e < CPL; ++e) x[e] = load_elem<BF16>(wave ? ap.v : ap.k, pair * D + lane * CPL + e);
     float sc;
     const uint32_t codes = quantize_token_lane<FMT, CPL>(x, &sc);
-    store_token_codes<CPL>(cv, pair, t, wave == 1, lane, codes, sc);
+    store_token_codes<FMT, CPL>(cv, pair, t, wave == 1, lane, codes, sc);
     float c[2];  // the codes as values, exactly
-    if constexpr (FMT == KVQ_FMT_FP8_E4M3) {
+    if constexpr (FMT == KVQ_FMT_BF16) {
+      c[0] = bf_lo(codes);
+      c[1] = bf_hi(codes);
+    } else if constexpr (FMT == KVQ_FMT_FP8_E4M3) {
       const uint32_t w = fp8x2_bf16<0>(codes);
       c[0] = bf_lo(w);
       c[1] = bf_hi(w);
@@ -613,7 +628,8 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   constexpr int NMT = D / 16;                 // channel tiles of the value MFMA
   constexpr int KB = D * BITS / 8;            // bytes per Key row
   constexpr int LKB = CPL * BITS / 8;         // Key bytes per lane per token
-  constexpr int VWB = BITS == 8 ? 8 : 4;      // bytes per Value word (one channel, one block)
+  constexpr int VWB = BITS == 16 ? 16 : BITS == 8 ? 8 : 4;  // bytes per Value word (one channel, one block)
+  constexpr bool SCALED = FMT != KVQ_FMT_BF16;  // per-token scales (FP8/INT8) or KIVI metadata
   constexpr int TB = BITS == 2 ? 16 : 8;      // tokens per Value block
   constexpr int VW = 16 / VWB;                // Value words per 16-byte load
   constexpr int NVL = D / (16 * VW);          // 16-byte Value loads per lane per tile
@@ -676,8 +692,11 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   const uint8_t* kpair = cv.k_codes + pair * size_t(cv.cap) * KB;
   const uint8_t* vpair = cv.v_codes + pair * size_t(cv.cap / TB) * D * VWB;
   uint32_t koff[2];
+  // bf16 rows: the lane's k-step kk is the 16-byte piece at 64 kk + 16 r, so
+  // each load instruction covers 64 contiguous bytes of every row it touches
 #pragma unroll
-  for (int t = 0; t < 2; ++t) koff[t] = uint32_t(tok<BITS>(t, m >> 2, m & 3) * KB + (KSPLIT ? 16 * r : LKB * r));
+  for (int t = 0; t < 2; ++t)
+    koff[t] = uint32_t(tok<BITS>(t, m >> 2, m & 3) * KB + (KSPLIT || BITS == 16 ? 16 * r : LKB * r));
   const uint32_t voff = uint32_t((size_t(BITS == 2 ? (r >> 1) : r) * D + VW * m) * VWB);
   // the pair's code regions as buffers; a tile past the wave's run loads
   // through an empty buffer (reads 0, fetches nothing), so the loads in
@@ -715,7 +734,10 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
     const uint32_t ks = uint32_t(T0) * KB;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      if constexpr (KSPLIT) {
+      if constexpr (BITS == 16) {
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) buffer_bytes<16, kCodeAux>(kr, koff[t] + 64 * kk, ks, sl.kw[t] + 4 * kk);
+      } else if constexpr (KSPLIT) {
         buffer_bytes<16, kCodeAux>(kr, koff[t], ks, sl.kw[t]);
         buffer_bytes<16, kCodeAux>(kr, koff[t] + 64, ks, sl.kw[t] + 4);
       } else {
@@ -728,7 +750,10 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
     // metadata: lanes 0-31 the Key (or Value scale) half, lanes 32-63 the
     // Value (or Value zero) half, NVG floats per lane
     const int part = lane >> 5, qi = lane & 31;
-    if constexpr (!KIVI) {
+    if constexpr (!SCALED) {
+      (void)part;
+      (void)qi;
+    } else if constexpr (!KIVI) {
       sl.mw[0] = load_vec<float, kMetaNT>(
           reinterpret_cast<const uint8_t*>((part ? cv.v_scale : cv.k_scale) + (pair * cv.cap + T0 + qi)));
     } else {
@@ -769,7 +794,10 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
     load_elems<BF16, EPT>(q, (size_t(b) * cv.Hq + size_t(h) * g + min(j, g - 1)) * D + c, qx);
   } else {
     const size_t qrow = (size_t(b) * cv.Hq + size_t(h) * g + min(hh, g - 1)) * D;
-    if constexpr (KSPLIT) {
+    if constexpr (BITS == 16) {
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) load_elems<BF16, 8>(q, qrow + 32 * kk + 8 * r, qx + 8 * kk);
+    } else if constexpr (KSPLIT) {
       load_elems<BF16, CPL / 2>(q, qrow + 16 * r, qx);
       load_elems<BF16, CPL / 2>(q, qrow + 64 + 16 * r, qx + CPL / 2);
     } else {
@@ -838,8 +866,10 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
     {
       const int part = lane >> 5, qi = lane & 31;
       float* mdst = (part ? meta1 : meta0) + qi * NVG;
+      if constexpr (SCALED) {
 #pragma unroll
-      for (int j = 0; j < NVG; ++j) mdst[j] = sl.mw[j];
+        for (int j = 0; j < NVG; ++j) mdst[j] = sl.mw[j];
+      }
       if constexpr (KIVI) {
         if (grp_open) {
           // Key scales (lanes 0-31; >= 0) scaled by 2^kes so that the
@@ -911,7 +941,7 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
     const int valid = KIVI ? kTile : min(kTile, t1 - T0);
     // this lane's tokens: tok(t, r, j) = base_t + j, 4 consecutive per t
     f32x4 ks[2], vs[2];
-    if constexpr (!KIVI) {
+    if constexpr (!KIVI && SCALED) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         ks[t] = *reinterpret_cast<const f32x4*>(meta0 + tok<BITS>(t, r, 0));
@@ -926,7 +956,8 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
       for (int j = 0; j < 4; ++j) {
         float x = add_ror8(acc[t][j]);
         if constexpr (KIVI) x = fmaf(x, kscale, kbias);
-        else x = x * ks[t][j] * sm_log2;
+        else if constexpr (SCALED) x = x * ks[t][j] * sm_log2;
+        else x = x * sm_log2;
         if (tok<BITS>(t, r, j) >= valid) x = -INFINITY;
         sc[t][j] = x;
         tmax = fmaxf(tmax, x);
@@ -963,7 +994,8 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pv[t][j] = tok<BITS>(t, r, j) < valid ? sc[t][j] * vs[t][j] : 0.0f;
+        for (int j = 0; j < 4; ++j)
+          pv[t][j] = tok<BITS>(t, r, j) < valid ? (SCALED ? sc[t][j] * vs[t][j] : sc[t][j]) : 0.0f;
       const u32x4 bp = prob_operand<BITS>(pv, lo_col);
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
@@ -1332,7 +1364,8 @@ __device__ __forceinline__ void split_residual(const CacheView& cv, int b, int h
 template <int FMT, int BITS, int D, int G>
 constexpr int min_wg_per_cu() {
   if constexpr (KVQ_DECODE_MIN_WG_PER_CU > 0) return KVQ_DECODE_MIN_WG_PER_CU;
-  return (FMT == KVQ_FMT_KIVI && BITS == 4 && D == 128 && G == 32) ? 2 : 3;
+  // bf16 rows hold twice the 8-bit codes' registers in the prefetch ring
+  return (FMT == KVQ_FMT_KIVI && BITS == 4 && D == 128 && G == 32) || BITS == 16 ? 2 : 3;
 }
 
 template <int FMT, int BITS, int D, int G, bool BF16, bool FUSED>
@@ -1342,6 +1375,16 @@ __global__ __launch_bounds__(kThreads, (min_wg_per_cu<FMT, BITS, D, G>())) void 
   constexpr bool KIVI = FMT == KVQ_FMT_KIVI;
   __shared__ float smem[smem_floats<D, G, FUSED>()];
   __shared__ uint32_t ticket;
+  // What a fused call needs after the token loop is parked in LDS, so that
+  // it does not hold scalar registers through the loop.
+  struct FusedTail {
+    int32_t* seq_lens;
+    uint32_t* bcount;
+    int n, hkv;
+    uint32_t last;  // ticket of the workgroup that merges
+    int every;
+  };
+  __shared__ FusedTail tail;
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int g = cv.g;
@@ -1374,6 +1417,9 @@ __global__ __launch_bounds__(kThreads, (min_wg_per_cu<FMT, BITS, D, G>())) void 
   // workgroup of the sequence (also one with no tokens) takes a ticket: the
   // last merge of the sequence then knows that all of them have read it.
   const bool every = FUSED && app;
+  if constexpr (FUSED) {
+    if (tid == 0) tail = {ap.seq_lens, wk.bcount, n, cv.Hkv, uint32_t(every ? int(gridDim.x) - 1 : nact - 1), every};
+  }
   if (nact == 0) {
     if (s == 0)
       for (int e = tid; e < g * D; e += kThreads) out[(size_t(b) * cv.Hq + size_t(h) * g) * D + e] = 0.0f;
@@ -1401,7 +1447,10 @@ __global__ __launch_bounds__(kThreads, (min_wg_per_cu<FMT, BITS, D, G>())) void 
   __syncthreads();                 // ... for every thread, before the ticket is taken
   if (tid == 0) ticket = __hip_atomic_fetch_add(&wk.count[pair], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  if (ticket != uint32_t(every ? int(gridDim.x) - 1 : nact - 1)) return;
+  uint32_t last;
+  if constexpr (FUSED) last = tail.last;
+  else last = uint32_t(nact - 1);
+  if (ticket != last) return;
 
   // Merge by the log-sum-exp rule. Thread (j, c4) owns channels [4 c4,
   // 4 c4 + 4) of head j. For up to kMergeBatch pieces at a time it loads,
@@ -1458,13 +1507,16 @@ __global__ __launch_bounds__(kThreads, (min_wg_per_cu<FMT, BITS, D, G>())) void 
         acc * (L > 0.0f ? 1.0f / L : 0.0f);
   if (tid == 0) {
     __hip_atomic_store(&wk.count[pair], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (every) {
-      // the last (sequence, kv head) merge of sequence b: every workgroup of
-      // the sequence has read seq_lens[b]
-      const uint32_t done = __hip_atomic_fetch_add(&wk.bcount[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (done == uint32_t(cv.Hkv - 1)) {
-        __hip_atomic_store(&wk.bcount[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ap.seq_lens[b] = n;
+    if constexpr (FUSED) {
+      const FusedTail ft = tail;
+      if (ft.every) {
+        // the last (sequence, kv head) merge of sequence b: every workgroup
+        // of the sequence has read seq_lens[b]
+        const uint32_t done = __hip_atomic_fetch_add(&ft.bcount[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == uint32_t(ft.hkv - 1)) {
+          __hip_atomic_store(&ft.bcount[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ft.seq_lens[b] = ft.n;
+        }
       }
     }
   }
@@ -1498,6 +1550,7 @@ void visit_fmt(const CacheView& cv, F&& f) {
   switch (cv.fmt) {
     case KVQ_FMT_FP8_E4M3: visit_d<KVQ_FMT_FP8_E4M3, 8, BF16>(cv, f); break;
     case KVQ_FMT_INT8: visit_d<KVQ_FMT_INT8, 8, BF16>(cv, f); break;
+    case KVQ_FMT_BF16: visit_d<KVQ_FMT_BF16, 16, BF16>(cv, f); break;
     default:
       if (cv.bits == 4) visit_d<KVQ_FMT_KIVI, 4, BF16>(cv, f);
       else visit_d<KVQ_FMT_KIVI, 2, BF16>(cv, f);

@@ -30,11 +30,25 @@ constexpr int kQuantThreads = 256;  // workgroup size the group-flush steps assu
 // Per-token FP8 E4M3 / INT8: one wave quantizes one token row, CPL = D / 64
 // channels per lane (channel lane * CPL + j in x[j]).
 // ---------------------------------------------------------------------------
-// Returns the lane's CPL code bytes (channel lane * CPL + j in byte j) and
-// sets *scale to the row's scale. Wave-collective.
+// Two floats to a bfloat16 pair, round to nearest even (x0 in the low half).
+typedef __bf16 quant_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float quant_f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pair_rne(float x0, float x1) {
+  const quant_f32x2 v = {x0, x1};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, quant_bf16x2));
+}
+
+// Returns the lane's CPL codes (channel lane * CPL + j in byte j; BF16: in
+// the 16-bit half j) and sets *scale to the row's scale (1 for BF16, whose
+// codes are the bfloat16 values). Wave-collective for FP8/INT8.
 template <int FMT, int CPL>
 __device__ __forceinline__ uint32_t quantize_token_lane(const float (&x)[CPL], float* scale) {
 #pragma clang fp contract(off)
+  if constexpr (FMT == KVQ_FMT_BF16) {
+    *scale = 1.0f;
+    const uint32_t w = bf16_pair_rne(x[0], CPL == 2 ? x[CPL - 1] : 0.0f);
+    return CPL == 2 ? w : (w & 0xffffu);
+  }
   float a = 0.0f;
 #pragma unroll
   for (int j = 0; j < CPL; ++j) a = fmaxf(a, fabsf(x[j]));
@@ -61,13 +75,27 @@ __device__ __forceinline__ uint32_t quantize_token_lane(const float (&x)[CPL], f
   return codes;
 }
 
-// Stores one lane's code bytes and (lane 0) the scale of token t of pair
-// `pair`: Key rows token-major, Value codes in 8-token blocks with one
-// 8-byte word per (permuted) channel slot.
-template <int CPL>
+// Stores one lane's codes and (lane 0) the scale of token t of pair `pair`:
+// Key rows token-major, Value codes in 8-token blocks with one 8-byte word
+// per (permuted) channel slot; BF16: 2-byte codes, 16-byte Value words in
+// channel order, no scale.
+template <int FMT, int CPL>
 __device__ __forceinline__ void store_token_codes(const CacheView& cv, size_t pair, int t, bool value, int lane,
                                                   uint32_t codes, float s) {
   constexpr int D = CPL * kWave;
+  if constexpr (FMT == KVQ_FMT_BF16) {
+    if (!value) {
+      uint8_t* dst = cv.k_codes + ((pair * cv.cap + t) * D + lane * CPL) * 2;
+      if constexpr (CPL == 2) *reinterpret_cast<uint32_t*>(dst) = codes;
+      else *reinterpret_cast<uint16_t*>(dst) = uint16_t(codes);
+    } else {
+      uint8_t* blk = cv.v_codes + (pair * (cv.cap / 8) + t / 8) * (size_t(D) * 16) + (t & 7) * 2;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j)
+        *reinterpret_cast<uint16_t*>(blk + size_t(lane * CPL + j) * 16) = uint16_t(codes >> (16 * j));
+    }
+    return;
+  }
   if (!value) {
     uint8_t* dst = cv.k_codes + (pair * cv.cap + t) * D + lane * CPL;
     if constexpr (CPL == 2) *reinterpret_cast<uint16_t*>(dst) = uint16_t(codes);

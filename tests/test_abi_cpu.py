@@ -43,7 +43,7 @@ def test_status_strings_and_version():
 
 
 def _cfg(w, max_tokens=None, **kw):
-    c = kvq.make_config({"fp8": 1, "int8": 2, "kivi": 3}[w.fmt], w.bits, w.group, w.residual, w.batch,
+    c = kvq.make_config({"fp8": 1, "int8": 2, "kivi": 3, "bf16": 4}[w.fmt], w.bits, w.group, w.residual, w.batch,
                         w.n_kv_heads, w.n_q_heads, w.head_dim, max_tokens or w.context + 64,
                         0 if w.dtype == "f32" else 1)
     for k, v in kw.items():
@@ -51,9 +51,12 @@ def _cfg(w, max_tokens=None, **kw):
     return c
 
 
-@pytest.mark.parametrize("idx", sorted(WORKLOADS))
+BF16_CACHE = {i: WORKLOADS[i].scaled(fmt="bf16", bits=16, group=0, residual=0) for i in (2, 3)}
+
+
+@pytest.mark.parametrize("idx", sorted(WORKLOADS) + ["bf16-2", "bf16-3"])
 def test_layout_matches_documented_formulas(idx):
-    w = WORKLOADS[idx]
+    w = BF16_CACHE[int(idx[5:])] if isinstance(idx, str) else WORKLOADS[idx]
     cfg = _cfg(w)
     lay = kvq.kvq_get_layout(cfg)
     pairs = w.batch * w.n_kv_heads
@@ -75,6 +78,11 @@ def test_layout_matches_documented_formulas(idx):
         order = [0, 1, 2, 4, 3, 5, 6, 7]     # k_scale, k_zero, v_scale, v_zero
         offs = [offs[i] for i in order]
         sizes = [sizes[i] for i in order]
+    elif w.fmt == "bf16":
+        # two bytes per element, no scale arrays
+        assert lay.row_bytes == 2 * w.head_dim
+        assert lay.k_scale_off == 0 and lay.v_scale_off == 0 and lay.k_zero_off == 0 and lay.resid_slots == 0
+        offs, sizes = offs[:2], sizes[:2]
     else:
         sizes += [pairs * cap * 4] * 2
         assert lay.k_zero_off == 0 and lay.k_resid_off == 0 and lay.resid_slots == 0
@@ -106,11 +114,11 @@ def test_config_validation(field, value, status):
 
 
 def test_per_token_formats_reject_kivi_fields():
-    for fmt in (kvq.FMT_FP8_E4M3, kvq.FMT_INT8):
-        cfg = _cfg(WORKLOADS[2], format=fmt)
+    for fmt, bits in ((kvq.FMT_FP8_E4M3, 8), (kvq.FMT_INT8, 8), (kvq.FMT_BF16, 16)):
+        cfg = _cfg(WORKLOADS[2], format=fmt, bits=bits)
         assert kvq.lib().kvq_get_layout(ctypes.byref(cfg), ctypes.byref(kvq.KvqLayout())) == 0
-        for field, val in (("bits", 4), ("group", 32), ("residual", 16)):
-            bad = _cfg(WORKLOADS[2], format=fmt)
+        for field, val in (("bits", 4), ("bits", 8 if bits == 16 else 16), ("group", 32), ("residual", 16)):
+            bad = _cfg(WORKLOADS[2], format=fmt, bits=bits)
             setattr(bad, field, val)
             assert kvq.lib().kvq_get_layout(ctypes.byref(bad), ctypes.byref(kvq.KvqLayout())) == kvq.ERR_INVALID
 
