@@ -173,6 +173,37 @@ def bf16_value(bits) -> np.ndarray:
     return b.view(F32).astype(F64)
 
 
+# ---------------------------------------------------------------------------
+# Group-wise symmetric INT4  [LLMS "2. INT8 and INT4 Uniform Group-Wise
+# Quantization": 4-bit codes in groups of 32, 64 or 128 elements along the
+# channel dimension, one scale per group, symmetric like the INT8 entry of the
+# same section]
+# ---------------------------------------------------------------------------
+def quantize_int4_groupwise(x, group: int):
+    """x: float32 [T, d]. Per token and per group of ``group`` consecutive
+    channels: s = max|x| / 7; code = clamp(round_half_even(x / s), -8, 7)
+    (the codes stay within [-7, 7] since s is the group's max-abs over 7); a
+    zero group gets s = 0 and codes 0. Returns codes int8 [T, d] and s
+    float32 [T, d/group]."""
+    x = np.asarray(x, dtype=F32)
+    t, d = x.shape
+    if group <= 0 or d % group:
+        raise ValueError("channel groups must divide head_dim")
+    xg = x.reshape(t, d // group, group)
+    a = np.max(np.abs(xg), axis=2)
+    s = (a / F32(7.0)) + F32(0.0)
+    pos = s > 0
+    div = np.where(pos, s, F32(1.0))[..., None]
+    q = np.rint(xg / div)
+    q = np.where(pos[..., None], np.clip(q, F32(-8.0), F32(7.0)), F32(0.0))
+    return q.reshape(t, d).astype(np.int8), s.astype(F32)
+
+
+def dequantize_int4_groupwise(codes, s, group: int):
+    """codes [T, d] with per-token-group s [T, d/group] -> float64 [T, d]."""
+    return np.asarray(codes, F64) * np.repeat(np.asarray(s, F64), group, axis=1)
+
+
 def dequantize_int8(codes, s):
     return np.asarray(codes, F64) * np.asarray(s, F64)[..., None]
 
@@ -279,8 +310,9 @@ def unpack_codes(packed, bits: int) -> np.ndarray:
 class SequenceCache:
     """State of one sequence's cache for one KV head.
 
-    fmt: "fp8", "int8", "kivi" or "bf16" (the unquantized 16-bit cache:
-    codes are the bfloat16 patterns of the inputs, no scales). Inputs are
+    fmt: "fp8", "int8", "kivi", "int4" (group-wise symmetric, ``group``
+    channels per scale, Key and Value alike) or "bf16" (the unquantized
+    16-bit cache: codes are the bfloat16 patterns of the inputs, no scales). Inputs are
     float32 rows (bf16 inputs are widened exactly by the caller). For KIVI,
     flushed groups are kept as lists of arrays, the residual as float32 rows
     in arrival order.
@@ -288,7 +320,7 @@ class SequenceCache:
 
     def __init__(self, fmt: str, head_dim: int, bits: int = 8, group: int = 0,
                  residual: int = 0):
-        if fmt not in ("fp8", "int8", "kivi", "bf16"):
+        if fmt not in ("fp8", "int8", "kivi", "int4", "bf16"):
             raise ValueError(fmt)
         self.fmt, self.d, self.bits, self.group, self.residual = fmt, head_dim, bits, group, residual
         self.n = 0
@@ -309,6 +341,11 @@ class SequenceCache:
         if self.fmt == "int8":
             for x, codes, scales in ((k, self.k_codes, self.k_scale), (v, self.v_codes, self.v_scale)):
                 q, s = quantize_int8_per_token(x)
+                codes.append(q)
+                scales.append(s)
+        elif self.fmt == "int4":
+            for x, codes, scales in ((k, self.k_codes, self.k_scale), (v, self.v_codes, self.v_scale)):
+                q, s = quantize_int4_groupwise(x, self.group)
                 codes.append(q)
                 scales.append(s)
         elif self.fmt == "bf16":
@@ -364,6 +401,9 @@ class SequenceCache:
                   for c, s, z in zip(self.v_codes, self.v_scale, self.v_zero)]
             ks.append(self.resid_k.astype(F64))
             vs.append(self.resid_v.astype(F64))
+        elif self.fmt == "int4":
+            ks = [dequantize_int4_groupwise(c, s, self.group) for c, s in zip(self.k_codes, self.k_scale)]
+            vs = [dequantize_int4_groupwise(c, s, self.group) for c, s in zip(self.v_codes, self.v_scale)]
         elif self.fmt == "bf16":
             ks = [bf16_value(c) for c in self.k_codes]
             vs = [bf16_value(c) for c in self.v_codes]

@@ -462,3 +462,59 @@ def test_bf16_cache_halves_nothing_the_memory_table_says_2_bytes():
     # [BEA] §1: BF16 is the 2-byte row of the table (320 KB per token for the
     # 80-layer, 8-KV-head, d = 128 model); the bf16 cache stores exactly that
     assert O.kv_bytes_per_token(80, 8, 128, 2) == 327680
+
+
+# --- group-wise symmetric INT4 (llms.blog "2. INT8 and INT4 Uniform Group-Wise Quantization") ---
+def test_int4_groupwise_ties_and_closed_form():
+    # max-abs 7 -> s = 1 exactly; ties round half to even
+    x = np.array([[7.0, 3.5, -3.5, 2.5, 0.5, -0.5, 1.5, 0.0]], F32)
+    codes, s = O.quantize_int4_groupwise(x, 8)
+    assert s.shape == (1, 1) and s[0, 0] == F32(1.0)
+    assert list(codes[0]) == [7, 4, -4, 2, 0, 0, 2, 0]
+    # max-abs element of each group maps to +-7; the range never needs -8
+    rng = np.random.default_rng(5)
+    y = rng.standard_normal((300, 128)).astype(F32) * np.exp(rng.standard_normal((300, 1))).astype(F32)
+    for G in (32, 64, 128):
+        c, sc = O.quantize_int4_groupwise(y, G)
+        assert sc.shape == (300, 128 // G)
+        cg = np.abs(c.astype(int)).reshape(300, 128 // G, G)
+        assert np.all(cg.max(axis=2) == 7) and c.min() >= -7
+        np.testing.assert_array_equal(sc, np.max(np.abs(y.reshape(300, -1, G)), axis=2) / F32(7))
+
+
+def test_int4_groupwise_isolates_outlier_channel_page_matrix():
+    """The page: grouping isolates channel outliers to specific sub-vectors.
+    On the worked Key matrix, one group over a token's 4 channels lets the
+    outlier channel (8.0 .. 9.0) crush the small channels to code 0; groups
+    of 2 keep the first two channels' resolution."""
+    K = np.array(_golden("bea_kivi_examples.json")["key_matrix"], F32)
+    c4, s4 = O.quantize_int4_groupwise(K, 4)
+    np.testing.assert_array_equal(s4[:, 0], np.max(np.abs(K), axis=1) / F32(7))
+    assert np.all(c4[:, [0, 1, 3]] == 0) and np.all(c4[:, 2] == 7)
+    c2, s2 = O.quantize_int4_groupwise(K, 2)
+    assert np.all(np.abs(c2[:, :2]).max(axis=1) == 7)          # small channels keep full range
+    np.testing.assert_array_equal(s2[:, 0], np.max(np.abs(K[:, :2]), axis=1) / F32(7))
+    # scaling the outlier group leaves the other group's codes unchanged
+    K2 = K.copy()
+    K2[:, 2:] *= F32(16.0)
+    c2b, _ = O.quantize_int4_groupwise(K2, 2)
+    np.testing.assert_array_equal(c2b[:, :2], c2[:, :2])
+
+
+def test_int4_groupwise_round_trip_and_zero_groups():
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((64, 128)) * 3).astype(F32)
+    x[5, 32:64] = 0.0                                            # an all-zero group
+    codes, s = O.quantize_int4_groupwise(x, 32)
+    assert s[5, 1] == 0 and np.all(codes[5, 32:64] == 0)
+    deq = O.dequantize_int4_groupwise(codes, s, 32)
+    bound = np.repeat(s.astype(np.float64), 32, axis=1) / 2
+    slack = 2.0 ** -20 * np.repeat(np.max(np.abs(x.reshape(64, 4, 32)), axis=2), 32, axis=1)
+    assert np.all(np.abs(deq - x) <= bound + slack)
+    # a sequence cache of this format appends chunk by chunk like the others
+    seq = O.SequenceCache("int4", 128, 4, 32)
+    seq.append(x[:10], -x[:10])
+    seq.append(x[10:], -x[10:])
+    K, V = seq.dequantized()
+    np.testing.assert_array_equal(K, deq)
+    np.testing.assert_array_equal(V, O.dequantize_int4_groupwise(*O.quantize_int4_groupwise(-x, 32), 32))
