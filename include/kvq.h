@@ -81,7 +81,8 @@ typedef enum kvq_format {
   KVQ_FMT_FP8_E4M3 = 1,    /* per-token OCP FP8 E4M3, fp32 scale per token   */
   KVQ_FMT_INT8 = 2,        /* per-token symmetric INT8, fp32 scale per token */
   KVQ_FMT_KIVI = 3,        /* KIVI asymmetric INT4/INT2 + residual window    */
-  KVQ_FMT_BF16 = 4         /* unquantized bfloat16 cache (the 16-bit baseline) */
+  KVQ_FMT_BF16 = 4,        /* unquantized bfloat16 cache (the 16-bit baseline) */
+  KVQ_FMT_INT4 = 5         /* group-wise symmetric INT4, per token, fp32 scale per group */
 } kvq_format;
 
 typedef enum kvq_dtype {
@@ -93,6 +94,11 @@ typedef enum kvq_dtype {
  * n_q_heads = g * n_kv_heads with g in 1..8; bits 8 for FP8/INT8 and 16 for
  * BF16 (group and residual must be 0), bits 4 or 2 for KIVI with group 32
  * or 64 dividing head_dim and 0 <= residual <= 4096; 1 <= max_tokens <= 2^24.
+ * KVQ_FMT_INT4 ([LLMS] "2. INT8 and INT4 Uniform Group-Wise Quantization"):
+ * bits 4, group 32, 64 or 128 dividing head_dim, residual 0; Key and Value
+ * alike, per token and per group of `group` consecutive channels, s = max|x|
+ * / 7, code = clamp(rint(x / s), -8, 7) (within [-7, 7]), dequantized code *
+ * s, stored as the nibble code + 8.
  * KVQ_FMT_BF16 is the unquantized 16-bit cache of [BEA] §1's table (2 bytes
  * per element): it stores each input rounded to bfloat16 (to nearest, ties
  * to even; bf16 inputs bit-unchanged) with no scales, and decodes through
@@ -100,8 +106,8 @@ typedef enum kvq_dtype {
  * that store fewer bytes. */
 typedef struct kvq_config {
   int32_t format;      /* kvq_format                                         */
-  int32_t bits;        /* code width: 8 (FP8, INT8), 4 or 2 (KIVI), 16 (BF16) */
-  int32_t group;       /* KIVI G: tokens per Key group = channels per Value group */
+  int32_t bits;        /* code width: 8 (FP8, INT8), 4 or 2 (KIVI), 4 (INT4), 16 (BF16) */
+  int32_t group;       /* KIVI G: tokens per Key group = channels per Value group; INT4: channels per scale */
   int32_t residual;    /* KIVI R: most recent tokens always kept unquantized */
   int32_t batch;       /* B sequences                                        */
   int32_t n_kv_heads;  /* Hkv                                                */
@@ -129,6 +135,11 @@ typedef struct kvq_config {
  *           channel 16*x + m of that chunk, so a 16-byte load at slot W*m
  *           returns channel m of W consecutive 16-channel tiles (W = 1, BF16:
  *           no permutation).
+ *  INT4:    k_codes rows of d nibbles (code + 8) in chunks of 8 channels:
+ *           chunk (kk, r) = channels [32 kk + 8 r, 32 kk + 8 r + 8) sits at
+ *           byte (d/8) r + 4 kk, channel 32 kk + 8 r + e in nibble e (low
+ *           nibble first); v_codes as KIVI INT4 (TB = 8, 4-byte words);
+ *           k_scale, v_scale [B][Hkv][cap][d/group] fp32.
  *  FP8/INT8: k_scale, v_scale [B][Hkv][cap] fp32; k_zero, v_zero unused (0).
  *  BF16:    no scale or zero-point arrays (offsets 0).
  *  KIVI:    k_scale, k_zero [B][Hkv][cap/G][d] fp32 (per group, per channel);
@@ -142,7 +153,7 @@ typedef struct kvq_layout {
   uint64_t k_scale_off, v_scale_off;
   uint64_t k_zero_off, v_zero_off;
   uint64_t k_resid_off, v_resid_off;
-  int32_t token_capacity;  /* cap: max_tokens rounded up to 32 (FP8/INT8/BF16) or to G (KIVI) */
+  int32_t token_capacity;  /* cap: max_tokens rounded up to 32 (FP8/INT8/INT4/BF16) or to G (KIVI) */
   int32_t resid_slots;     /* KIVI ring slots = residual + group; 0 otherwise */
   int32_t row_bytes;       /* head_dim * bits / 8                             */
   int32_t elem_bytes;      /* bytes of one in_dtype element (4 or 2)          */

@@ -72,6 +72,58 @@ __global__ __launch_bounds__(kThreads) void append_per_token(CacheView cv, const
 }
 
 // ---------------------------------------------------------------------------
+// Group-wise symmetric INT4: one wave per 8-token Value block. The wave
+// quantizes the block's new tokens one row at a time (Key and Value),
+// stores the Key nibbles and the scales as it goes, and collects the Value
+// nibbles of its lanes' channels; it then rewrites each channel's block word
+// once, keeping the nibbles of tokens it does not own. Each block word has
+// one writer per call, so the read-modify-write is race-free.
+// ---------------------------------------------------------------------------
+template <int D, int G, bool BF16>
+__global__ __launch_bounds__(kThreads) void append_int4(CacheView cv, const int32_t* __restrict__ seq_lens,
+                                                       const void* __restrict__ kin, const void* __restrict__ vin,
+                                                       int T, const int32_t* __restrict__ append_lens) {
+  constexpr int CPL = D / kWave;
+  const int b = blockIdx.z, h = blockIdx.y;
+  int n, tb;
+  if (!append_range(cv, seq_lens, append_lens, T, b, &n, &tb)) return;
+  if (tb == 0) return;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const size_t pair = pair_index(cv, b, h);
+  const int blk = n / 8 + int(blockIdx.x) * (kThreads / kWave) + wave;
+  const int t_lo = max(n, 8 * blk), t_hi = min(n + tb, 8 * blk + 8);
+  if (t_lo >= t_hi) return;
+  uint32_t vw[CPL], vm[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) vw[j] = vm[j] = 0u;
+  for (int t = t_lo; t < t_hi; ++t) {
+    const size_t in_base = (pair * T + (t - n)) * D + lane * CPL;
+    float xk[CPL], xv[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      xk[j] = load_elem<BF16>(kin, in_base + j);
+      xv[j] = load_elem<BF16>(vin, in_base + j);
+    }
+    float sk, sv;
+    const uint32_t uk = quantize_token_int4<G, CPL>(xk, &sk);
+    const uint32_t uv = quantize_token_int4<G, CPL>(xv, &sv);
+    store_int4_key<G, CPL>(cv, pair, t, lane, uk, sk);
+    if (lane % (G / CPL) == 0) cv.v_scale[(pair * cv.cap + t) * (D / G) + (lane * CPL) / G] = sv;
+    const int sh = 4 * (t % 8);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      vw[j] |= ((uv >> (4 * j)) & 0xFu) << sh;
+      vm[j] |= 0xFu << sh;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    uint32_t* w = int4_value_word<D>(cv, pair, t_lo, lane * CPL + j);
+    *w = (*w & ~vm[j]) | vw[j];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // KIVI group flush: one workgroup per (group slot, kv head, sequence). The
 // steps (staging, Key half, Value half) are shared with the fused append +
 // decode kernel.
@@ -141,6 +193,28 @@ void launch_per_token(const CacheView& cv, int32_t* seq_lens, const void* k, con
   append_per_token<FMT, D, BF16><<<grid, kThreads, 0, st>>>(cv, seq_lens, k, v, T, al);
 }
 
+template <int D, int G, bool BF16>
+void launch_int4(const CacheView& cv, int32_t* seq_lens, const void* k, const void* v, int T, const int32_t* al,
+                 hipStream_t st) {
+  // blocks touched by T tokens starting anywhere: at most T / 8 + 2
+  const int nblk = T / 8 + 2;
+  const dim3 grid((nblk + kThreads / kWave - 1) / (kThreads / kWave), cv.Hkv, cv.B);
+  append_int4<D, G, BF16><<<grid, kThreads, 0, st>>>(cv, seq_lens, k, v, T, al);
+}
+
+template <bool BF16>
+void int4_dg(const CacheView& cv, int32_t* sl, const void* k, const void* v, int T, const int32_t* al,
+             hipStream_t st) {
+  if (cv.D == 128) {
+    if (cv.G == 32) launch_int4<128, 32, BF16>(cv, sl, k, v, T, al, st);
+    else if (cv.G == 64) launch_int4<128, 64, BF16>(cv, sl, k, v, T, al, st);
+    else launch_int4<128, 128, BF16>(cv, sl, k, v, T, al, st);
+  } else {
+    if (cv.G == 32) launch_int4<64, 32, BF16>(cv, sl, k, v, T, al, st);
+    else launch_int4<64, 64, BF16>(cv, sl, k, v, T, al, st);
+  }
+}
+
 template <int BITS, int G, int D, bool BF16>
 void launch_flush(const CacheView& cv, int32_t* seq_lens, const void* k, const void* v, int T,
                   const int32_t* al, hipStream_t st) {
@@ -184,6 +258,9 @@ hipError_t launch_append(const CacheView& cv, int32_t* seq_lens, const void* k_n
     if (cv.fmt == KVQ_FMT_FP8_E4M3) {
       if (cv.bf16) per_token_d<KVQ_FMT_FP8_E4M3, true>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
       else per_token_d<KVQ_FMT_FP8_E4M3, false>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
+    } else if (cv.fmt == KVQ_FMT_INT4) {
+      if (cv.bf16) int4_dg<true>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
+      else int4_dg<false>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
     } else if (cv.fmt == KVQ_FMT_BF16) {
       if (cv.bf16) per_token_d<KVQ_FMT_BF16, true>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
       else per_token_d<KVQ_FMT_BF16, false>(cv, seq_lens, k_new, v_new, T, append_lens, stream);

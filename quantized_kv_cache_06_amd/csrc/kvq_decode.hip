@@ -348,7 +348,13 @@ __device__ __forceinline__ constexpr int kfactor_log2(int kk, int i) {
 template <int FMT, int BITS>
 __device__ __forceinline__ u32x4 key_operand(const uint32_t* kw, int kk) {
   u32x4 a;
-  if constexpr (BITS == 16) {
+  if constexpr (FMT == KVQ_FMT_INT4) {
+    // group-wise INT4: chunk word kk holds the k-step's 8 nibbles (code + 8);
+    // pair j = (nibble j, nibble j + 4) as bf16 128 + nibble, exact
+    const uint32_t w = kw[kk];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = and_or(w >> (4 * j), 0x000F000Fu, kMagic128);
+  } else if constexpr (BITS == 16) {
     // bf16 rows: 16-byte piece kk holds the k-step's 8 channels as they are
     a[0] = kw[4 * kk];
     a[1] = kw[4 * kk + 1];
@@ -556,7 +562,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 // as one more piece of the workgroup's wave merge: maximum = its score, sum
 // = 1, output = its dequantized Value row. Every load (the two new rows and
 // the query) is issued before the first barrier. Workgroup-collective.
-template <int FMT, int D, bool BF16>
+template <int FMT, int D, int G, bool BF16>
 __device__ __forceinline__ void new_token_piece(const CacheView& cv, int b, int h, int t, const AppendIn& ap,
                                                 const void* __restrict__ q, float sm_log2, SmemQuant<D>& sm) {
   constexpr int CPL = D / kWave;
@@ -572,10 +578,30 @@ __device__ __forceinline__ void new_token_piece(const CacheView& cv, int b, int 
 #pragma unroll
     for (int e = 0; e < CPL; ++e) x[e] = load_elem<BF16>(wave ? ap.v : ap.k, pair * D + lane * CPL + e);
     float sc;
-    const uint32_t codes = quantize_token_lane<FMT, CPL>(x, &sc);
-    store_token_codes<FMT, CPL>(cv, pair, t, wave == 1, lane, codes, sc);
+    uint32_t codes;
+    if constexpr (FMT == KVQ_FMT_INT4) {
+      codes = quantize_token_int4<G, CPL>(x, &sc);
+      if (wave == 0) {
+        store_int4_key<G, CPL>(cv, pair, t, lane, codes, sc);
+      } else {
+        if (lane % (G / CPL) == 0) cv.v_scale[(pair * cv.cap + t) * (D / G) + (lane * CPL) / G] = sc;
+        // this workgroup is the only writer of the sequence's block words
+        const int sh = 4 * (t % 8);
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+          uint32_t* w = int4_value_word<D>(cv, pair, t, lane * CPL + e);
+          *w = (*w & ~(0xFu << sh)) | (((codes >> (4 * e)) & 0xFu) << sh);
+        }
+      }
+    } else {
+      codes = quantize_token_lane<FMT, CPL>(x, &sc);
+      store_token_codes<FMT, CPL>(cv, pair, t, wave == 1, lane, codes, sc);
+    }
     float c[2];  // the codes as values, exactly
-    if constexpr (FMT == KVQ_FMT_BF16) {
+    if constexpr (FMT == KVQ_FMT_INT4) {
+      c[0] = float(int(codes & 0xFu) - 8);
+      c[1] = float(int((codes >> 4) & 0xFu) - 8);
+    } else if constexpr (FMT == KVQ_FMT_BF16) {
       c[0] = bf_lo(codes);
       c[1] = bf_hi(codes);
     } else if constexpr (FMT == KVQ_FMT_FP8_E4M3) {
@@ -630,11 +656,14 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   constexpr int LKB = CPL * BITS / 8;         // Key bytes per lane per token
   constexpr int VWB = BITS == 16 ? 16 : BITS == 8 ? 8 : 4;  // bytes per Value word (one channel, one block)
   constexpr bool SCALED = FMT != KVQ_FMT_BF16;  // per-token scales (FP8/INT8) or KIVI metadata
+  // group-wise INT4: per-token scales of each channel group for Key and Value
+  constexpr bool INT4G = FMT == KVQ_FMT_INT4;
   constexpr int TB = BITS == 2 ? 16 : 8;      // tokens per Value block
   constexpr int VW = 16 / VWB;                // Value words per 16-byte load
   constexpr int NVL = D / (16 * VW);          // 16-byte Value loads per lane per tile
-  constexpr int NVG = KIVI ? D / (G > 0 ? G : 1) : 1;  // Value channel groups
-  constexpr int MPG = KIVI ? G / 16 : NMT;    // channel tiles per Value channel group
+  constexpr int NVG = KIVI || INT4G ? D / (G > 0 ? G : 1) : 1;  // Value channel groups
+  constexpr int MPG = KIVI || INT4G ? G / 16 : NMT;    // channel tiles per Value channel group
+  constexpr int KPG = INT4G ? G / 32 : 1;     // INT4: score k-steps per channel group
   constexpr int KGL = D / 32;                 // Key group floats per lane (lanes 0-31 scale, 32-63 zero)
   constexpr int NPF = (KIVI && G == 32 && KVQ_DECODE_NPF > 2) ? 2 : KVQ_DECODE_NPF;  // ring slots (register budget)
   static_assert(KGL == 2 || KGL == 4, "group load width");
@@ -677,7 +706,9 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   for (int i = 0; i < NMT; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   // KIVI: per channel group, sum_t p_t (z_t + kCenter s_t): the zero-points
   // plus the centre the Value codes are taken about in the matrix core
-  constexpr float kCenter = BITS == 4 ? 7.0f : 1.0f;
+  // (group-wise INT4: the codes are stored as code + 8, so the centre 8
+  // leaves exactly code * p')
+  constexpr float kCenter = INT4G ? 8.0f : BITS == 4 ? 7.0f : 1.0f;
   const uint32_t cpair = pack_bf16(-(128.0f + kCenter), -(128.0f + kCenter));
   const u32x4 kCenterA = {cpair, cpair, cpair, cpair};
   float zb[NVG];
@@ -753,6 +784,17 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
     if constexpr (!SCALED) {
       (void)part;
       (void)qi;
+    } else if constexpr (INT4G) {
+      const float* src = (part ? cv.v_scale : cv.k_scale) + (pair * cv.cap + T0 + qi) * NVG;
+      if constexpr (NVG == 4) {
+        const f32x4 x = load_vec<f32x4, kMetaNT>(reinterpret_cast<const uint8_t*>(src));
+        sl.mw[0] = x[0]; sl.mw[1] = x[1]; sl.mw[2] = x[2]; sl.mw[3] = x[3];
+      } else if constexpr (NVG == 2) {
+        const f32x2 x = load_vec<f32x2, kMetaNT>(reinterpret_cast<const uint8_t*>(src));
+        sl.mw[0] = x[0]; sl.mw[1] = x[1];
+      } else {
+        sl.mw[0] = load_vec<float, kMetaNT>(reinterpret_cast<const uint8_t*>(src));
+      }
     } else if constexpr (!KIVI) {
       sl.mw[0] = load_vec<float, kMetaNT>(
           reinterpret_cast<const uint8_t*>((part ? cv.v_scale : cv.k_scale) + (pair * cv.cap + T0 + qi)));
@@ -794,7 +836,8 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
     load_elems<BF16, EPT>(q, (size_t(b) * cv.Hq + size_t(h) * g + min(j, g - 1)) * D + c, qx);
   } else {
     const size_t qrow = (size_t(b) * cv.Hq + size_t(h) * g + min(hh, g - 1)) * D;
-    if constexpr (BITS == 16) {
+    if constexpr (BITS == 16 || INT4G) {
+      // k-step kk of row group r: channels [32 kk + 8 r, 32 kk + 8 r + 8)
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) load_elems<BF16, 8>(q, qrow + 32 * kk + 8 * r, qx + 8 * kk);
     } else if constexpr (KSPLIT) {
@@ -815,6 +858,7 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   // elements, eq putting the head's largest |q * 2^-kfactor| in [64, 128).
   constexpr int NKW = NKK / 2;
   float qn[NKW][4][2];
+  float kb4[NVG];  // group-wise INT4: 136 * the query sum of each channel group
   int eq = 0, fbase = 0;
   const float m1 = KIVI ? opaque_minus_one() : -1.0f;
   if constexpr (KIVI) {
@@ -846,6 +890,13 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) qn[kw][e][h2] = __builtin_amdgcn_ldexpf(qn[kw][e][h2], eq);
   } else {
+    // group-wise INT4: the Key codes enter as 128 + (code + 8), so 136 times
+    // the query sum of each channel group comes off its dot product. The sum
+    // is taken over the hi + lo values the matrix core multiplies (exact in
+    // fp32), so the offset cancels exactly.
+    float qs[NVG];
+#pragma unroll
+    for (int gi = 0; gi < NVG; ++gi) qs[gi] = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
@@ -854,7 +905,14 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
         const float x1 = hh < g ? qx[cperm<BITS>(kk, 2 * e + 1)] : 0.0f;
         const Split2 sp = split_pair(x0, x1);
         bq[kk][e] = lo_col ? sp.lo : sp.hi;
+        if constexpr (INT4G) {
+          qs[kk / KPG] += (bf_lo(sp.hi) + bf_lo(sp.lo)) + (bf_hi(sp.hi) + bf_hi(sp.lo));
+        }
       }
+    }
+    if constexpr (INT4G) {
+#pragma unroll
+      for (int gi = 0; gi < NVG; ++gi) kb4[gi] = sum_rows(qs[gi]) * 136.0f;
     }
   }
 
@@ -928,20 +986,25 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
     }
 
     // ---- scores ----
-    f32x4 acc[2];
+    // group-wise INT4: one accumulator per channel group (its scale is per
+    // token); the others: one per score tile
+    constexpr int NACC = INT4G ? NVG : 1;
+    f32x4 acc[2][NACC];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int gi = 0; gi < NACC; ++gi) acc[t][gi] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        if constexpr (KIVI) acc[t] = mfma_f16(key_operand<FMT, BITS>(kc[t], kk), bq[kk], acc[t]);
-        else acc[t] = mfma_bf16(key_operand<FMT, BITS>(kc[t], kk), bq[kk], acc[t]);
+        const int gi = INT4G ? kk / KPG : 0;
+        if constexpr (KIVI) acc[t][gi] = mfma_f16(key_operand<FMT, BITS>(kc[t], kk), bq[kk], acc[t][gi]);
+        else acc[t][gi] = mfma_bf16(key_operand<FMT, BITS>(kc[t], kk), bq[kk], acc[t][gi]);
       }
     }
     const int valid = KIVI ? kTile : min(kTile, t1 - T0);
     // this lane's tokens: tok(t, r, j) = base_t + j, 4 consecutive per t
     f32x4 ks[2], vs[2];
-    if constexpr (!KIVI && SCALED) {
+    if constexpr (!KIVI && SCALED && !INT4G) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         ks[t] = *reinterpret_cast<const f32x4*>(meta0 + tok<BITS>(t, r, 0));
@@ -954,8 +1017,19 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float x = add_ror8(acc[t][j]);
+        float x;
+        if constexpr (INT4G) {
+          // sum over channel groups of (dot - bias) * the token's group scale
+          const float* ksr = meta0 + tok<BITS>(t, r, j) * NVG;
+          x = 0.0f;
+#pragma unroll
+          for (int gi = 0; gi < NVG; ++gi) x = fmaf(add_ror8(acc[t][gi][j]) - kb4[gi], ksr[gi], x);
+          x *= sm_log2;
+        } else {
+          x = add_ror8(acc[t][0][j]);
+        }
         if constexpr (KIVI) x = fmaf(x, kscale, kbias);
+        else if constexpr (INT4G) (void)0;
         else if constexpr (SCALED) x = x * ks[t][j] * sm_log2;
         else x = x * sm_log2;
         if (tok<BITS>(t, r, j) >= valid) x = -INFINITY;
@@ -974,8 +1048,10 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < NMT; ++i) o[i] *= alpha;
+      if constexpr (KIVI) {
 #pragma unroll
-      for (int j = 0; j < NVG; ++j) zb[j] *= alpha;
+        for (int j = 0; j < NVG; ++j) zb[j] *= alpha;
+      }
     }
     float psum = 0.0f;
 #pragma unroll
@@ -989,7 +1065,7 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
     l_run += psum;
 
     // ---- values ----
-    if constexpr (!KIVI) {
+    if constexpr (!KIVI && !INT4G) {
       float pv[2][4];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -1017,19 +1093,22 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
         for (int u = 0; u < 2; ++u) ps[t][u] = select_bits(lo_mask, sc[t][2 + u], sc[t][u]);
       // per-token Value scale and zero of each channel group, for the lane's
       // two tokens of each score tile
+      // KIVI: meta0 Value scales, meta1 Value zero-points; group-wise INT4:
+      // meta1 Value scales (meta0 holds the Key scales), no zero-points
+      const float* vsm = INT4G ? meta1 : meta0;
       float vsf[2][2 * NVG], vzf[2][2 * NVG];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int off = (tok<BITS>(t, r, 0) + ja) * NVG;
         if constexpr (NVG == 1) {
-          const f32x2 a = *reinterpret_cast<const f32x2*>(meta0 + off);
+          const f32x2 a = *reinterpret_cast<const f32x2*>(vsm + off);
           const f32x2 z = *reinterpret_cast<const f32x2*>(meta1 + off);
           vsf[t][0] = a[0]; vsf[t][1] = a[1];
           vzf[t][0] = z[0]; vzf[t][1] = z[1];
         } else {
 #pragma unroll
           for (int v = 0; v < NVG / 2; ++v) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(meta0 + off + 4 * v);
+            const f32x4 a = *reinterpret_cast<const f32x4*>(vsm + off + 4 * v);
             const f32x4 z = *reinterpret_cast<const f32x4*>(meta1 + off + 4 * v);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -1049,9 +1128,9 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
           for (int u = 0; u < 2; ++u) {
             const float vsc = vsf[t][u * NVG + jg];
             pv[t][u] = ps[t][u] * vsc;
-            zs = fmaf(ps[t][u], fmaf(kCenter, vsc, vzf[t][u * NVG + jg]), zs);
+            if constexpr (KIVI) zs = fmaf(ps[t][u], fmaf(kCenter, vsc, vzf[t][u * NVG + jg]), zs);
           }
-        zb[jg] += zs;
+        if constexpr (KIVI) zb[jg] += zs;
         const Split2 s0 = split_pair(pv[0][0], pv[1][0]);  // pair ja
         const Split2 s1 = split_pair(pv[0][1], pv[1][1]);  // pair ja + 1
         u32x4 bp;
@@ -1086,7 +1165,7 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   bool has_new = false;
   if constexpr (FUSED && !KIVI) {
     has_new = t_new >= 0;  // uniform
-    if (has_new) new_token_piece<FMT, D, BF16>(cv, b, h, t_new, ap, q, sm_log2, sm);
+    if (has_new) new_token_piece<FMT, D, G, BF16>(cv, b, h, t_new, ap, q, sm_log2, sm);
   }
 
   // ---- merge the 4 waves (and the new token) through LDS ----
@@ -1373,7 +1452,7 @@ __global__ __launch_bounds__(kThreads, (min_wg_per_cu<FMT, BITS, D, G>())) void 
                                                         const void* __restrict__ q, float sm_log2, float* __restrict__ out,
                                                         DecodeWork wk, AppendIn ap) {
   constexpr bool KIVI = FMT == KVQ_FMT_KIVI;
-  __shared__ float smem[smem_floats<D, G, FUSED>()];
+  __shared__ float smem[smem_floats<D, (KIVI ? G : 0), FUSED>()];
   __shared__ uint32_t ticket;
   // What a fused call needs after the token loop is parked in LDS, so that
   // it does not hold scalar registers through the loop.
@@ -1531,7 +1610,13 @@ struct Variant {
 
 template <int FMT, int BITS, int D, bool BF16, class F>
 void visit_g(const CacheView& cv, F&& f) {
-  if constexpr (FMT == KVQ_FMT_KIVI) {
+  if constexpr (FMT == KVQ_FMT_INT4) {
+    // groups divide head_dim: 128-channel groups exist only at d = 128
+    if (cv.G == 32) f(Variant<FMT, BITS, D, 32, BF16>{});
+    else if constexpr (D == 64) f(Variant<FMT, BITS, D, 64, BF16>{});
+    else if (cv.G == 64) f(Variant<FMT, BITS, D, 64, BF16>{});
+    else f(Variant<FMT, BITS, D, 128, BF16>{});
+  } else if constexpr (FMT == KVQ_FMT_KIVI) {
     if (cv.G == 32) f(Variant<FMT, BITS, D, 32, BF16>{});
     else f(Variant<FMT, BITS, D, 64, BF16>{});
   } else {
@@ -1551,6 +1636,7 @@ void visit_fmt(const CacheView& cv, F&& f) {
     case KVQ_FMT_FP8_E4M3: visit_d<KVQ_FMT_FP8_E4M3, 8, BF16>(cv, f); break;
     case KVQ_FMT_INT8: visit_d<KVQ_FMT_INT8, 8, BF16>(cv, f); break;
     case KVQ_FMT_BF16: visit_d<KVQ_FMT_BF16, 16, BF16>(cv, f); break;
+    case KVQ_FMT_INT4: visit_d<KVQ_FMT_INT4, 4, BF16>(cv, f); break;
     default:
       if (cv.bits == 4) visit_d<KVQ_FMT_KIVI, 4, BF16>(cv, f);
       else visit_d<KVQ_FMT_KIVI, 2, BF16>(cv, f);

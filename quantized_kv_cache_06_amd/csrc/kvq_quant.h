@@ -110,6 +110,68 @@ __device__ __forceinline__ void store_token_codes(const CacheView& cv, size_t pa
 }
 
 // ---------------------------------------------------------------------------
+// Group-wise symmetric INT4 ("KV Cache Quantization in Production LLM
+// Serving", llms.blog, "2. INT8 and INT4 Uniform Group-Wise Quantization"):
+// per token and per group of G channels, s = max|x| / 7, code =
+// clamp(rint(x / s), -8, 7) (within [-7, 7]), stored as the nibble code + 8.
+// One wave quantizes one token row, CPL = D / 64 channels per lane.
+// ---------------------------------------------------------------------------
+// Returns the lane's nibbles (channel lane * CPL + j in bits [4j, 4j + 4))
+// and sets *scale to the scale of the lane's channel group. Wave-collective.
+template <int G, int CPL>
+__device__ __forceinline__ uint32_t quantize_token_int4(const float (&x)[CPL], float* scale) {
+#pragma clang fp contract(off)
+  constexpr int LPG = G / CPL;  // lanes per channel group: an aligned power-of-two run
+  float a = 0.0f;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) a = fmaxf(a, fabsf(x[j]));
+#pragma unroll
+  for (int o = 1; o < LPG; o <<= 1) a = fmaxf(a, __shfl_xor(a, o, kWave));
+  const float s = a / 7.0f;
+  uint32_t u = 0;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    float qv = 0.0f;
+    if (s > 0.0f) qv = fminf(fmaxf(rintf(x[j] / s), -8.0f), 7.0f);
+    u |= uint32_t(int32_t(qv) + 8) << (4 * j);
+  }
+  *scale = s;
+  return u;
+}
+
+// Byte of a Key row (d nibbles) that holds channel c: rows are stored in
+// chunks of 8 channels, chunk (kk, r) = channels [32 kk + 8 r, 32 kk + 8 r + 8)
+// at byte (d / 8) r + 4 kk, channel 32 kk + 8 r + e in nibble e of the chunk.
+template <int D>
+__device__ __forceinline__ int int4_key_byte(int c) {
+  return (D / 8) * ((c % 32) / 8) + 4 * (c / 32) + (c % 8) / 2;
+}
+
+// Stores one lane's Key nibbles of token t and (each group's first lane) the
+// token's Key scales. With CPL = 1 neighbouring lanes share a byte.
+template <int G, int CPL>
+__device__ __forceinline__ void store_int4_key(const CacheView& cv, size_t pair, int t, int lane, uint32_t u,
+                                               float s) {
+  constexpr int D = CPL * kWave;
+  uint8_t* row = cv.k_codes + (pair * cv.cap + t) * (D / 2);
+  if constexpr (CPL == 2) {
+    row[int4_key_byte<D>(2 * lane)] = uint8_t(u);
+  } else {
+    const uint32_t other = uint32_t(__shfl_xor(int(u), 1, kWave));
+    if ((lane & 1) == 0) row[int4_key_byte<D>(lane)] = uint8_t(u | (other << 4));
+  }
+  if (lane % (G / CPL) == 0) cv.k_scale[(pair * cv.cap + t) * (D / G) + (lane * CPL) / G] = s;
+}
+
+// Value word of channel c in the 8-token block holding token t (the KIVI
+// INT4 layout: one 32-bit word per permuted channel slot, token t % 8 in
+// bits [4 (t % 8), 4 (t % 8) + 4)).
+template <int D>
+__device__ __forceinline__ uint32_t* int4_value_word(const CacheView& cv, size_t pair, int t, int c) {
+  return reinterpret_cast<uint32_t*>(cv.v_codes) + (pair * (cv.cap / 8) + t / 8) * D + value_slot<4>(c);
+}
+
+// ---------------------------------------------------------------------------
 // KIVI group flush, one workgroup of kQuantThreads threads per group. The G
 // tokens are staged in LDS as fp32; Key statistics run down each channel,
 // Value statistics along each token's channel groups.

@@ -43,7 +43,8 @@ def test_status_strings_and_version():
 
 
 def _cfg(w, max_tokens=None, **kw):
-    c = kvq.make_config({"fp8": 1, "int8": 2, "kivi": 3, "bf16": 4}[w.fmt], w.bits, w.group, w.residual, w.batch,
+    c = kvq.make_config({"fp8": 1, "int8": 2, "kivi": 3, "bf16": 4, "int4": 5}[w.fmt], w.bits, w.group, w.residual,
+                        w.batch,
                         w.n_kv_heads, w.n_q_heads, w.head_dim, max_tokens or w.context + 64,
                         0 if w.dtype == "f32" else 1)
     for k, v in kw.items():
@@ -51,12 +52,16 @@ def _cfg(w, max_tokens=None, **kw):
     return c
 
 
-BF16_CACHE = {i: WORKLOADS[i].scaled(fmt="bf16", bits=16, group=0, residual=0) for i in (2, 3)}
+VARIANTS = {"bf16-2": WORKLOADS[2].scaled(fmt="bf16", bits=16, group=0, residual=0),
+            "bf16-3": WORKLOADS[3].scaled(fmt="bf16", bits=16, group=0, residual=0),
+            "int4-g32": WORKLOADS[3].scaled(fmt="int4", bits=4, group=32, residual=0),
+            "int4-g128": WORKLOADS[2].scaled(fmt="int4", bits=4, group=128, residual=0),
+            "int4-d64-g64": WORKLOADS[1].scaled(fmt="int4", bits=4, group=64, residual=0)}
 
 
-@pytest.mark.parametrize("idx", sorted(WORKLOADS) + ["bf16-2", "bf16-3"])
+@pytest.mark.parametrize("idx", sorted(WORKLOADS) + sorted(VARIANTS))
 def test_layout_matches_documented_formulas(idx):
-    w = BF16_CACHE[int(idx[5:])] if isinstance(idx, str) else WORKLOADS[idx]
+    w = VARIANTS[idx] if isinstance(idx, str) else WORKLOADS[idx]
     cfg = _cfg(w)
     lay = kvq.kvq_get_layout(cfg)
     pairs = w.batch * w.n_kv_heads
@@ -78,6 +83,10 @@ def test_layout_matches_documented_formulas(idx):
         order = [0, 1, 2, 4, 3, 5, 6, 7]     # k_scale, k_zero, v_scale, v_zero
         offs = [offs[i] for i in order]
         sizes = [sizes[i] for i in order]
+    elif w.fmt == "int4":
+        # nibble codes, one fp32 scale per token and channel group for Key and Value
+        assert lay.row_bytes == w.head_dim // 2 and lay.k_zero_off == 0 and lay.resid_slots == 0
+        sizes += [pairs * cap * (w.head_dim // w.group) * 4] * 2
     elif w.fmt == "bf16":
         # two bytes per element, no scale arrays
         assert lay.row_bytes == 2 * w.head_dim
@@ -111,6 +120,20 @@ def test_config_validation(field, value, status):
     setattr(cfg, field, value)
     out = kvq.KvqLayout()
     assert kvq.lib().kvq_get_layout(ctypes.byref(cfg), ctypes.byref(out)) == status
+
+
+def test_int4_groupwise_config_rules():
+    ok = _cfg(WORKLOADS[3], format=kvq.FMT_INT4, bits=4, group=64)
+    assert kvq.lib().kvq_get_layout(ctypes.byref(ok), ctypes.byref(kvq.KvqLayout())) == 0
+    for field, val, st in (("bits", 8, kvq.ERR_INVALID), ("residual", 16, kvq.ERR_INVALID),
+                           ("group", 0, kvq.ERR_INVALID), ("group", 48, kvq.ERR_INVALID),
+                           ("group", 16, kvq.ERR_UNSUPPORTED)):
+        bad = _cfg(WORKLOADS[3], format=kvq.FMT_INT4, bits=4, group=64)
+        setattr(bad, field, val)
+        assert kvq.lib().kvq_get_layout(ctypes.byref(bad), ctypes.byref(kvq.KvqLayout())) == st, (field, val)
+    # 128-channel groups do not divide head_dim 64
+    bad = _cfg(WORKLOADS[1], format=kvq.FMT_INT4, bits=4, group=128, residual=0)
+    assert kvq.lib().kvq_get_layout(ctypes.byref(bad), ctypes.byref(kvq.KvqLayout())) == kvq.ERR_INVALID
 
 
 def test_per_token_formats_reject_kivi_fields():

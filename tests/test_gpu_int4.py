@@ -1,0 +1,114 @@
+"""GPU parity of the group-wise symmetric INT4 cache (KVQ_FMT_INT4: per
+token, one fp32 scale per group of 32, 64 or 128 channels, Key and Value
+alike) against the CPU oracle: nibble codes and scales bit-exact, attention
+within the tolerance of the other formats, through ragged bulk appends,
+single-token appends that cross 8-token Value blocks, chunked appends and
+the fused decode step."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import quantized_kv_cache_06_amd as kvq
+import kvq_testlib as T
+from kvq_workloads import WORKLOADS, context_lengths, kv_tokens, queries
+from oracle import kvq_oracle as O
+from test_gpu_parity import _check_decode, _oracle_all
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _int4(w, group, **kw):
+    return w.scaled(fmt="int4", bits=4, group=group, residual=0, **kw)
+
+
+CASES = {
+    "g32-d128-bf16-ragged": _int4(WORKLOADS[3], 32, batch=3, n_kv_heads=2, n_q_heads=16, context=900, context_min=301),
+    "g64-d128-bf16": _int4(WORKLOADS[2], 64, batch=2, n_kv_heads=2, n_q_heads=8, context=777, context_min=777),
+    "g128-d128-bf16": _int4(WORKLOADS[4], 128, batch=2, n_kv_heads=2, n_q_heads=16, context=1000, context_min=1000),
+    "g32-d64-f32": _int4(WORKLOADS[1], 32, context=300, context_min=300),
+    "g64-d64-f32-gqa3": _int4(WORKLOADS[3], 64, batch=2, n_kv_heads=2, n_q_heads=6, head_dim=64, dtype="f32",
+                              context=333, context_min=333),
+}
+
+
+def _lens(w):
+    return context_lengths(w) if w.ragged else torch.full((w.batch,), w.context, dtype=torch.int32)
+
+
+def _check_cache(w, cache, seqs):
+    contents = T.CacheContents(cache)
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            T.assert_cache_matches(contents, b, h, seqs[b][h], w)
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_int4_append_decode_stream_and_fused(name):
+    w = CASES[name]
+    _log(f"[int4 {name}: G={w.group} d={w.head_dim} {w.dtype} B={w.batch} Hkv={w.n_kv_heads} Hq={w.n_q_heads} "
+         f"n<={w.context}]")
+    steps = 21
+    cache = T.GpuCache(T.config(w, w.context + 2 * steps + 8))
+    k, v = kv_tokens(w, w.context, device="cuda")
+    lens = _lens(w)
+    cache.append(k, v, lens if w.ragged else None)
+    torch.cuda.synchronize()
+    seqs = _oracle_all(w, k, v, lens)
+    _check_cache(w, cache, seqs)
+    _log("  bulk append: bit-exact")
+    q = queries(w, device="cuda")
+    sm = O.default_sm_scale(w.head_dim)
+    for st in (0, 64, 512):
+        _check_decode(w, cache, seqs, q, sm, st, f"split{st}")
+    kk, vv = kv_tokens(w, 2 * steps, stream=1, device="cuda")
+    kf, vf = T.as_f32(kk), T.as_f32(vv)
+    for s in range(steps):
+        cache.append(kk[:, :, s:s + 1], vv[:, :, s:s + 1])
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            seqs[b][h].append(kf[b, h, :steps], vf[b, h, :steps])
+    torch.cuda.synchronize()
+    _check_cache(w, cache, seqs)
+    _log(f"  {steps} single-token appends: bit-exact")
+    for s in range(steps, 2 * steps):
+        qs = queries(w, step=s, device="cuda")
+        out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+        kvq.kvq_append_decode(cache.cfg, cache.buf, cache.seq_lens, kk[:, :, s:s + 1].contiguous(),
+                              vv[:, :, s:s + 1].contiguous(), qs, float(sm), out, cache.ws)
+        out = out.cpu().numpy()
+        qf = T.as_f32(qs)
+        for b in range(w.batch):
+            for h in range(w.n_kv_heads):
+                seqs[b][h].append(kf[b, h, s:s + 1], vf[b, h, s:s + 1])
+            ref = O.decode_attention(seqs[b], qf[b], sm)
+            ma, rel = T.attention_errors(out[b], ref)
+            assert ma <= T.MAX_ABS_TOL and rel <= T.REL_L2_TOL, f"fused step {s} b={b}: {ma:.3g} {rel:.3g}"
+    torch.cuda.synchronize()
+    _check_cache(w, cache, seqs)
+    _log(f"  {steps} fused steps: bit-exact cache, attention in tolerance")
+
+
+def test_int4_chunked_append_equals_bulk():
+    """Chunk boundaries inside 8-token Value blocks: the packed words of a
+    block written by several calls equal the bulk append's."""
+    w = CASES["g64-d128-bf16"]
+    n = 300
+    cuts = [0, 1, 3, 8, 13, 16, 17, 40, 100, 101, 255, 299, n]
+    _log("[int4 chunked vs bulk]")
+    k, v = kv_tokens(w, n, device="cuda")
+    bulk = T.GpuCache(T.config(w, n + 8))
+    bulk.append(k, v)
+    chunked = T.GpuCache(T.config(w, n + 8))
+    for a, c in zip(cuts[:-1], cuts[1:]):
+        chunked.append(k[:, :, a:c], v[:, :, a:c])
+    torch.cuda.synchronize()
+    assert torch.equal(bulk.buf, chunked.buf)
+    seqs = _oracle_all(w, k, v, torch.full((w.batch,), n, dtype=torch.int32))
+    _check_cache(w, bulk, seqs)
