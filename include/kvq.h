@@ -181,7 +181,7 @@ int32_t kvq_get_layout(const kvq_config* cfg, kvq_layout* layout);
  *  t_new        tokens per sequence in k_new/v_new, >= 0 (0 is a no-op).
  *  append_lens  device int32 [B] or NULL: sequence b appends only its first
  *               append_lens[b] tokens (ragged batches); NULL = t_new for all.
- * FP8/INT8 quantize each token on arrival. KIVI writes new tokens to the
+ * FP8/INT8/INT4 quantize each token on arrival (BF16 rounds it). KIVI writes new tokens to the
  * residual ring and quantizes (and packs) every whole group of G tokens
  * that the flush rule admits, Key per channel and Value per token; a group
  * may mix older residual tokens with new ones. The result depends only on
