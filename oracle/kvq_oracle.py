@@ -204,6 +204,14 @@ def dequantize_int4_groupwise(codes, s, group: int):
     return np.asarray(codes, F64) * np.repeat(np.asarray(s, F64), group, axis=1)
 
 
+def quantize_fp8_static(x):
+    """Per-tensor FP8 without calibration [LLMS "1. FP8 KV Cache": scaling
+    strategies, per-tensor uncalibrated scale = 1.0]: code = E4M3(clamp(x,
+    -448, 448)); values beyond the E4M3 range saturate. No scale is stored."""
+    x = np.asarray(x, dtype=F32)
+    return e4m3_encode(np.clip(x, F32(-E4M3_MAX), F32(E4M3_MAX)))
+
+
 def dequantize_int8(codes, s):
     return np.asarray(codes, F64) * np.asarray(s, F64)[..., None]
 
@@ -310,7 +318,8 @@ def unpack_codes(packed, bits: int) -> np.ndarray:
 class SequenceCache:
     """State of one sequence's cache for one KV head.
 
-    fmt: "fp8", "int8", "kivi", "int4" (group-wise symmetric, ``group``
+    fmt: "fp8", "fp8s" (FP8 with the static scale 1.0), "int8", "kivi",
+    "int4" (group-wise symmetric, ``group``
     channels per scale, Key and Value alike) or "bf16" (the unquantized
     16-bit cache: codes are the bfloat16 patterns of the inputs, no scales). Inputs are
     float32 rows (bf16 inputs are widened exactly by the caller). For KIVI,
@@ -320,7 +329,7 @@ class SequenceCache:
 
     def __init__(self, fmt: str, head_dim: int, bits: int = 8, group: int = 0,
                  residual: int = 0):
-        if fmt not in ("fp8", "int8", "kivi", "int4", "bf16"):
+        if fmt not in ("fp8", "fp8s", "int8", "kivi", "int4", "bf16"):
             raise ValueError(fmt)
         self.fmt, self.d, self.bits, self.group, self.residual = fmt, head_dim, bits, group, residual
         self.n = 0
@@ -343,6 +352,9 @@ class SequenceCache:
                 q, s = quantize_int8_per_token(x)
                 codes.append(q)
                 scales.append(s)
+        elif self.fmt == "fp8s":
+            self.k_codes.append(quantize_fp8_static(k))
+            self.v_codes.append(quantize_fp8_static(v))
         elif self.fmt == "int4":
             for x, codes, scales in ((k, self.k_codes, self.k_scale), (v, self.v_codes, self.v_scale)):
                 q, s = quantize_int4_groupwise(x, self.group)
@@ -401,6 +413,9 @@ class SequenceCache:
                   for c, s, z in zip(self.v_codes, self.v_scale, self.v_zero)]
             ks.append(self.resid_k.astype(F64))
             vs.append(self.resid_v.astype(F64))
+        elif self.fmt == "fp8s":
+            ks = [e4m3_decode(c) for c in self.k_codes]
+            vs = [e4m3_decode(c) for c in self.v_codes]
         elif self.fmt == "int4":
             ks = [dequantize_int4_groupwise(c, s, self.group) for c, s in zip(self.k_codes, self.k_scale)]
             vs = [dequantize_int4_groupwise(c, s, self.group) for c, s in zip(self.v_codes, self.v_scale)]

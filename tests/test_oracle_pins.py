@@ -518,3 +518,25 @@ def test_int4_groupwise_round_trip_and_zero_groups():
     K, V = seq.dequantized()
     np.testing.assert_array_equal(K, deq)
     np.testing.assert_array_equal(V, O.dequantize_int4_groupwise(*O.quantize_int4_groupwise(-x, 32), 32))
+
+
+# --- static per-tensor FP8 (llms.blog "1. FP8 KV Cache": uncalibrated scale = 1.0) ---
+def test_fp8_static_scale_one_saturates_and_matches_torch():
+    """With scale 1.0 the code is E4M3 of the value itself: it equals torch's
+    float8_e4m3fn cast (a library routine) inside the range, and values
+    beyond +-448 saturate to the largest code instead of becoming NaN."""
+    rng = np.random.default_rng(21)
+    x = np.concatenate([rng.standard_normal(5000) * 50, rng.standard_normal(200) * 1e-3,
+                        [448.0, -448.0, 464.0 - 1e-3, 0.0]]).astype(F32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(O.quantize_fp8_static(x), ref)
+    big = np.array([465.0, 1e4, -1e6], F32)
+    np.testing.assert_array_equal(O.quantize_fp8_static(big), [0x7E, 0x7E, 0xFE])
+    assert np.all(O.e4m3_decode(O.quantize_fp8_static(big)) == [448.0, 448.0, -448.0])
+    # the sequence cache holds the codes and no scales
+    s = O.SequenceCache("fp8s", 4)
+    s.append(np.array([[1.0, 2.0, 3.0, 500.0]], F32), np.array([[0.5, -0.25, 0.0, 0.125]], F32))
+    K, V = s.dequantized()
+    np.testing.assert_array_equal(K, [[1.0, 2.0, 3.0, 448.0]])
+    np.testing.assert_array_equal(V, [[0.5, -0.25, 0.0, 0.125]])
+    assert s.k_scale == []
