@@ -82,7 +82,8 @@ typedef enum kvq_format {
   KVQ_FMT_INT8 = 2,        /* per-token symmetric INT8, fp32 scale per token */
   KVQ_FMT_KIVI = 3,        /* KIVI asymmetric INT4/INT2 + residual window    */
   KVQ_FMT_BF16 = 4,        /* unquantized bfloat16 cache (the 16-bit baseline) */
-  KVQ_FMT_INT4 = 5         /* group-wise symmetric INT4, per token, fp32 scale per group */
+  KVQ_FMT_INT4 = 5,        /* group-wise symmetric INT4, per token, fp32 scale per group */
+  KVQ_FMT_FP8_STATIC = 6   /* OCP FP8 E4M3 with the static per-tensor scale 1.0      */
 } kvq_format;
 
 typedef enum kvq_dtype {
@@ -99,6 +100,9 @@ typedef enum kvq_dtype {
  * alike, per token and per group of `group` consecutive channels, s = max|x|
  * / 7, code = clamp(rint(x / s), -8, 7) (within [-7, 7]), dequantized code *
  * s, stored as the nibble code + 8.
+ * KVQ_FMT_FP8_STATIC ([LLMS] "1. FP8 KV Cache", per-tensor uncalibrated
+ * scaling): bits 8, group and residual 0; code = E4M3_rne(clamp(x, -448,
+ * 448)), dequantized as the code's value; no scale arrays.
  * KVQ_FMT_BF16 is the unquantized 16-bit cache of [BEA] §1's table (2 bytes
  * per element): it stores each input rounded to bfloat16 (to nearest, ties
  * to even; bf16 inputs bit-unchanged) with no scales, and decodes through
@@ -141,7 +145,8 @@ typedef struct kvq_config {
  *           nibble first); v_codes as KIVI INT4 (TB = 8, 4-byte words);
  *           k_scale, v_scale [B][Hkv][cap][d/group] fp32.
  *  FP8/INT8: k_scale, v_scale [B][Hkv][cap] fp32; k_zero, v_zero unused (0).
- *  BF16:    no scale or zero-point arrays (offsets 0).
+ *  BF16, FP8_STATIC: no scale or zero-point arrays (offsets 0); FP8_STATIC
+ *           codes are laid out as FP8's.
  *  KIVI:    k_scale, k_zero [B][Hkv][cap/G][d] fp32 (per group, per channel);
  *           v_scale, v_zero [B][Hkv][cap][d/G] fp32 (per token, per channel
  *           group); k_resid, v_resid [B][Hkv][resid_slots][d] in in_dtype,
@@ -181,7 +186,7 @@ int32_t kvq_get_layout(const kvq_config* cfg, kvq_layout* layout);
  *  t_new        tokens per sequence in k_new/v_new, >= 0 (0 is a no-op).
  *  append_lens  device int32 [B] or NULL: sequence b appends only its first
  *               append_lens[b] tokens (ragged batches); NULL = t_new for all.
- * FP8/INT8/INT4 quantize each token on arrival (BF16 rounds it). KIVI writes new tokens to the
+ * FP8/INT8/INT4/FP8_STATIC quantize each token on arrival (BF16 rounds it). KIVI writes new tokens to the
  * residual ring and quantizes (and packs) every whole group of G tokens
  * that the flush rule admits, Key per channel and Value per token; a group
  * may mix older residual tokens with new ones. The result depends only on

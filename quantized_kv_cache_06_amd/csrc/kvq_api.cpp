@@ -29,6 +29,7 @@ int32_t validate(const kvq_config* c) {
   if (c->batch > 65535 || c->n_kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
   switch (c->format) {
     case KVQ_FMT_FP8_E4M3:
+    case KVQ_FMT_FP8_STATIC:
     case KVQ_FMT_INT8:
       if (c->bits != 8 || c->group != 0 || c->residual != 0) return KVQ_ERR_INVALID;
       break;
@@ -71,7 +72,7 @@ void make_layout(const kvq_config* c, kvq_layout* L) {
   };
   L->k_codes_off = region(pairs * cap * L->row_bytes);
   L->v_codes_off = region(pairs * cap * L->row_bytes);
-  if (c->format == KVQ_FMT_BF16) {
+  if (c->format == KVQ_FMT_BF16 || c->format == KVQ_FMT_FP8_STATIC) {
     // no scales: the codes are the values
   } else if (c->format == KVQ_FMT_INT4) {
     L->k_scale_off = region(pairs * cap * (D / c->group) * 4);
@@ -113,7 +114,7 @@ kvq::CacheView make_view(const kvq_config* c, const kvq_layout& L, const void* c
   v.row_bytes = L.row_bytes;
   v.k_codes = base + L.k_codes_off;
   v.v_codes = base + L.v_codes_off;
-  const bool scaled = c->format != KVQ_FMT_BF16;
+  const bool scaled = c->format != KVQ_FMT_BF16 && c->format != KVQ_FMT_FP8_STATIC;
   v.k_scale = scaled ? reinterpret_cast<float*>(base + L.k_scale_off) : nullptr;
   v.v_scale = scaled ? reinterpret_cast<float*>(base + L.v_scale_off) : nullptr;
   v.k_zero = kivi ? reinterpret_cast<float*>(base + L.k_zero_off) : nullptr;

@@ -258,6 +258,9 @@ hipError_t launch_append(const CacheView& cv, int32_t* seq_lens, const void* k_n
     if (cv.fmt == KVQ_FMT_FP8_E4M3) {
       if (cv.bf16) per_token_d<KVQ_FMT_FP8_E4M3, true>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
       else per_token_d<KVQ_FMT_FP8_E4M3, false>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
+    } else if (cv.fmt == KVQ_FMT_FP8_STATIC) {
+      if (cv.bf16) per_token_d<KVQ_FMT_FP8_STATIC, true>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
+      else per_token_d<KVQ_FMT_FP8_STATIC, false>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
     } else if (cv.fmt == KVQ_FMT_INT4) {
       if (cv.bf16) int4_dg<true>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
       else int4_dg<false>(cv, seq_lens, k_new, v_new, T, append_lens, stream);

@@ -213,7 +213,7 @@ __device__ __forceinline__ uint32_t i8x2_bf16(uint32_t w) {
 // Byte pair SEL of w (8-bit formats) to a bf16 pair, exact.
 template <int FMT, int SEL>
 __device__ __forceinline__ uint32_t byte_pair_bf16(uint32_t w) {
-  if constexpr (FMT == KVQ_FMT_FP8_E4M3) return fp8x2_bf16<SEL>(w);
+  if constexpr (FMT == KVQ_FMT_FP8_E4M3 || FMT == KVQ_FMT_FP8_STATIC) return fp8x2_bf16<SEL>(w);
   else return i8x2_bf16<SEL>(w);
 }
 
@@ -604,7 +604,7 @@ __device__ __forceinline__ void new_token_piece(const CacheView& cv, int b, int 
     } else if constexpr (FMT == KVQ_FMT_BF16) {
       c[0] = bf_lo(codes);
       c[1] = bf_hi(codes);
-    } else if constexpr (FMT == KVQ_FMT_FP8_E4M3) {
+    } else if constexpr (FMT == KVQ_FMT_FP8_E4M3 || FMT == KVQ_FMT_FP8_STATIC) {
       const uint32_t w = fp8x2_bf16<0>(codes);
       c[0] = bf_lo(w);
       c[1] = bf_hi(w);
@@ -655,7 +655,9 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   constexpr int KB = D * BITS / 8;            // bytes per Key row
   constexpr int LKB = CPL * BITS / 8;         // Key bytes per lane per token
   constexpr int VWB = BITS == 16 ? 16 : BITS == 8 ? 8 : 4;  // bytes per Value word (one channel, one block)
-  constexpr bool SCALED = FMT != KVQ_FMT_BF16;  // per-token scales (FP8/INT8) or KIVI metadata
+  // per-token scales (FP8/INT8), KIVI metadata or INT4 group scales; none for
+  // the bf16 cache and the static-scale FP8
+  constexpr bool SCALED = FMT != KVQ_FMT_BF16 && FMT != KVQ_FMT_FP8_STATIC;
   // group-wise INT4: per-token scales of each channel group for Key and Value
   constexpr bool INT4G = FMT == KVQ_FMT_INT4;
   constexpr int TB = BITS == 2 ? 16 : 8;      // tokens per Value block
@@ -1637,6 +1639,7 @@ void visit_fmt(const CacheView& cv, F&& f) {
     case KVQ_FMT_INT8: visit_d<KVQ_FMT_INT8, 8, BF16>(cv, f); break;
     case KVQ_FMT_BF16: visit_d<KVQ_FMT_BF16, 16, BF16>(cv, f); break;
     case KVQ_FMT_INT4: visit_d<KVQ_FMT_INT4, 4, BF16>(cv, f); break;
+    case KVQ_FMT_FP8_STATIC: visit_d<KVQ_FMT_FP8_STATIC, 8, BF16>(cv, f); break;
     default:
       if (cv.bits == 4) visit_d<KVQ_FMT_KIVI, 4, BF16>(cv, f);
       else visit_d<KVQ_FMT_KIVI, 2, BF16>(cv, f);

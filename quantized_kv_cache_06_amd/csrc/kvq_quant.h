@@ -49,6 +49,13 @@ __device__ __forceinline__ uint32_t quantize_token_lane(const float (&x)[CPL], f
     const uint32_t w = bf16_pair_rne(x[0], CPL == 2 ? x[CPL - 1] : 0.0f);
     return CPL == 2 ? w : (w & 0xffffu);
   }
+  if constexpr (FMT == KVQ_FMT_FP8_STATIC) {
+    // the static scale 1.0: E4M3 of the value, saturated to +-448
+    *scale = 1.0f;
+    const float y0 = fminf(fmaxf(x[0], -448.0f), 448.0f);
+    const float y1 = CPL == 2 ? fminf(fmaxf(x[CPL - 1], -448.0f), 448.0f) : 0.0f;
+    return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false)) & (CPL == 2 ? 0xffffu : 0xffu);
+  }
   float a = 0.0f;
 #pragma unroll
   for (int j = 0; j < CPL; ++j) a = fmaxf(a, fabsf(x[j]));
@@ -100,12 +107,12 @@ __device__ __forceinline__ void store_token_codes(const CacheView& cv, size_t pa
     uint8_t* dst = cv.k_codes + (pair * cv.cap + t) * D + lane * CPL;
     if constexpr (CPL == 2) *reinterpret_cast<uint16_t*>(dst) = uint16_t(codes);
     else *dst = uint8_t(codes);
-    if (lane == 0) cv.k_scale[pair * cv.cap + t] = s;
+    if (FMT != KVQ_FMT_FP8_STATIC && lane == 0) cv.k_scale[pair * cv.cap + t] = s;
   } else {
     uint8_t* blk = cv.v_codes + (pair * (cv.cap / 8) + t / 8) * (size_t(D) * 8) + (t & 7);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) blk[size_t(value_slot<2>(lane * CPL + j)) * 8] = uint8_t(codes >> (8 * j));
-    if (lane == 0) cv.v_scale[pair * cv.cap + t] = s;
+    if (FMT != KVQ_FMT_FP8_STATIC && lane == 0) cv.v_scale[pair * cv.cap + t] = s;
   }
 }
 

@@ -11,7 +11,7 @@ from kvq_workloads import Workload
 from oracle import kvq_oracle as O
 
 FMT = {"fp8": kvq.FMT_FP8_E4M3, "int8": kvq.FMT_INT8, "kivi": kvq.FMT_KIVI, "bf16": kvq.FMT_BF16,
-       "int4": kvq.FMT_INT4}
+       "int4": kvq.FMT_INT4, "fp8s": kvq.FMT_FP8_STATIC}
 
 
 def config(w: Workload, max_tokens: int, batch: int = None) -> kvq.KvqConfig:
@@ -214,7 +214,7 @@ def assert_cache_matches(contents: CacheContents, b: int, h: int, ref: O.Sequenc
         rk, rv = contents.residual(b, h, nq, n)
         np.testing.assert_array_equal(rk.view(np.uint32), ref.resid_k.view(np.uint32), err_msg="K residual")
         np.testing.assert_array_equal(rv.view(np.uint32), ref.resid_v.view(np.uint32), err_msg="V residual")
-    elif w.fmt == "bf16":
+    elif w.fmt in ("bf16", "fp8s"):
         pass  # no scales: the codes are the values
     elif w.fmt == "int4":
         ks, vs = contents.group_scales(b, h, nq)

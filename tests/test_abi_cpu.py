@@ -43,7 +43,8 @@ def test_status_strings_and_version():
 
 
 def _cfg(w, max_tokens=None, **kw):
-    c = kvq.make_config({"fp8": 1, "int8": 2, "kivi": 3, "bf16": 4, "int4": 5}[w.fmt], w.bits, w.group, w.residual,
+    c = kvq.make_config({"fp8": 1, "int8": 2, "kivi": 3, "bf16": 4, "int4": 5, "fp8s": 6}[w.fmt], w.bits, w.group,
+                        w.residual,
                         w.batch,
                         w.n_kv_heads, w.n_q_heads, w.head_dim, max_tokens or w.context + 64,
                         0 if w.dtype == "f32" else 1)
@@ -56,7 +57,8 @@ VARIANTS = {"bf16-2": WORKLOADS[2].scaled(fmt="bf16", bits=16, group=0, residual
             "bf16-3": WORKLOADS[3].scaled(fmt="bf16", bits=16, group=0, residual=0),
             "int4-g32": WORKLOADS[3].scaled(fmt="int4", bits=4, group=32, residual=0),
             "int4-g128": WORKLOADS[2].scaled(fmt="int4", bits=4, group=128, residual=0),
-            "int4-d64-g64": WORKLOADS[1].scaled(fmt="int4", bits=4, group=64, residual=0)}
+            "int4-d64-g64": WORKLOADS[1].scaled(fmt="int4", bits=4, group=64, residual=0),
+            "fp8s-2": WORKLOADS[2].scaled(fmt="fp8s")}
 
 
 @pytest.mark.parametrize("idx", sorted(WORKLOADS) + sorted(VARIANTS))
@@ -87,9 +89,9 @@ def test_layout_matches_documented_formulas(idx):
         # nibble codes, one fp32 scale per token and channel group for Key and Value
         assert lay.row_bytes == w.head_dim // 2 and lay.k_zero_off == 0 and lay.resid_slots == 0
         sizes += [pairs * cap * (w.head_dim // w.group) * 4] * 2
-    elif w.fmt == "bf16":
-        # two bytes per element, no scale arrays
-        assert lay.row_bytes == 2 * w.head_dim
+    elif w.fmt in ("bf16", "fp8s"):
+        # no scale arrays
+        assert lay.row_bytes == w.head_dim * w.bits // 8
         assert lay.k_scale_off == 0 and lay.v_scale_off == 0 and lay.k_zero_off == 0 and lay.resid_slots == 0
         offs, sizes = offs[:2], sizes[:2]
     else:
@@ -137,7 +139,7 @@ def test_int4_groupwise_config_rules():
 
 
 def test_per_token_formats_reject_kivi_fields():
-    for fmt, bits in ((kvq.FMT_FP8_E4M3, 8), (kvq.FMT_INT8, 8), (kvq.FMT_BF16, 16)):
+    for fmt, bits in ((kvq.FMT_FP8_E4M3, 8), (kvq.FMT_INT8, 8), (kvq.FMT_BF16, 16), (kvq.FMT_FP8_STATIC, 8)):
         cfg = _cfg(WORKLOADS[2], format=fmt, bits=bits)
         assert kvq.lib().kvq_get_layout(ctypes.byref(cfg), ctypes.byref(kvq.KvqLayout())) == 0
         for field, val in (("bits", 4), ("bits", 8 if bits == 16 else 16), ("group", 32), ("residual", 16)):
