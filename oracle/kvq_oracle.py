@@ -212,6 +212,45 @@ def quantize_fp8_static(x):
     return e4m3_encode(np.clip(x, F32(-E4M3_MAX), F32(E4M3_MAX)))
 
 
+# ---------------------------------------------------------------------------
+# Walsh-Hadamard rotation of the Keys  [LLMS "5. QuaRot and RotateKV:
+# Orthogonal Hadamard Dispersal": orthogonal Walsh-Hadamard rotations keep
+# inner products, spread outlier energy over all dimensions so that uniform
+# 4-bit codes suffice, and run online as fast transforms inside the kernels]
+# ---------------------------------------------------------------------------
+def fwht_f32(x) -> np.ndarray:
+    """Unnormalized fast Walsh-Hadamard transform along the last axis
+    (length a power of two) in float32: stages h = 1, 2, 4, ...; in each,
+    every pair (i, i + h) with bit h of i clear becomes (a + b, a - b). The
+    result is H x with H the Sylvester Hadamard matrix (entries +-1,
+    H H = d I). Each output of a stage is one float32 add or subtract of the
+    same two inputs, whatever the order the pairs are visited in."""
+    y = np.array(x, dtype=F32, copy=True)
+    d = y.shape[-1]
+    if d & (d - 1):
+        raise ValueError("length must be a power of two")
+    h = 1
+    while h < d:
+        z = y.reshape(*y.shape[:-1], d // (2 * h), 2, h)
+        a, b = z[..., 0, :].copy(), z[..., 1, :].copy()
+        z[..., 0, :] = a + b
+        z[..., 1, :] = a - b
+        y = z.reshape(*y.shape[:-1], d)
+        h *= 2
+    return y
+
+
+def hadamard_f64(d: int) -> np.ndarray:
+    """Sylvester Hadamard matrix H_d (+-1 entries), float64, by its closed
+    form: entry (i, j) is (-1)^(popcount(i & j))."""
+    i = np.arange(d)
+    bits = np.bitwise_and(i[:, None], i[None, :])
+    pop = np.zeros_like(bits)
+    for k in range(int(np.log2(d)) + 1):
+        pop += (bits >> k) & 1
+    return np.where(pop % 2 == 0, 1.0, -1.0)
+
+
 def dequantize_int8(codes, s):
     return np.asarray(codes, F64) * np.asarray(s, F64)[..., None]
 
@@ -319,6 +358,9 @@ class SequenceCache:
     """State of one sequence's cache for one KV head.
 
     fmt: "fp8", "fp8s" (FP8 with the static scale 1.0), "int8", "kivi",
+    "int4h" (int4 whose Keys are stored rotated: the float32 FWHT of each
+    Key row is what is quantized; dequantized() rotates them back, H x / d in
+    float64, so attention sees the original coordinates),
     "int4" (group-wise symmetric, ``group``
     channels per scale, Key and Value alike) or "bf16" (the unquantized
     16-bit cache: codes are the bfloat16 patterns of the inputs, no scales). Inputs are
@@ -329,7 +371,7 @@ class SequenceCache:
 
     def __init__(self, fmt: str, head_dim: int, bits: int = 8, group: int = 0,
                  residual: int = 0):
-        if fmt not in ("fp8", "fp8s", "int8", "kivi", "int4", "bf16"):
+        if fmt not in ("fp8", "fp8s", "int8", "kivi", "int4", "int4h", "bf16"):
             raise ValueError(fmt)
         self.fmt, self.d, self.bits, self.group, self.residual = fmt, head_dim, bits, group, residual
         self.n = 0
@@ -355,7 +397,9 @@ class SequenceCache:
         elif self.fmt == "fp8s":
             self.k_codes.append(quantize_fp8_static(k))
             self.v_codes.append(quantize_fp8_static(v))
-        elif self.fmt == "int4":
+        elif self.fmt in ("int4", "int4h"):
+            if self.fmt == "int4h":
+                k = fwht_f32(k)
             for x, codes, scales in ((k, self.k_codes, self.k_scale), (v, self.v_codes, self.v_scale)):
                 q, s = quantize_int4_groupwise(x, self.group)
                 codes.append(q)
@@ -416,8 +460,12 @@ class SequenceCache:
         elif self.fmt == "fp8s":
             ks = [e4m3_decode(c) for c in self.k_codes]
             vs = [e4m3_decode(c) for c in self.v_codes]
-        elif self.fmt == "int4":
+        elif self.fmt in ("int4", "int4h"):
             ks = [dequantize_int4_groupwise(c, s, self.group) for c, s in zip(self.k_codes, self.k_scale)]
+            if self.fmt == "int4h":
+                # back to the original coordinates: H (H k) = d k
+                H = hadamard_f64(d)
+                ks = [kr @ H / d for kr in ks]
             vs = [dequantize_int4_groupwise(c, s, self.group) for c, s in zip(self.v_codes, self.v_scale)]
         elif self.fmt == "bf16":
             ks = [bf16_value(c) for c in self.k_codes]

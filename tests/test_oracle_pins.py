@@ -540,3 +540,50 @@ def test_fp8_static_scale_one_saturates_and_matches_torch():
     np.testing.assert_array_equal(K, [[1.0, 2.0, 3.0, 448.0]])
     np.testing.assert_array_equal(V, [[0.5, -0.25, 0.0, 0.125]])
     assert s.k_scale == []
+
+
+# --- Walsh-Hadamard rotated Keys (llms.blog "5. QuaRot and RotateKV") ---------
+def test_fwht_equals_hadamard_matrix_and_is_exact_on_integers():
+    for d in (2, 8, 64, 128):
+        H = O.hadamard_f64(d)
+        np.testing.assert_array_equal(H @ H, d * np.eye(d))          # orthogonal up to d, symmetric
+        x = np.random.default_rng(d).integers(-50, 50, (7, d)).astype(F32)
+        # small integers: every butterfly is exact, so the transform equals the matrix product
+        np.testing.assert_array_equal(O.fwht_f32(x).astype(np.float64), x.astype(np.float64) @ H.T)
+        np.testing.assert_array_equal(O.fwht_f32(O.fwht_f32(x)), d * x)
+    # H_2 and H_4 written out
+    np.testing.assert_array_equal(O.hadamard_f64(2), [[1, 1], [1, -1]])
+    np.testing.assert_array_equal(O.hadamard_f64(4)[3], [1, -1, -1, 1])
+
+
+def test_fwht_float_rounding_and_inner_products():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((50, 128)).astype(F32)
+    y = O.fwht_f32(x).astype(np.float64)
+    ref = x.astype(np.float64) @ O.hadamard_f64(128).T
+    assert np.max(np.abs(y - ref)) <= 7 * 2.0 ** -23 * np.max(np.abs(ref)) * 8
+    # the rotation keeps inner products: (H q) . (H k) / d = q . k
+    q, k = rng.standard_normal(128), rng.standard_normal(128)
+    H = O.hadamard_f64(128)
+    assert abs((H @ q) @ (H @ k) / 128 - q @ k) < 1e-10
+
+
+def test_rotation_spreads_an_outlier_channel():
+    """The page: rotating spreads concentrated outlier energy over all
+    dimensions. A one-hot row becomes flat; Keys with one outlier channel
+    quantize per token to 4 bits with a smaller error after rotation."""
+    e = np.zeros(64, F32)
+    e[3] = 1.0
+    np.testing.assert_array_equal(np.abs(O.fwht_f32(e)), np.ones(64, F32))
+    rng = np.random.default_rng(8)
+    K = rng.standard_normal((256, 128)).astype(F32)
+    K[:, 5] *= 20
+    plain = O.SequenceCache("int4", 128, 4, 128)
+    rot = O.SequenceCache("int4h", 128, 4, 128)
+    for s in (plain, rot):
+        s.append(K, K)
+    err_plain = np.linalg.norm(plain.dequantized()[0] - K) / np.linalg.norm(K)
+    err_rot = np.linalg.norm(rot.dequantized()[0] - K) / np.linalg.norm(K)
+    assert err_rot < 0.6 * err_plain
+    # values are not rotated: both caches hold the same Value codes
+    np.testing.assert_array_equal(plain.value_codes(), rot.value_codes())
