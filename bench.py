@@ -45,10 +45,11 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--decode-rounds", type=int, default=20, help="passes over all copies in the decode-only timing")
-    p.add_argument("--cache-format", choices=("native", "bf16", "int4", "fp8s"), default="native",
+    p.add_argument("--cache-format", choices=("native", "bf16", "int4", "int4h", "fp8s"), default="native",
                    help="bf16: the same workload shapes and inputs with the unquantized 16-bit cache "
                         "(the baseline the quantized formats save bytes against); int4: with the "
-                        "group-wise symmetric INT4 cache (--group channels per scale); fp8s: FP8 with "
+                        "group-wise symmetric INT4 cache (--group channels per scale); int4h: the same "
+                        "with Walsh-Hadamard rotated Keys; fp8s: FP8 with "
                         "the static per-tensor scale 1.0")
     p.add_argument("--group", type=int, default=32, help="channels per scale of --cache-format int4")
     p.add_argument("--unfused", action="store_true",
@@ -64,7 +65,7 @@ def bytes_per_token_head(w):
     d = w.head_dim
     if w.fmt == "bf16":
         return 2 * d * 2
-    if w.fmt == "int4":
+    if w.fmt in ("int4", "int4h"):
         return 2 * d // 2 + 2 * 4 * (d // w.group)
     if w.fmt == "fp8s":
         return 2 * d
@@ -236,6 +237,8 @@ def main():
         w = w.scaled(fmt="bf16", bits=16, group=0, residual=0)
     elif args.cache_format == "int4":
         w = w.scaled(fmt="int4", bits=4, group=args.group, residual=0)
+    elif args.cache_format == "int4h":
+        w = w.scaled(fmt="int4h", bits=4, group=args.group, residual=0)
     elif args.cache_format == "fp8s":
         w = w.scaled(fmt="fp8s", bits=8, group=0, residual=0)
     dev = torch.device("cuda:0")
@@ -243,7 +246,7 @@ def main():
     n_max = int(lens0.max())
     grow = args.warmup + 2 * args.steps + 1  # warm-up steps, an untimed and a timed replay of the steps
     fmt = {"fp8": kvq.FMT_FP8_E4M3, "int8": kvq.FMT_INT8, "kivi": kvq.FMT_KIVI, "bf16": kvq.FMT_BF16,
-           "int4": kvq.FMT_INT4, "fp8s": kvq.FMT_FP8_STATIC}[w.fmt]
+           "int4": kvq.FMT_INT4, "fp8s": kvq.FMT_FP8_STATIC, "int4h": kvq.FMT_INT4_HADAMARD}[w.fmt]
     cfg = kvq.make_config(fmt, w.bits, w.group, w.residual, w.batch, w.n_kv_heads, w.n_q_heads, w.head_dim,
                           n_max + grow, kvq.DT_BF16 if w.dtype == "bf16" else kvq.DT_F32)
     lay = kvq.kvq_get_layout(cfg)
@@ -387,7 +390,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"fp8": "e4m3", "fp8s": "e4m3", "int8": "i8", "bf16": "bf16", "int4": "s4"}.get(w.fmt, f"u{w.bits}") +
+        "dtype": {"fp8": "e4m3", "fp8s": "e4m3", "int8": "i8", "bf16": "bf16", "int4": "s4",
+                  "int4h": "s4"}.get(w.fmt, f"u{w.bits}") +
                  " codes, bf16 MFMA (hi+lo), f32 accumulate",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "n_kv_heads": w.n_kv_heads, "n_q_heads": w.n_q_heads,

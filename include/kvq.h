@@ -83,7 +83,8 @@ typedef enum kvq_format {
   KVQ_FMT_KIVI = 3,        /* KIVI asymmetric INT4/INT2 + residual window    */
   KVQ_FMT_BF16 = 4,        /* unquantized bfloat16 cache (the 16-bit baseline) */
   KVQ_FMT_INT4 = 5,        /* group-wise symmetric INT4, per token, fp32 scale per group */
-  KVQ_FMT_FP8_STATIC = 6   /* OCP FP8 E4M3 with the static per-tensor scale 1.0      */
+  KVQ_FMT_FP8_STATIC = 6,  /* OCP FP8 E4M3 with the static per-tensor scale 1.0      */
+  KVQ_FMT_INT4_HADAMARD = 7 /* KVQ_FMT_INT4 with Walsh-Hadamard rotated Keys          */
 } kvq_format;
 
 typedef enum kvq_dtype {
@@ -100,6 +101,14 @@ typedef enum kvq_dtype {
  * alike, per token and per group of `group` consecutive channels, s = max|x|
  * / 7, code = clamp(rint(x / s), -8, 7) (within [-7, 7]), dequantized code *
  * s, stored as the nibble code + 8.
+ * KVQ_FMT_INT4_HADAMARD ([LLMS] "5. QuaRot and RotateKV: Orthogonal
+ * Hadamard Dispersal"): KVQ_FMT_INT4 whose Key rows are rotated before
+ * they are quantized, by the unnormalized fast Walsh-Hadamard transform over
+ * head_dim in fp32 (stages h = 1, 2, 4, ...: pairs (i, i + h) become
+ * (a + b, a - b)); decode rotates the query the same way and scales it by
+ * 1/head_dim, so scores are unchanged (H H = d I). The rotation spreads a
+ * Key outlier channel over all channels, so one group per token (group =
+ * head_dim) suffices. Values are not rotated. Same layout as KVQ_FMT_INT4.
  * KVQ_FMT_FP8_STATIC ([LLMS] "1. FP8 KV Cache", per-tensor uncalibrated
  * scaling): bits 8, group and residual 0; code = E4M3_rne(clamp(x, -448,
  * 448)), dequantized as the code's value; no scale arrays.
@@ -139,7 +148,7 @@ typedef struct kvq_config {
  *           channel 16*x + m of that chunk, so a 16-byte load at slot W*m
  *           returns channel m of W consecutive 16-channel tiles (W = 1, BF16:
  *           no permutation).
- *  INT4:    k_codes rows of d nibbles (code + 8) in chunks of 8 channels:
+ *  INT4, INT4_HADAMARD: k_codes rows of d nibbles (code + 8) in chunks of 8 channels:
  *           chunk (kk, r) = channels [32 kk + 8 r, 32 kk + 8 r + 8) sits at
  *           byte (d/8) r + 4 kk, channel 32 kk + 8 r + e in nibble e (low
  *           nibble first); v_codes as KIVI INT4 (TB = 8, 4-byte words);

@@ -37,6 +37,7 @@ int32_t validate(const kvq_config* c) {
       if (c->bits != 16 || c->group != 0 || c->residual != 0) return KVQ_ERR_INVALID;
       break;
     case KVQ_FMT_INT4:
+    case KVQ_FMT_INT4_HADAMARD:
       if (c->bits != 4 || c->residual != 0 || c->group <= 0) return KVQ_ERR_INVALID;
       if (c->head_dim % c->group != 0) return KVQ_ERR_INVALID;
       if (c->group != 32 && c->group != 64 && c->group != 128) return KVQ_ERR_UNSUPPORTED;
@@ -74,7 +75,7 @@ void make_layout(const kvq_config* c, kvq_layout* L) {
   L->v_codes_off = region(pairs * cap * L->row_bytes);
   if (c->format == KVQ_FMT_BF16 || c->format == KVQ_FMT_FP8_STATIC) {
     // no scales: the codes are the values
-  } else if (c->format == KVQ_FMT_INT4) {
+  } else if (c->format == KVQ_FMT_INT4 || c->format == KVQ_FMT_INT4_HADAMARD) {
     L->k_scale_off = region(pairs * cap * (D / c->group) * 4);
     L->v_scale_off = region(pairs * cap * (D / c->group) * 4);
   } else if (!kivi) {

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void append_per_token(CacheView cv, const
 // once, keeping the nibbles of tokens it does not own. Each block word has
 // one writer per call, so the read-modify-write is race-free.
 // ---------------------------------------------------------------------------
-template <int D, int G, bool BF16>
+template <int D, int G, bool BF16, bool ROT>
 __global__ __launch_bounds__(kThreads) void append_int4(CacheView cv, const int32_t* __restrict__ seq_lens,
                                                        const void* __restrict__ kin, const void* __restrict__ vin,
                                                        int T, const int32_t* __restrict__ append_lens) {
@@ -104,6 +104,7 @@ __global__ __launch_bounds__(kThreads) void append_int4(CacheView cv, const int3
       xk[j] = load_elem<BF16>(kin, in_base + j);
       xv[j] = load_elem<BF16>(vin, in_base + j);
     }
+    if constexpr (ROT) fwht_wave<CPL>(xk);  // Keys are stored rotated
     float sk, sv;
     const uint32_t uk = quantize_token_int4<G, CPL>(xk, &sk);
     const uint32_t uv = quantize_token_int4<G, CPL>(xv, &sv);
@@ -193,25 +194,25 @@ void launch_per_token(const CacheView& cv, int32_t* seq_lens, const void* k, con
   append_per_token<FMT, D, BF16><<<grid, kThreads, 0, st>>>(cv, seq_lens, k, v, T, al);
 }
 
-template <int D, int G, bool BF16>
+template <int D, int G, bool BF16, bool ROT>
 void launch_int4(const CacheView& cv, int32_t* seq_lens, const void* k, const void* v, int T, const int32_t* al,
                  hipStream_t st) {
   // blocks touched by T tokens starting anywhere: at most T / 8 + 2
   const int nblk = T / 8 + 2;
   const dim3 grid((nblk + kThreads / kWave - 1) / (kThreads / kWave), cv.Hkv, cv.B);
-  append_int4<D, G, BF16><<<grid, kThreads, 0, st>>>(cv, seq_lens, k, v, T, al);
+  append_int4<D, G, BF16, ROT><<<grid, kThreads, 0, st>>>(cv, seq_lens, k, v, T, al);
 }
 
-template <bool BF16>
+template <bool BF16, bool ROT>
 void int4_dg(const CacheView& cv, int32_t* sl, const void* k, const void* v, int T, const int32_t* al,
              hipStream_t st) {
   if (cv.D == 128) {
-    if (cv.G == 32) launch_int4<128, 32, BF16>(cv, sl, k, v, T, al, st);
-    else if (cv.G == 64) launch_int4<128, 64, BF16>(cv, sl, k, v, T, al, st);
-    else launch_int4<128, 128, BF16>(cv, sl, k, v, T, al, st);
+    if (cv.G == 32) launch_int4<128, 32, BF16, ROT>(cv, sl, k, v, T, al, st);
+    else if (cv.G == 64) launch_int4<128, 64, BF16, ROT>(cv, sl, k, v, T, al, st);
+    else launch_int4<128, 128, BF16, ROT>(cv, sl, k, v, T, al, st);
   } else {
-    if (cv.G == 32) launch_int4<64, 32, BF16>(cv, sl, k, v, T, al, st);
-    else launch_int4<64, 64, BF16>(cv, sl, k, v, T, al, st);
+    if (cv.G == 32) launch_int4<64, 32, BF16, ROT>(cv, sl, k, v, T, al, st);
+    else launch_int4<64, 64, BF16, ROT>(cv, sl, k, v, T, al, st);
   }
 }
 
@@ -262,8 +263,11 @@ hipError_t launch_append(const CacheView& cv, int32_t* seq_lens, const void* k_n
       if (cv.bf16) per_token_d<KVQ_FMT_FP8_STATIC, true>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
       else per_token_d<KVQ_FMT_FP8_STATIC, false>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
     } else if (cv.fmt == KVQ_FMT_INT4) {
-      if (cv.bf16) int4_dg<true>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
-      else int4_dg<false>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
+      if (cv.bf16) int4_dg<true, false>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
+      else int4_dg<false, false>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
+    } else if (cv.fmt == KVQ_FMT_INT4_HADAMARD) {
+      if (cv.bf16) int4_dg<true, true>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
+      else int4_dg<false, true>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
     } else if (cv.fmt == KVQ_FMT_BF16) {
       if (cv.bf16) per_token_d<KVQ_FMT_BF16, true>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
       else per_token_d<KVQ_FMT_BF16, false>(cv, seq_lens, k_new, v_new, T, append_lens, stream);

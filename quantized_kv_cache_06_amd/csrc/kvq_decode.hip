@@ -348,7 +348,7 @@ __device__ __forceinline__ constexpr int kfactor_log2(int kk, int i) {
 template <int FMT, int BITS>
 __device__ __forceinline__ u32x4 key_operand(const uint32_t* kw, int kk) {
   u32x4 a;
-  if constexpr (FMT == KVQ_FMT_INT4) {
+  if constexpr (FMT == KVQ_FMT_INT4 || FMT == KVQ_FMT_INT4_HADAMARD) {
     // group-wise INT4: chunk word kk holds the k-step's 8 nibbles (code + 8);
     // pair j = (nibble j, nibble j + 4) as bf16 128 + nibble, exact
     const uint32_t w = kw[kk];
@@ -570,16 +570,27 @@ __device__ __forceinline__ void new_token_piece(const CacheView& cv, int b, int 
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int g = cv.g;
   const size_t pair = pair_index(cv, b, h);
+  constexpr bool INT4G = FMT == KVQ_FMT_INT4 || FMT == KVQ_FMT_INT4_HADAMARD;
+  constexpr bool ROT = FMT == KVQ_FMT_INT4_HADAMARD;
   const int j = tid / 32, part = tid % 32;
   float qx[CPT];
-  load_elems<BF16, CPT>(q, (size_t(b) * cv.Hq + size_t(h) * g + min(j, g - 1)) * D + part * CPT, qx);
+  if constexpr (ROT) {
+    // the rotated query q' = H q / d that the workgroup staged in LDS
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) qx[k] = sm.q[j][part * CPT + k];
+  } else {
+    load_elems<BF16, CPT>(q, (size_t(b) * cv.Hq + size_t(h) * g + min(j, g - 1)) * D + part * CPT, qx);
+  }
   if (wave < 2) {
     float x[CPL];
 #pragma unroll
     for (int e = 0; e < CPL; ++e) x[e] = load_elem<BF16>(wave ? ap.v : ap.k, pair * D + lane * CPL + e);
+    if constexpr (ROT) {
+      if (wave == 0) fwht_wave<CPL>(x);  // Keys are stored rotated (wave-uniform branch)
+    }
     float sc;
     uint32_t codes;
-    if constexpr (FMT == KVQ_FMT_INT4) {
+    if constexpr (INT4G) {
       codes = quantize_token_int4<G, CPL>(x, &sc);
       if (wave == 0) {
         store_int4_key<G, CPL>(cv, pair, t, lane, codes, sc);
@@ -598,7 +609,7 @@ __device__ __forceinline__ void new_token_piece(const CacheView& cv, int b, int 
       store_token_codes<FMT, CPL>(cv, pair, t, wave == 1, lane, codes, sc);
     }
     float c[2];  // the codes as values, exactly
-    if constexpr (FMT == KVQ_FMT_INT4) {
+    if constexpr (INT4G) {
       c[0] = float(int(codes & 0xFu) - 8);
       c[1] = float(int((codes >> 4) & 0xFu) - 8);
     } else if constexpr (FMT == KVQ_FMT_BF16) {
@@ -659,7 +670,10 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   // the bf16 cache and the static-scale FP8
   constexpr bool SCALED = FMT != KVQ_FMT_BF16 && FMT != KVQ_FMT_FP8_STATIC;
   // group-wise INT4: per-token scales of each channel group for Key and Value
-  constexpr bool INT4G = FMT == KVQ_FMT_INT4;
+  // (ROT: the Keys are stored Walsh-Hadamard rotated, the query is rotated
+  // here the same way)
+  constexpr bool INT4G = FMT == KVQ_FMT_INT4 || FMT == KVQ_FMT_INT4_HADAMARD;
+  constexpr bool ROT = FMT == KVQ_FMT_INT4_HADAMARD;
   constexpr int TB = BITS == 2 ? 16 : 8;      // tokens per Value block
   constexpr int VW = 16 / VWB;                // Value words per 16-byte load
   constexpr int NVL = D / (16 * VW);          // 16-byte Value loads per lane per tile
@@ -836,6 +850,16 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   if constexpr (KIVI) {
     const int e0 = tid * EPT, j = e0 / D, c = e0 % D;
     load_elems<BF16, EPT>(q, (size_t(b) * cv.Hq + size_t(h) * g + min(j, g - 1)) * D + c, qx);
+  } else if constexpr (ROT) {
+    // whole query rows of heads wave and wave + 4, CPL channels per lane,
+    // rotated after the tiles' loads are issued
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int j = min(wave + 4 * u, g - 1);
+      const size_t at = (size_t(b) * cv.Hq + size_t(h) * g + j) * D + lane * (D / kWave);
+#pragma unroll
+      for (int e = 0; e < D / kWave; ++e) qx[u * (D / kWave) + e] = load_elem<BF16>(q, at + e);
+    }
   } else {
     const size_t qrow = (size_t(b) * cv.Hq + size_t(h) * g + min(hh, g - 1)) * D;
     if constexpr (BITS == 16 || INT4G) {
@@ -892,6 +916,26 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) qn[kw][e][h2] = __builtin_amdgcn_ldexpf(qn[kw][e][h2], eq);
   } else {
+    if constexpr (ROT) {
+      // q' = H q / d in LDS (H H = d I, so q' . (H k) = q . k); then the
+      // lane's k-step channels as for the unrotated format
+      constexpr int QPL = D / kWave;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float row[QPL];
+#pragma unroll
+        for (int e = 0; e < QPL; ++e) row[e] = qx[u * QPL + e];
+        fwht_wave<QPL>(row);
+        const int j = wave + 4 * u;
+#pragma unroll
+        for (int e = 0; e < QPL; ++e) sm.q[j][lane * QPL + e] = j < g ? row[e] * (1.0f / float(D)) : 0.0f;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qx[8 * kk + e] = sm.q[hh][32 * kk + 8 * r + e];
+    }
     // group-wise INT4: the Key codes enter as 128 + (code + 8), so 136 times
     // the query sum of each channel group comes off its dot product. The sum
     // is taken over the hi + lo values the matrix core multiplies (exact in
@@ -1612,7 +1656,7 @@ struct Variant {
 
 template <int FMT, int BITS, int D, bool BF16, class F>
 void visit_g(const CacheView& cv, F&& f) {
-  if constexpr (FMT == KVQ_FMT_INT4) {
+  if constexpr (FMT == KVQ_FMT_INT4 || FMT == KVQ_FMT_INT4_HADAMARD) {
     // groups divide head_dim: 128-channel groups exist only at d = 128
     if (cv.G == 32) f(Variant<FMT, BITS, D, 32, BF16>{});
     else if constexpr (D == 64) f(Variant<FMT, BITS, D, 64, BF16>{});
@@ -1640,6 +1684,7 @@ void visit_fmt(const CacheView& cv, F&& f) {
     case KVQ_FMT_BF16: visit_d<KVQ_FMT_BF16, 16, BF16>(cv, f); break;
     case KVQ_FMT_INT4: visit_d<KVQ_FMT_INT4, 4, BF16>(cv, f); break;
     case KVQ_FMT_FP8_STATIC: visit_d<KVQ_FMT_FP8_STATIC, 8, BF16>(cv, f); break;
+    case KVQ_FMT_INT4_HADAMARD: visit_d<KVQ_FMT_INT4_HADAMARD, 4, BF16>(cv, f); break;
     default:
       if (cv.bits == 4) visit_d<KVQ_FMT_KIVI, 4, BF16>(cv, f);
       else visit_d<KVQ_FMT_KIVI, 2, BF16>(cv, f);

@@ -146,6 +146,33 @@ __device__ __forceinline__ uint32_t quantize_token_int4(const float (&x)[CPL], f
   return u;
 }
 
+// Unnormalized fast Walsh-Hadamard transform of one row held by a wave
+// (channel lane * CPL + j in x[j]; d = 64 * CPL): stages h = 1, 2, 4, ...,
+// the pair (i, i + h) becoming (a + b, a - b). Each output is one fp32 add
+// or subtract of the same two inputs in any evaluation order, so the result
+// is reproducible bit for bit ("KV Cache Quantization in Production LLM
+// Serving", llms.blog, "5. QuaRot and RotateKV": online fast transforms).
+template <int CPL>
+__device__ __forceinline__ void fwht_wave(float (&x)[CPL]) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x % kWave;
+  if constexpr (CPL == 2) {
+    const float a = x[0], b = x[1];
+    x[0] = a + b;
+    x[1] = a - b;
+  }
+  // the remaining channel bits are the lane's bits 0..5
+#pragma unroll
+  for (int k = 0; k < 6; ++k) {
+    const int m = 1 << k;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const float y = __shfl_xor(x[j], m, kWave);
+      x[j] = (lane & m) ? y - x[j] : x[j] + y;
+    }
+  }
+}
+
 // Byte of a Key row (d nibbles) that holds channel c: rows are stored in
 // chunks of 8 channels, chunk (kk, r) = channels [32 kk + 8 r, 32 kk + 8 r + 8)
 // at byte (d / 8) r + 4 kk, channel 32 kk + 8 r + e in nibble e of the chunk.

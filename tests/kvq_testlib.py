@@ -11,7 +11,7 @@ from kvq_workloads import Workload
 from oracle import kvq_oracle as O
 
 FMT = {"fp8": kvq.FMT_FP8_E4M3, "int8": kvq.FMT_INT8, "kivi": kvq.FMT_KIVI, "bf16": kvq.FMT_BF16,
-       "int4": kvq.FMT_INT4, "fp8s": kvq.FMT_FP8_STATIC}
+       "int4": kvq.FMT_INT4, "fp8s": kvq.FMT_FP8_STATIC, "int4h": kvq.FMT_INT4_HADAMARD}
 
 
 def config(w: Workload, max_tokens: int, batch: int = None) -> kvq.KvqConfig:
@@ -193,7 +193,7 @@ def assert_cache_matches(contents: CacheContents, b: int, h: int, ref: O.Sequenc
     vc = contents.value_codes(b, h, nq)
     if w.fmt == "int8":
         kc, vc = kc.view(np.int8), vc.view(np.int8)
-    if w.fmt == "int4":
+    if w.fmt in ("int4", "int4h"):
         # nibbles hold code + 8; Key rows are stored chunk-permuted
         cap, rb = contents.lay.token_capacity, contents.lay.row_bytes
         rows = contents._per_pair(contents.lay.k_codes_off, (cap, rb), np.uint8, b, h)[:nq]
@@ -216,7 +216,7 @@ def assert_cache_matches(contents: CacheContents, b: int, h: int, ref: O.Sequenc
         np.testing.assert_array_equal(rv.view(np.uint32), ref.resid_v.view(np.uint32), err_msg="V residual")
     elif w.fmt in ("bf16", "fp8s"):
         pass  # no scales: the codes are the values
-    elif w.fmt == "int4":
+    elif w.fmt in ("int4", "int4h"):
         ks, vs = contents.group_scales(b, h, nq)
         if nq:
             np.testing.assert_array_equal(ks.view(np.uint32), np.concatenate(ref.k_scale).view(np.uint32))

@@ -43,7 +43,8 @@ def test_status_strings_and_version():
 
 
 def _cfg(w, max_tokens=None, **kw):
-    c = kvq.make_config({"fp8": 1, "int8": 2, "kivi": 3, "bf16": 4, "int4": 5, "fp8s": 6}[w.fmt], w.bits, w.group,
+    c = kvq.make_config({"fp8": 1, "int8": 2, "kivi": 3, "bf16": 4, "int4": 5, "fp8s": 6, "int4h": 7}[w.fmt], w.bits,
+                        w.group,
                         w.residual,
                         w.batch,
                         w.n_kv_heads, w.n_q_heads, w.head_dim, max_tokens or w.context + 64,
@@ -58,7 +59,8 @@ VARIANTS = {"bf16-2": WORKLOADS[2].scaled(fmt="bf16", bits=16, group=0, residual
             "int4-g32": WORKLOADS[3].scaled(fmt="int4", bits=4, group=32, residual=0),
             "int4-g128": WORKLOADS[2].scaled(fmt="int4", bits=4, group=128, residual=0),
             "int4-d64-g64": WORKLOADS[1].scaled(fmt="int4", bits=4, group=64, residual=0),
-            "fp8s-2": WORKLOADS[2].scaled(fmt="fp8s")}
+            "fp8s-2": WORKLOADS[2].scaled(fmt="fp8s"),
+            "int4h-g128": WORKLOADS[5].scaled(fmt="int4h", bits=4, group=128, residual=0)}
 
 
 @pytest.mark.parametrize("idx", sorted(WORKLOADS) + sorted(VARIANTS))
@@ -85,7 +87,7 @@ def test_layout_matches_documented_formulas(idx):
         order = [0, 1, 2, 4, 3, 5, 6, 7]     # k_scale, k_zero, v_scale, v_zero
         offs = [offs[i] for i in order]
         sizes = [sizes[i] for i in order]
-    elif w.fmt == "int4":
+    elif w.fmt in ("int4", "int4h"):
         # nibble codes, one fp32 scale per token and channel group for Key and Value
         assert lay.row_bytes == w.head_dim // 2 and lay.k_zero_off == 0 and lay.resid_slots == 0
         sizes += [pairs * cap * (w.head_dim // w.group) * 4] * 2

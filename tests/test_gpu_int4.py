@@ -24,8 +24,8 @@ def _log(msg):
     sys.stdout.flush()
 
 
-def _int4(w, group, **kw):
-    return w.scaled(fmt="int4", bits=4, group=group, residual=0, **kw)
+def _int4(w, group, fmt="int4", **kw):
+    return w.scaled(fmt=fmt, bits=4, group=group, residual=0, **kw)
 
 
 CASES = {
@@ -35,6 +35,12 @@ CASES = {
     "g32-d64-f32": _int4(WORKLOADS[1], 32, context=300, context_min=300),
     "g64-d64-f32-gqa3": _int4(WORKLOADS[3], 64, batch=2, n_kv_heads=2, n_q_heads=6, head_dim=64, dtype="f32",
                               context=333, context_min=333),
+    # Walsh-Hadamard rotated Keys (the query is rotated inside the kernel)
+    "hadamard-g128-d128-bf16": _int4(WORKLOADS[5], 128, fmt="int4h", batch=3, n_kv_heads=2, n_q_heads=16,
+                                     context=1100, context_min=500, layers=1),
+    "hadamard-g32-d128-bf16": _int4(WORKLOADS[2], 32, fmt="int4h", batch=2, n_kv_heads=2, n_q_heads=8, context=640,
+                                    context_min=640),
+    "hadamard-g64-d64-f32": _int4(WORKLOADS[1], 64, fmt="int4h", context=300, context_min=300),
 }
 
 
