@@ -283,6 +283,28 @@ def asym_quantize(x, bits: int, axis: int):
     return q.astype(np.uint8), s.astype(F32), z.astype(F32)
 
 
+def asym_quantize_f16meta(x, bits: int, axis: int):
+    """asym_quantize with half-precision metadata: s and z are computed as
+    there in float32, rounded to float16 (to nearest even), and the codes are
+    taken against the rounded values, clamp(round_half_even((x - z16) /
+    s16), 0, 2^b - 1) in float32 (code 0 where s16 == 0), so that
+    dequantization code * s16 + z16 uses exactly what is stored. Returns
+    (codes uint8, s16 float16, z16 float16)."""
+    x = np.asarray(x, dtype=F32)
+    levels = F32(2 ** bits - 1)
+    mn = np.min(x, axis=axis, keepdims=True)
+    mx = np.max(x, axis=axis, keepdims=True)
+    s16 = (((mx - mn) / levels) + F32(0.0)).astype(np.float16)
+    z16 = (mn + F32(0.0)).astype(np.float16) + np.float16(0.0)
+    s = s16.astype(F32)
+    z = z16.astype(F32)
+    pos = s > 0
+    div = np.where(pos, s, F32(1.0))
+    q = np.rint((x - z) / div)
+    q = np.where(pos, np.clip(q, F32(0.0), levels), F32(0.0))
+    return q.astype(np.uint8), s16, z16
+
+
 def kivi_quantize_key_group(k_group, bits: int):
     """Key: per-channel [BEA §3 "Key: Per-Channel Quantization"]. k_group is
     [G tokens, d]; statistics run over the G tokens of each channel.
@@ -358,6 +380,7 @@ class SequenceCache:
     """State of one sequence's cache for one KV head.
 
     fmt: "fp8", "fp8s" (FP8 with the static scale 1.0), "int8", "kivi",
+    "kivi16" (kivi with float16 scales and zero-points, asym_quantize_f16meta),
     "int4h" (int4 whose Keys are stored rotated: the float32 FWHT of each
     Key row is what is quantized; dequantized() rotates them back, H x / d in
     float64, so attention sees the original coordinates),
@@ -371,7 +394,7 @@ class SequenceCache:
 
     def __init__(self, fmt: str, head_dim: int, bits: int = 8, group: int = 0,
                  residual: int = 0):
-        if fmt not in ("fp8", "fp8s", "int8", "kivi", "int4", "int4h", "bf16"):
+        if fmt not in ("fp8", "fp8s", "int8", "kivi", "kivi16", "int4", "int4h", "bf16"):
             raise ValueError(fmt)
         self.fmt, self.d, self.bits, self.group, self.residual = fmt, head_dim, bits, group, residual
         self.n = 0
@@ -422,8 +445,14 @@ class SequenceCache:
             while self.resid_k.shape[0] - R >= G:
                 kg, self.resid_k = self.resid_k[:G], self.resid_k[G:]
                 vg, self.resid_v = self.resid_v[:G], self.resid_v[G:]
-                qk, sk, zk = kivi_quantize_key_group(kg, self.bits)
-                qv, sv, zv = kivi_quantize_value_tokens(vg, self.bits, G)
+                if self.fmt == "kivi16":
+                    qk, sk, zk = asym_quantize_f16meta(kg, self.bits, axis=0)
+                    qk, sk, zk = qk, sk[0], zk[0]
+                    qv3, sv, zv = asym_quantize_f16meta(vg.reshape(G, self.d // G, G), self.bits, axis=2)
+                    qv, sv, zv = qv3.reshape(G, self.d), sv[..., 0], zv[..., 0]
+                else:
+                    qk, sk, zk = kivi_quantize_key_group(kg, self.bits)
+                    qv, sv, zv = kivi_quantize_value_tokens(vg, self.bits, G)
                 self.k_codes.append(qk)
                 self.k_scale.append(sk)
                 self.k_zero.append(zk)
@@ -435,7 +464,7 @@ class SequenceCache:
     # -- views --------------------------------------------------------------
     @property
     def n_quantized(self) -> int:
-        if self.fmt == "kivi":
+        if self.fmt in ("kivi", "kivi16"):
             return len(self.k_codes) * self.group
         return self.n
 
@@ -451,7 +480,7 @@ class SequenceCache:
         """(K, V) as float64 [n, d]: quantized tokens first, then the residual
         window as stored."""
         d = self.d
-        if self.fmt == "kivi":
+        if self.fmt in ("kivi", "kivi16"):
             ks = [kivi_dequantize_keys(c, s, z) for c, s, z in zip(self.k_codes, self.k_scale, self.k_zero)]
             vs = [kivi_dequantize_values(c, s, z, self.group)
                   for c, s, z in zip(self.v_codes, self.v_scale, self.v_zero)]

@@ -587,3 +587,44 @@ def test_rotation_spreads_an_outlier_channel():
     assert err_rot < 0.6 * err_plain
     # values are not rotated: both caches hold the same Value codes
     np.testing.assert_array_equal(plain.value_codes(), rot.value_codes())
+
+
+# --- KIVI with half-precision scales and zero-points -------------------------
+def test_kivi_f16_metadata_page_example_and_rounding():
+    """The worked Key matrix (G = 3 tokens, INT4): channel 3's s = 0.1 is
+    stored as the float16 nearest to it (numpy's float16 cast, a library
+    routine), z = 7.5 is exact in float16, and the codes are taken against
+    the stored values: 8.0 -> 5, 9.0 -> 15, 7.5 -> 0."""
+    K = np.array(_golden("bea_kivi_examples.json")["key_matrix"], F32)
+    codes, s16, z16 = O.asym_quantize_f16meta(K, 4, axis=0)
+    assert s16.dtype == np.float16 and z16.dtype == np.float16
+    assert s16[0, 2] == np.float16(F32(1.5) / F32(15)) and float(s16[0, 2]) != 0.1
+    assert z16[0, 2] == np.float16(7.5)
+    assert list(codes[:, 2]) == [5, 15, 0]
+    # codes use the stored scale: a value exactly on the float16 grid round-trips
+    x = np.array([[0.0], [15 * float(np.float16(0.3))], [3 * float(np.float16(0.3))]], F32)
+    c, s, z = O.asym_quantize_f16meta(x, 4, axis=0)
+    assert s[0, 0] == np.float16(0.3) and z[0, 0] == 0 and list(c[:, 0]) == [0, 15, 3]
+
+
+def test_kivi_f16_metadata_round_trip_bound():
+    rng = np.random.default_rng(13)
+    for bits in (2, 4):
+        x = (rng.standard_normal((64, 128)) * 4).astype(F32)
+        c, s16, z16 = O.asym_quantize_f16meta(x, bits, axis=0)
+        s, z = s16.astype(np.float64), z16.astype(np.float64)
+        deq = c.astype(np.float64) * s + z
+        mn = x.min(axis=0, keepdims=True).astype(np.float64)
+        # within half a (stored) step, plus the zero-point's float16 rounding
+        # at the bottom of the range, plus the top code's reach
+        slack = np.abs(z - mn) + (2 ** bits - 1) * np.abs(s - (x.max(axis=0) - x.min(axis=0)) / (2 ** bits - 1))
+        assert np.all(np.abs(deq - x) <= s / 2 + slack + 1e-6 * np.abs(x))
+    # a sequence cache of this format flushes like plain KIVI, and its
+    # stored metadata are float16
+    seq = O.SequenceCache("kivi16", 64, 4, 32, 16)
+    k = rng.standard_normal((100, 64)).astype(F32)
+    seq.append(k[:50], k[:50])
+    seq.append(k[50:], k[50:])
+    assert seq.n_quantized == 64 and seq.k_scale[0].dtype == np.float16
+    K, _ = seq.dequantized()
+    np.testing.assert_array_equal(K[64:], k[64:].astype(np.float64))
