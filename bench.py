@@ -45,11 +45,12 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--decode-rounds", type=int, default=20, help="passes over all copies in the decode-only timing")
-    p.add_argument("--cache-format", choices=("native", "bf16", "int4", "int4h", "fp8s"), default="native",
+    p.add_argument("--cache-format", choices=("native", "bf16", "int4", "int4h", "fp8s", "kivi16"), default="native",
                    help="bf16: the same workload shapes and inputs with the unquantized 16-bit cache "
                         "(the baseline the quantized formats save bytes against); int4: with the "
                         "group-wise symmetric INT4 cache (--group channels per scale); int4h: the same "
-                        "with Walsh-Hadamard rotated Keys; fp8s: FP8 with "
+                        "with Walsh-Hadamard rotated Keys; kivi16: a KIVI workload with fp16 scales and "
+                        "zero-points; fp8s: FP8 with "
                         "the static per-tensor scale 1.0")
     p.add_argument("--group", type=int, default=32, help="channels per scale of --cache-format int4")
     p.add_argument("--unfused", action="store_true",
@@ -72,8 +73,9 @@ def bytes_per_token_head(w):
     if w.fmt in ("fp8", "int8"):
         return 2 * d + 2 * 4
     codes = 2 * d * w.bits // 8
-    key_meta = 2 * 4 * d / w.group        # per-channel scale + zero, amortized over G tokens
-    val_meta = 2 * 4 * (d // w.group)     # per-token scale + zero per channel group
+    mb = 2 if w.fmt == "kivi16" else 4    # bytes per scale or zero-point
+    key_meta = 2 * mb * d / w.group       # per-channel scale + zero, amortized over G tokens
+    val_meta = 2 * mb * (d // w.group)    # per-token scale + zero per channel group
     return codes + key_meta + val_meta
 
 
@@ -81,8 +83,12 @@ def resid_bytes_per_token_head(w):
     return 2 * w.head_dim * (2 if w.dtype == "bf16" else 4)
 
 
+def is_kivi(w):
+    return w.fmt in ("kivi", "kivi16")
+
+
 def nq_of(w, n):
-    if w.fmt != "kivi":
+    if not is_kivi(w):
         return n
     return w.group * (max(n - w.residual, 0) // w.group)
 
@@ -107,7 +113,7 @@ def append_bytes(w, lens_before, t):
     for n in lens_before:
         n = int(n)
         per_head = 2 * t * d * elem                       # read new K and V
-        if w.fmt != "kivi":
+        if not is_kivi(w):
             per_head += t * bytes_per_token_head(w)       # codes + scales written
         else:
             q0, q1 = nq_of(w, n), nq_of(w, n + t)
@@ -239,6 +245,10 @@ def main():
         w = w.scaled(fmt="int4", bits=4, group=args.group, residual=0)
     elif args.cache_format == "int4h":
         w = w.scaled(fmt="int4h", bits=4, group=args.group, residual=0)
+    elif args.cache_format == "kivi16":
+        if w.fmt != "kivi":
+            sys.exit("--cache-format kivi16 needs a KIVI workload (4 or 5)")
+        w = w.scaled(fmt="kivi16")
     elif args.cache_format == "fp8s":
         w = w.scaled(fmt="fp8s", bits=8, group=0, residual=0)
     dev = torch.device("cuda:0")
@@ -246,7 +256,8 @@ def main():
     n_max = int(lens0.max())
     grow = args.warmup + 2 * args.steps + 1  # warm-up steps, an untimed and a timed replay of the steps
     fmt = {"fp8": kvq.FMT_FP8_E4M3, "int8": kvq.FMT_INT8, "kivi": kvq.FMT_KIVI, "bf16": kvq.FMT_BF16,
-           "int4": kvq.FMT_INT4, "fp8s": kvq.FMT_FP8_STATIC, "int4h": kvq.FMT_INT4_HADAMARD}[w.fmt]
+           "int4": kvq.FMT_INT4, "fp8s": kvq.FMT_FP8_STATIC, "int4h": kvq.FMT_INT4_HADAMARD,
+           "kivi16": kvq.FMT_KIVI_F16}[w.fmt]
     cfg = kvq.make_config(fmt, w.bits, w.group, w.residual, w.batch, w.n_kv_heads, w.n_q_heads, w.head_dim,
                           n_max + grow, kvq.DT_BF16 if w.dtype == "bf16" else kvq.DT_F32)
     lay = kvq.kvq_get_layout(cfg)

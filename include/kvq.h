@@ -84,7 +84,8 @@ typedef enum kvq_format {
   KVQ_FMT_BF16 = 4,        /* unquantized bfloat16 cache (the 16-bit baseline) */
   KVQ_FMT_INT4 = 5,        /* group-wise symmetric INT4, per token, fp32 scale per group */
   KVQ_FMT_FP8_STATIC = 6,  /* OCP FP8 E4M3 with the static per-tensor scale 1.0      */
-  KVQ_FMT_INT4_HADAMARD = 7 /* KVQ_FMT_INT4 with Walsh-Hadamard rotated Keys          */
+  KVQ_FMT_INT4_HADAMARD = 7, /* KVQ_FMT_INT4 with Walsh-Hadamard rotated Keys         */
+  KVQ_FMT_KIVI_F16 = 8     /* KIVI with fp16 scales and zero-points             */
 } kvq_format;
 
 typedef enum kvq_dtype {
@@ -101,6 +102,13 @@ typedef enum kvq_dtype {
  * alike, per token and per group of `group` consecutive channels, s = max|x|
  * / 7, code = clamp(rint(x / s), -8, 7) (within [-7, 7]), dequantized code *
  * s, stored as the nibble code + 8.
+ * KVQ_FMT_KIVI_F16: KIVI (same bits, group, residual and layout) with its
+ * scales and zero-points stored as IEEE binary16: s and z are computed in
+ * fp32 as for KIVI, rounded to the nearest binary16 (ties to even), and the
+ * codes are taken against the stored values, clamp(rint((x - z16) / s16),
+ * 0, 2^bits - 1); dequantized code * s16 + z16. Half the metadata bytes;
+ * the values' scales and minima must be within binary16 range (|.| <
+ * 65504; a scale below 2^-24 stores 0 and gives code 0).
  * KVQ_FMT_INT4_HADAMARD ([LLMS] "5. QuaRot and RotateKV: Orthogonal
  * Hadamard Dispersal"): KVQ_FMT_INT4 whose Key rows are rotated before
  * they are quantized, by the unnormalized fast Walsh-Hadamard transform over
@@ -156,7 +164,8 @@ typedef struct kvq_config {
  *  FP8/INT8: k_scale, v_scale [B][Hkv][cap] fp32; k_zero, v_zero unused (0).
  *  BF16, FP8_STATIC: no scale or zero-point arrays (offsets 0); FP8_STATIC
  *           codes are laid out as FP8's.
- *  KIVI:    k_scale, k_zero [B][Hkv][cap/G][d] fp32 (per group, per channel);
+ *  KIVI:    k_scale, k_zero [B][Hkv][cap/G][d] fp32 (per group, per channel;
+ *           KIVI_F16: binary16, here and in v_scale, v_zero);
  *           v_scale, v_zero [B][Hkv][cap][d/G] fp32 (per token, per channel
  *           group); k_resid, v_resid [B][Hkv][resid_slots][d] in in_dtype,
  *           token t of a sequence in slot t % resid_slots.

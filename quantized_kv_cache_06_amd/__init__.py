@@ -13,7 +13,7 @@ import os
 from typing import Optional
 
 __all__ = [
-    "FMT_FP8_E4M3", "FMT_INT8", "FMT_KIVI", "FMT_BF16", "FMT_INT4", "FMT_FP8_STATIC", "FMT_INT4_HADAMARD", "DT_F32",
+    "FMT_FP8_E4M3", "FMT_INT8", "FMT_KIVI", "FMT_BF16", "FMT_INT4", "FMT_FP8_STATIC", "FMT_INT4_HADAMARD", "FMT_KIVI_F16", "DT_F32",
     "DT_BF16",
     "KvqConfig", "KvqLayout", "KvqError", "LIB_PATH", "lib", "make_config",
     "kvq_status_string", "kvq_version", "kvq_get_layout", "kvq_quantize_append",
@@ -23,7 +23,7 @@ __all__ = [
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvq.so")
 
-FMT_FP8_E4M3, FMT_INT8, FMT_KIVI, FMT_BF16, FMT_INT4, FMT_FP8_STATIC, FMT_INT4_HADAMARD = 1, 2, 3, 4, 5, 6, 7
+FMT_FP8_E4M3, FMT_INT8, FMT_KIVI, FMT_BF16, FMT_INT4, FMT_FP8_STATIC, FMT_INT4_HADAMARD, FMT_KIVI_F16 = range(1, 9)
 DT_F32, DT_BF16 = 0, 1
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 

@@ -43,6 +43,7 @@ int32_t validate(const kvq_config* c) {
       if (c->group != 32 && c->group != 64 && c->group != 128) return KVQ_ERR_UNSUPPORTED;
       break;
     case KVQ_FMT_KIVI:
+    case KVQ_FMT_KIVI_F16:
       if (c->bits != 4 && c->bits != 2) return KVQ_ERR_INVALID;
       if (c->group <= 0 || c->residual < 0) return KVQ_ERR_INVALID;
       if (c->head_dim % c->group != 0) return KVQ_ERR_INVALID;
@@ -57,7 +58,8 @@ int32_t validate(const kvq_config* c) {
 
 void make_layout(const kvq_config* c, kvq_layout* L) {
   memset(L, 0, sizeof(*L));
-  const bool kivi = c->format == KVQ_FMT_KIVI;
+  const bool kivi = c->format == KVQ_FMT_KIVI || c->format == KVQ_FMT_KIVI_F16;
+  const uint64_t meta = c->format == KVQ_FMT_KIVI_F16 ? 2 : 4;  // bytes per scale or zero-point
   const uint64_t pairs = uint64_t(c->batch) * c->n_kv_heads;
   const int D = c->head_dim;
   const int unit = kivi ? c->group : 32;
@@ -84,10 +86,10 @@ void make_layout(const kvq_config* c, kvq_layout* L) {
   } else {
     const uint64_t groups = cap / c->group;
     const uint64_t vgroups = D / c->group;
-    L->k_scale_off = region(pairs * groups * D * 4);
-    L->k_zero_off = region(pairs * groups * D * 4);
-    L->v_scale_off = region(pairs * cap * vgroups * 4);
-    L->v_zero_off = region(pairs * cap * vgroups * 4);
+    L->k_scale_off = region(pairs * groups * D * meta);
+    L->k_zero_off = region(pairs * groups * D * meta);
+    L->v_scale_off = region(pairs * cap * vgroups * meta);
+    L->v_zero_off = region(pairs * cap * vgroups * meta);
     L->resid_slots = c->residual + c->group;
     L->k_resid_off = region(pairs * L->resid_slots * D * L->elem_bytes);
     L->v_resid_off = region(pairs * L->resid_slots * D * L->elem_bytes);
@@ -98,7 +100,7 @@ void make_layout(const kvq_config* c, kvq_layout* L) {
 kvq::CacheView make_view(const kvq_config* c, const kvq_layout& L, const void* cache) {
   kvq::CacheView v;
   uint8_t* base = static_cast<uint8_t*>(const_cast<void*>(cache));
-  const bool kivi = c->format == KVQ_FMT_KIVI;
+  const bool kivi = c->format == KVQ_FMT_KIVI || c->format == KVQ_FMT_KIVI_F16;
   v.fmt = c->format;
   v.bits = c->bits;
   v.G = c->group;
@@ -149,7 +151,8 @@ int auto_split_bound(const kvq_config* c) {
 // epilogue) share a compute unit.
 int auto_split(const kvq_config* c, int64_t resident, int64_t cus) {
   const int64_t pairs = int64_t(c->batch) * c->n_kv_heads;
-  int64_t n = c->format == KVQ_FMT_KIVI ? 4 * resident / pairs : 2 * cus / pairs;
+  const bool kivi = c->format == KVQ_FMT_KIVI || c->format == KVQ_FMT_KIVI_F16;
+  int64_t n = kivi ? 4 * resident / pairs : 2 * cus / pairs;
   const int bound = auto_split_bound(c);
   if (n < 1) n = 1;
   if (n > bound) n = bound;

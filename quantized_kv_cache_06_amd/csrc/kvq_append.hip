@@ -129,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void append_int4(CacheView cv, const int3
 // steps (staging, Key half, Value half) are shared with the fused append +
 // decode kernel.
 // ---------------------------------------------------------------------------
-template <int BITS, int G, int D, bool BF16>
+template <int BITS, int G, int D, bool BF16, bool M16>
 __global__ __launch_bounds__(kThreads) void kivi_flush(CacheView cv, const int32_t* __restrict__ seq_lens,
                                                       const void* __restrict__ kin, const void* __restrict__ vin,
                                                       int T, const int32_t* __restrict__ append_lens) {
@@ -145,9 +145,9 @@ __global__ __launch_bounds__(kThreads) void kivi_flush(CacheView cv, const int32
   __shared__ FlushSmem<G, D> f;
   const size_t pair = pair_index(cv, b, h);
   flush_stage<BF16, G, D>(f, cv, pair, grp, n, kin, T, cv.k_resid);
-  flush_key<BITS, G, D>(f, cv, pair, grp);
+  flush_key<BITS, G, D, M16>(f, cv, pair, grp);
   flush_stage<BF16, G, D>(f, cv, pair, grp, n, vin, T, cv.v_resid);
-  flush_value<BITS, G, D>(f, cv, pair, grp);
+  flush_value<BITS, G, D, M16>(f, cv, pair, grp);
 }
 
 // ---------------------------------------------------------------------------
@@ -220,7 +220,10 @@ template <int BITS, int G, int D, bool BF16>
 void launch_flush(const CacheView& cv, int32_t* seq_lens, const void* k, const void* v, int T,
                   const int32_t* al, hipStream_t st) {
   const dim3 grid(T / G + 1, cv.Hkv, cv.B);
-  kivi_flush<BITS, G, D, BF16><<<grid, kThreads, 0, st>>>(cv, seq_lens, k, v, T, al);
+  if (cv.fmt == KVQ_FMT_KIVI_F16)
+    kivi_flush<BITS, G, D, BF16, true><<<grid, kThreads, 0, st>>>(cv, seq_lens, k, v, T, al);
+  else
+    kivi_flush<BITS, G, D, BF16, false><<<grid, kThreads, 0, st>>>(cv, seq_lens, k, v, T, al);
 }
 
 template <int FMT, bool BF16>
@@ -246,7 +249,7 @@ void flush_gd(const CacheView& cv, int32_t* sl, const void* k, const void* v, in
 
 hipError_t launch_append(const CacheView& cv, int32_t* seq_lens, const void* k_new, const void* v_new, int T,
                          const int32_t* append_lens, hipStream_t stream) {
-  if (cv.fmt == KVQ_FMT_KIVI) {
+  if (cv.fmt == KVQ_FMT_KIVI || cv.fmt == KVQ_FMT_KIVI_F16) {
     if (cv.bits == 4) {
       if (cv.bf16) flush_gd<4, true>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
       else flush_gd<4, false>(cv, seq_lens, k_new, v_new, T, append_lens, stream);

@@ -640,6 +640,14 @@ __device__ __forceinline__ void new_token_piece(const CacheView& cv, int b, int 
   }
 }
 
+// Element j of binary16 values packed two per 32-bit register, widened
+// exactly.
+template <int N>
+__device__ __forceinline__ float half_at(const uint32_t (&w)[N], int j) {
+  const uint32_t bits = w[j / 2];
+  return float(__builtin_bit_cast(_Float16, uint16_t((j & 1) ? bits >> 16 : bits)));
+}
+
 // ---------------------------------------------------------------------------
 // Quantized tokens [t0, t1) of one split: 4 waves on the matrix cores.
 // Every global load of a tile (codes, scales, zero-points, and the Key
@@ -654,7 +662,10 @@ template <int FMT, int BITS, int D, int G, bool BF16, bool FUSED>
 __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int h, int s, int t0, int t1,
                                                 const void* __restrict__ q, float sm_log2, const DecodeWork& wk,
                                                 SmemQuant<D>& sm, int t_new, const AppendIn& ap) {
-  constexpr bool KIVI = FMT == KVQ_FMT_KIVI;
+  constexpr bool KIVI = FMT == KVQ_FMT_KIVI || FMT == KVQ_FMT_KIVI_F16;
+  // KIVI with binary16 metadata: the raw halves ride in the ring (two per
+  // register) and are widened when the tile is processed
+  constexpr bool M16 = FMT == KVQ_FMT_KIVI_F16;
   constexpr int CPL = D / 4;                  // channels per row group (score MFMA)
   // 8-bit codes at d = 128: row group r holds channels [16r, 16r+16) and
   // [64+16r, 64+16r+16), so each Key load instruction covers 64 contiguous
@@ -762,6 +773,8 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   struct Slot {
     uint32_t kw[2][LKB / 4], vw[NVL * 4];
     float mw[NVG], gw[KGL];
+    // binary16 metadata (M16): raw halves, two per register
+    uint32_t mh[(NVG + 1) / 2], gh[KGL / 2];
   };
   Slot ring[NPF];
   // Loads are issued unconditionally (a tile index past the wave's run is
@@ -814,6 +827,29 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
     } else if constexpr (!KIVI) {
       sl.mw[0] = load_vec<float, kMetaNT>(
           reinterpret_cast<const uint8_t*>((part ? cv.v_scale : cv.k_scale) + (pair * cv.cap + T0 + qi)));
+    } else if constexpr (M16) {
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(part ? cv.v_zero : cv.v_scale) +
+                           (pair * cv.cap + T0 + qi) * NVG * 2;
+      if constexpr (NVG == 4) {
+        const u32x2 x = load_vec<u32x2, kMetaNT>(src);
+        sl.mh[0] = x[0];
+        sl.mh[1] = x[1];
+      } else if constexpr (NVG == 2) {
+        sl.mh[0] = load_vec<uint32_t, kMetaNT>(src);
+      } else {
+        sl.mh[0] = uint32_t(*reinterpret_cast<const uint16_t*>(src));
+      }
+      if constexpr (kGroupLoad) {
+        const uint8_t* gsrc = reinterpret_cast<const uint8_t*>(part ? cv.k_zero : cv.k_scale) +
+                              ((pair * (cv.cap / GG) + T0 / GG) * D + qi * KGL) * 2;
+        if constexpr (KGL == 4) {
+          const u32x2 x = *reinterpret_cast<const u32x2*>(gsrc);
+          sl.gh[0] = x[0];
+          sl.gh[1] = x[1];
+        } else {
+          sl.gh[0] = *reinterpret_cast<const uint32_t*>(gsrc);
+        }
+      }
     } else {
       const float* src = (part ? cv.v_zero : cv.v_scale) + (pair * cv.cap + T0 + qi) * NVG;
       if constexpr (NVG == 4) {
@@ -970,7 +1006,10 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
     {
       const int part = lane >> 5, qi = lane & 31;
       float* mdst = (part ? meta1 : meta0) + qi * NVG;
-      if constexpr (SCALED) {
+      if constexpr (M16) {
+#pragma unroll
+        for (int j = 0; j < NVG; ++j) mdst[j] = half_at(sl.mh, j);
+      } else if constexpr (SCALED) {
 #pragma unroll
         for (int j = 0; j < NVG; ++j) mdst[j] = sl.mw[j];
       }
@@ -978,16 +1017,22 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
         if (grp_open) {
           // Key scales (lanes 0-31; >= 0) scaled by 2^kes so that the
           // group's largest lies in [64, 128); zero-points as they are
+          float gv[KGL];
+#pragma unroll
+          for (int j = 0; j < KGL; ++j) {
+            if constexpr (M16) gv[j] = half_at(sl.gh, j);
+            else gv[j] = sl.gw[j];
+          }
           float ms = 0.0f;
 #pragma unroll
-          for (int j = 0; j < KGL; ++j) ms = fmaxf(ms, sl.gw[j]);
+          for (int j = 0; j < KGL; ++j) ms = fmaxf(ms, gv[j]);
 #pragma unroll
           for (int o = 1; o < 32; o <<= 1) ms = fmaxf(ms, __shfl_xor(ms, o, kWave));
           ms = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, ms)));
           kes = ms > 0.0f ? 7 - __builtin_amdgcn_frexp_expf(ms) : 0;
           float* gdst = sm.kgrp[wave][part] + qi * KGL;
 #pragma unroll
-          for (int j = 0; j < KGL; ++j) gdst[j] = part ? sl.gw[j] : __builtin_amdgcn_ldexpf(sl.gw[j], kes);
+          for (int j = 0; j < KGL; ++j) gdst[j] = part ? gv[j] : __builtin_amdgcn_ldexpf(gv[j], kes);
         }
       }
     }
@@ -1280,7 +1325,7 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
 // own steps, and attention reads it as the dequantized codes, code * s + z,
 // exactly as an attention call after the append would.
 // ---------------------------------------------------------------------------
-template <int D, bool BF16, int BITS, int G, bool FUSED>
+template <int D, bool BF16, int BITS, int G, bool FUSED, bool M16>
 __device__ __forceinline__ void split_residual(const CacheView& cv, int b, int h, int s, int nq, int n,
                                                const void* __restrict__ q, float sm_log2, const DecodeWork& wk,
                                                SmemResidT<D, G, FUSED>& sm, const AppendIn& ap, bool app) {
@@ -1388,7 +1433,7 @@ __device__ __forceinline__ void split_residual(const CacheView& cv, int b, int h
         const int grp = nq / G;
         FlushSmem<G, D>& f = sm.f;
         flush_stage<BF16, G, D>(f, cv, pair, grp, t_new, ap.k, 1, cv.k_resid);
-        flush_key<BITS, G, D>(f, cv, pair, grp);
+        flush_key<BITS, G, D, M16>(f, cv, pair, grp);
         // the staged tile becomes the dequantized Key rows, code * s + z
         for (int e = tid; e < G * D; e += kThreads) {
           const int i = e / D, c = e % D;
@@ -1407,7 +1452,7 @@ __device__ __forceinline__ void split_residual(const CacheView& cv, int b, int h
         put_scores(sco, G);
         softmax_step(G);
         flush_stage<BF16, G, D>(f, cv, pair, grp, t_new, ap.v, 1, cv.v_resid);
-        flush_value<BITS, G, D>(f, cv, pair, grp);
+        flush_value<BITS, G, D, M16>(f, cv, pair, grp);
         for (int e = tid; e < G * D; e += kThreads) {
           const int i = e / D, c = e % D;
           const float sv = f.sv[i][c / G], zv = f.zv[i][c / G];
@@ -1486,18 +1531,23 @@ __device__ __forceinline__ void split_residual(const CacheView& cv, int b, int h
 // Three resident workgroups per compute unit (12 waves, at most 168
 // registers per lane) measure fastest: more loads in flight per unit. KIVI
 // INT4 with groups of 32 at d = 128 needs a few more registers and keeps two.
-template <int FMT, int BITS, int D, int G>
+template <int FMT, int BITS, int D, int G, bool FUSED>
 constexpr int min_wg_per_cu() {
   if constexpr (KVQ_DECODE_MIN_WG_PER_CU > 0) return KVQ_DECODE_MIN_WG_PER_CU;
+  // INT2 KIVI with binary16 metadata at G = 32, d = 128 (a Key fold every
+  // tile plus the half widening; the fused step also the flush path) needs
+  // a few registers more than three workgroups per unit leave
+  if constexpr (FMT == KVQ_FMT_KIVI_F16 && BITS == 2 && D == 128 && G == 32) return 2;
   // bf16 rows hold twice the 8-bit codes' registers in the prefetch ring
-  return (FMT == KVQ_FMT_KIVI && BITS == 4 && D == 128 && G == 32) || BITS == 16 ? 2 : 3;
+  return ((FMT == KVQ_FMT_KIVI || FMT == KVQ_FMT_KIVI_F16) && BITS == 4 && D == 128 && G == 32) || BITS == 16 ? 2
+                                                                                                        : 3;
 }
 
 template <int FMT, int BITS, int D, int G, bool BF16, bool FUSED>
-__global__ __launch_bounds__(kThreads, (min_wg_per_cu<FMT, BITS, D, G>())) void decode_split(CacheView cv, const int32_t* seq_lens,
+__global__ __launch_bounds__(kThreads, (min_wg_per_cu<FMT, BITS, D, G, FUSED>())) void decode_split(CacheView cv, const int32_t* seq_lens,
                                                         const void* __restrict__ q, float sm_log2, float* __restrict__ out,
                                                         DecodeWork wk, AppendIn ap) {
-  constexpr bool KIVI = FMT == KVQ_FMT_KIVI;
+  constexpr bool KIVI = FMT == KVQ_FMT_KIVI || FMT == KVQ_FMT_KIVI_F16;
   __shared__ float smem[smem_floats<D, (KIVI ? G : 0), FUSED>()];
   __shared__ uint32_t ticket;
   // What a fused call needs after the token loop is parked in LDS, so that
@@ -1554,7 +1604,7 @@ __global__ __launch_bounds__(kThreads, (min_wg_per_cu<FMT, BITS, D, G>())) void 
     if (!extra) {
       if (!every) return;
     } else if constexpr (KIVI) {
-      split_residual<D, BF16, BITS, G, FUSED>(cv, b, h, s, nq, n, q, sm_log2, wk,
+      split_residual<D, BF16, BITS, G, FUSED, FMT == KVQ_FMT_KIVI_F16>(cv, b, h, s, nq, n, q, sm_log2, wk,
                                               *reinterpret_cast<SmemResidT<D, G, FUSED>*>(smem), ap, app);
     }
   } else if (s >= nsq) {
@@ -1662,7 +1712,7 @@ void visit_g(const CacheView& cv, F&& f) {
     else if constexpr (D == 64) f(Variant<FMT, BITS, D, 64, BF16>{});
     else if (cv.G == 64) f(Variant<FMT, BITS, D, 64, BF16>{});
     else f(Variant<FMT, BITS, D, 128, BF16>{});
-  } else if constexpr (FMT == KVQ_FMT_KIVI) {
+  } else if constexpr (FMT == KVQ_FMT_KIVI || FMT == KVQ_FMT_KIVI_F16) {
     if (cv.G == 32) f(Variant<FMT, BITS, D, 32, BF16>{});
     else f(Variant<FMT, BITS, D, 64, BF16>{});
   } else {
@@ -1685,6 +1735,10 @@ void visit_fmt(const CacheView& cv, F&& f) {
     case KVQ_FMT_INT4: visit_d<KVQ_FMT_INT4, 4, BF16>(cv, f); break;
     case KVQ_FMT_FP8_STATIC: visit_d<KVQ_FMT_FP8_STATIC, 8, BF16>(cv, f); break;
     case KVQ_FMT_INT4_HADAMARD: visit_d<KVQ_FMT_INT4_HADAMARD, 4, BF16>(cv, f); break;
+    case KVQ_FMT_KIVI_F16:
+      if (cv.bits == 4) visit_d<KVQ_FMT_KIVI_F16, 4, BF16>(cv, f);
+      else visit_d<KVQ_FMT_KIVI_F16, 2, BF16>(cv, f);
+      break;
     default:
       if (cv.bits == 4) visit_d<KVQ_FMT_KIVI, 4, BF16>(cv, f);
       else visit_d<KVQ_FMT_KIVI, 2, BF16>(cv, f);
@@ -1707,7 +1761,7 @@ hipError_t launch_decode(const CacheView& cv, const int32_t* seq_lens, const voi
   visit_variant(cv, [&](auto v) {
     using V = decltype(v);
     // slot S-1 (the KIVI residual window)
-    const dim3 grid(V::FMT == KVQ_FMT_KIVI ? work.S : work.S - 1, cv.Hkv, cv.B);
+    const dim3 grid(V::FMT == KVQ_FMT_KIVI || V::FMT == KVQ_FMT_KIVI_F16 ? work.S : work.S - 1, cv.Hkv, cv.B);
     if (app)
       decode_split<V::FMT, V::BITS, V::D, V::G, V::BF16, true><<<grid, kThreads, 0, stream>>>(
           cv, ap.seq_lens, q, sm_log2, out, work, ap);

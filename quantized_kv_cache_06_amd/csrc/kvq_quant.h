@@ -241,10 +241,24 @@ __device__ __forceinline__ void flush_stage(FlushSmem<G, D>& f, const CacheView&
   }
 }
 
+// A scale or zero-point as stored: fp32, or rounded to binary16 (M16;
+// nearest, ties to even), whose value the codes are then taken against.
+// store_meta writes element i of a metadata array of either width.
+template <bool M16>
+__device__ __forceinline__ float stored_meta(float x) {
+  if constexpr (M16) return float(_Float16(x)) + 0.0f;
+  else return x;
+}
+template <bool M16>
+__device__ __forceinline__ void store_meta(float* base, size_t i, float x) {
+  if constexpr (M16) reinterpret_cast<_Float16*>(base)[i] = _Float16(x);
+  else base[i] = x;
+}
+
 // Key half of a flush from the staged tile: per-channel scale and
 // zero-point (stored, and kept in f.sk / f.zk) and the packed codes.
-// Starts and ends with a barrier.
-template <int BITS, int G, int D>
+// Starts and ends with a barrier. M16: binary16 metadata.
+template <int BITS, int G, int D, bool M16 = false>
 __device__ __forceinline__ void flush_key(FlushSmem<G, D>& f, const CacheView& cv, size_t pair, int grp) {
 #pragma clang fp contract(off)
   constexpr float QMAX = float((1 << BITS) - 1);
@@ -270,13 +284,13 @@ __device__ __forceinline__ void flush_key(FlushSmem<G, D>& f, const CacheView& c
       mn = fminf(mn, f.red_mn[p * D + tid]);
       mx = fmaxf(mx, f.red_mx[p * D + tid]);
     }
-    const float s = (mx - mn) / QMAX + 0.0f;
-    const float z = mn + 0.0f;
+    const float s = stored_meta<M16>((mx - mn) / QMAX + 0.0f);
+    const float z = stored_meta<M16>(mn + 0.0f);
     f.sk[tid] = s;
     f.zk[tid] = z;
     const size_t si = (pair * (cv.cap / G) + grp) * D + tid;
-    cv.k_scale[si] = s;
-    cv.k_zero[si] = z;
+    store_meta<M16>(cv.k_scale, si, s);
+    store_meta<M16>(cv.k_zero, si, z);
   }
   __syncthreads();
   {
@@ -298,8 +312,9 @@ __device__ __forceinline__ void flush_key(FlushSmem<G, D>& f, const CacheView& c
 // Value half of a flush from the staged tile: per-token, per-channel-group
 // scale and zero-point (stored, and kept in f.sv / f.zv) and the codes in
 // blocks of TB tokens (8 for INT4, 16 for INT2), one 32-bit word per
-// permuted channel slot. Starts and ends with a barrier.
-template <int BITS, int G, int D>
+// permuted channel slot. Starts and ends with a barrier. M16: binary16
+// metadata.
+template <int BITS, int G, int D, bool M16 = false>
 __device__ __forceinline__ void flush_value(FlushSmem<G, D>& f, const CacheView& cv, size_t pair, int grp) {
 #pragma clang fp contract(off)
   constexpr float QMAX = float((1 << BITS) - 1);
@@ -324,13 +339,13 @@ __device__ __forceinline__ void flush_value(FlushSmem<G, D>& f, const CacheView&
       mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
     }
     if (part == 0) {
-      const float s = (mx - mn) / QMAX + 0.0f;
-      const float z = mn + 0.0f;
+      const float s = stored_meta<M16>((mx - mn) / QMAX + 0.0f);
+      const float z = stored_meta<M16>(mn + 0.0f);
       f.sv[i][j] = s;
       f.zv[i][j] = z;
       const size_t vi = (pair * cv.cap + size_t(grp) * G + i) * NVG + j;
-      cv.v_scale[vi] = s;
-      cv.v_zero[vi] = z;
+      store_meta<M16>(cv.v_scale, vi, s);
+      store_meta<M16>(cv.v_zero, vi, z);
     }
   }
   __syncthreads();

@@ -11,7 +11,8 @@ from kvq_workloads import Workload
 from oracle import kvq_oracle as O
 
 FMT = {"fp8": kvq.FMT_FP8_E4M3, "int8": kvq.FMT_INT8, "kivi": kvq.FMT_KIVI, "bf16": kvq.FMT_BF16,
-       "int4": kvq.FMT_INT4, "fp8s": kvq.FMT_FP8_STATIC, "int4h": kvq.FMT_INT4_HADAMARD}
+       "int4": kvq.FMT_INT4, "fp8s": kvq.FMT_FP8_STATIC, "int4h": kvq.FMT_INT4_HADAMARD,
+       "kivi16": kvq.FMT_KIVI_F16}
 
 
 def config(w: Workload, max_tokens: int, batch: int = None) -> kvq.KvqConfig:
@@ -144,16 +145,21 @@ class CacheContents:
         return (self._per_pair(self.lay.k_scale_off, (cap,), np.float32, b, h)[:n],
                 self._per_pair(self.lay.v_scale_off, (cap,), np.float32, b, h)[:n])
 
+    def _meta_dtype(self):
+        return np.float16 if self.cfg.format == kvq.FMT_KIVI_F16 else np.float32
+
     def kivi_key_params(self, b, h, n_groups):
         cap, d, G = self.lay.token_capacity, self.cfg.head_dim, self.cfg.group
-        s = self._per_pair(self.lay.k_scale_off, (cap // G, d), np.float32, b, h)[:n_groups]
-        z = self._per_pair(self.lay.k_zero_off, (cap // G, d), np.float32, b, h)[:n_groups]
+        dt = self._meta_dtype()
+        s = self._per_pair(self.lay.k_scale_off, (cap // G, d), dt, b, h)[:n_groups]
+        z = self._per_pair(self.lay.k_zero_off, (cap // G, d), dt, b, h)[:n_groups]
         return s, z
 
     def kivi_value_params(self, b, h, n):
         cap, d, G = self.lay.token_capacity, self.cfg.head_dim, self.cfg.group
-        s = self._per_pair(self.lay.v_scale_off, (cap, d // G), np.float32, b, h)[:n]
-        z = self._per_pair(self.lay.v_zero_off, (cap, d // G), np.float32, b, h)[:n]
+        dt = self._meta_dtype()
+        s = self._per_pair(self.lay.v_scale_off, (cap, d // G), dt, b, h)[:n]
+        z = self._per_pair(self.lay.v_zero_off, (cap, d // G), dt, b, h)[:n]
         return s, z
 
     def residual(self, b, h, start, end):
@@ -202,15 +208,16 @@ def assert_cache_matches(contents: CacheContents, b: int, h: int, ref: O.Sequenc
     d = w.head_dim
     np.testing.assert_array_equal(kc, ref.key_codes().reshape(nq, d), err_msg=f"K codes b={b} h={h}")
     np.testing.assert_array_equal(vc, ref.value_codes().reshape(nq, d), err_msg=f"V codes b={b} h={h}")
-    if w.fmt == "kivi":
+    if w.fmt in ("kivi", "kivi16"):
         ng = nq // w.group
         ks, kz = contents.kivi_key_params(b, h, ng)
+        u = np.uint16 if w.fmt == "kivi16" else np.uint32   # compare the stored bits
         if ng:
-            np.testing.assert_array_equal(ks.view(np.uint32), np.stack(ref.k_scale).view(np.uint32))
-            np.testing.assert_array_equal(kz.view(np.uint32), np.stack(ref.k_zero).view(np.uint32))
+            np.testing.assert_array_equal(ks.view(u), np.stack(ref.k_scale).view(u))
+            np.testing.assert_array_equal(kz.view(u), np.stack(ref.k_zero).view(u))
             vs, vz = contents.kivi_value_params(b, h, nq)
-            np.testing.assert_array_equal(vs.view(np.uint32), np.concatenate(ref.v_scale).view(np.uint32))
-            np.testing.assert_array_equal(vz.view(np.uint32), np.concatenate(ref.v_zero).view(np.uint32))
+            np.testing.assert_array_equal(vs.view(u), np.concatenate(ref.v_scale).view(u))
+            np.testing.assert_array_equal(vz.view(u), np.concatenate(ref.v_zero).view(u))
         rk, rv = contents.residual(b, h, nq, n)
         np.testing.assert_array_equal(rk.view(np.uint32), ref.resid_k.view(np.uint32), err_msg="K residual")
         np.testing.assert_array_equal(rv.view(np.uint32), ref.resid_v.view(np.uint32), err_msg="V residual")

@@ -43,7 +43,8 @@ def test_status_strings_and_version():
 
 
 def _cfg(w, max_tokens=None, **kw):
-    c = kvq.make_config({"fp8": 1, "int8": 2, "kivi": 3, "bf16": 4, "int4": 5, "fp8s": 6, "int4h": 7}[w.fmt], w.bits,
+    c = kvq.make_config({"fp8": 1, "int8": 2, "kivi": 3, "bf16": 4, "int4": 5, "fp8s": 6, "int4h": 7, "kivi16": 8}[w.fmt],
+                        w.bits,
                         w.group,
                         w.residual,
                         w.batch,
@@ -60,7 +61,9 @@ VARIANTS = {"bf16-2": WORKLOADS[2].scaled(fmt="bf16", bits=16, group=0, residual
             "int4-g128": WORKLOADS[2].scaled(fmt="int4", bits=4, group=128, residual=0),
             "int4-d64-g64": WORKLOADS[1].scaled(fmt="int4", bits=4, group=64, residual=0),
             "fp8s-2": WORKLOADS[2].scaled(fmt="fp8s"),
-            "int4h-g128": WORKLOADS[5].scaled(fmt="int4h", bits=4, group=128, residual=0)}
+            "int4h-g128": WORKLOADS[5].scaled(fmt="int4h", bits=4, group=128, residual=0),
+            "kivi16-4": WORKLOADS[4].scaled(fmt="kivi16"),
+            "kivi16-1": WORKLOADS[1].scaled(fmt="kivi16")}
 
 
 @pytest.mark.parametrize("idx", sorted(WORKLOADS) + sorted(VARIANTS))
@@ -69,20 +72,21 @@ def test_layout_matches_documented_formulas(idx):
     cfg = _cfg(w)
     lay = kvq.kvq_get_layout(cfg)
     pairs = w.batch * w.n_kv_heads
-    unit = w.group if w.fmt == "kivi" else 32
+    unit = w.group if w.fmt in ("kivi", "kivi16") else 32
     cap = -(-cfg.max_tokens // unit) * unit
     assert lay.token_capacity == cap
     assert lay.row_bytes == w.head_dim * w.bits // 8
     offs = [lay.k_codes_off, lay.v_codes_off, lay.k_scale_off, lay.v_scale_off]
     sizes = [pairs * cap * lay.row_bytes] * 2
-    if w.fmt == "kivi":
+    if w.fmt in ("kivi", "kivi16"):
         d, G = w.head_dim, w.group
+        mb = 2 if w.fmt == "kivi16" else 4            # bytes per scale or zero-point
         offs += [lay.k_zero_off, lay.v_zero_off, lay.k_resid_off, lay.v_resid_off]
         assert lay.resid_slots == w.residual + G
         elem = 4 if w.dtype == "f32" else 2
         assert lay.elem_bytes == elem
-        sizes += [pairs * (cap // G) * d * 4, pairs * cap * (d // G) * 4, pairs * (cap // G) * d * 4,
-                  pairs * cap * (d // G) * 4, pairs * lay.resid_slots * d * elem,
+        sizes += [pairs * (cap // G) * d * mb, pairs * cap * (d // G) * mb, pairs * (cap // G) * d * mb,
+                  pairs * cap * (d // G) * mb, pairs * lay.resid_slots * d * elem,
                   pairs * lay.resid_slots * d * elem]
         order = [0, 1, 2, 4, 3, 5, 6, 7]     # k_scale, k_zero, v_scale, v_zero
         offs = [offs[i] for i in order]

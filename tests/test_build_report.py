@@ -48,10 +48,10 @@ def _built_report():
 def test_built_kernels_use_no_scratch_and_keep_occupancy():
     kernels = _built_report()
     dec = [k for k in kernels if "decode_split" in k]
-    # (FP8 + static FP8 + INT8 + BF16) x 2 head dims + KIVI (2 bit widths x 2 head dims x 2 groups) +
-    # INT4 and Hadamard INT4 (groups 32, 64, 128 at d 128; 32, 64 at d 64), for 2 input types, each
-    # as the plain decode and as the fused append + decode step
-    assert len(dec) == 104
+    # (FP8 + static FP8 + INT8 + BF16) x 2 head dims + KIVI and KIVI with fp16 metadata (2 bit widths
+    # x 2 head dims x 2 groups) + INT4 and Hadamard INT4 (groups 32, 64, 128 at d 128; 32, 64 at
+    # d 64), for 2 input types, each as the plain decode and as the fused append + decode step
+    assert len(dec) == 136
     B.check_resource_usage(kernels)
     for k in dec:
         assert int(kernels[k]["Occupancy [waves/SIMD]"]) >= 2, k
