@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+import quantized_kv_cache_06_amd as kvq
 import kvq_testlib as T
 from kvq_workloads import WORKLOADS, context_lengths, kv_tokens, queries
 from oracle import kvq_oracle as O
@@ -271,8 +272,12 @@ def test_int8_and_kivi_round_half_even_ties():
 
 
 # --- full-size workloads: sampled (b, kv head) pairs ------------------------
-def _sampled_full(idx, pairs, n_decode_pairs, layer=0):
-    w = WORKLOADS[idx]
+def _sampled_full(idx, pairs, n_decode_pairs, layer=0, w=None, fused=False):
+    """Full-size workload idx (or the variant w of it): bulk fill, then
+    sampled (b, kv head) pairs bit-exact against the oracle and their query
+    heads' attention in tolerance. fused: one kvq_append_decode step first
+    (the oracle appends the same token)."""
+    w = WORKLOADS[idx] if w is None else w
     lens = context_lengths(w, layer)
     n_max = int(lens.max())
     _log(f"[full workload {idx}: {w.name} B={w.batch} n<={n_max} layer={layer}]")
@@ -295,7 +300,22 @@ def _sampled_full(idx, pairs, n_decode_pairs, layer=0):
     del k, v
     q = queries(w, layer=layer, device="cuda")
     sm = O.default_sm_scale(w.head_dim)
-    out = cache.decode(q, sm).cpu().numpy()
+    if fused:
+        k1, v1 = kv_tokens(w, 1, layer=layer, stream=1, device="cuda")
+        out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+        kvq.kvq_append_decode(cache.cfg, cache.buf, cache.seq_lens, k1.contiguous(), v1.contiguous(), q.contiguous(),
+                              float(sm), out, cache.ws)
+        out = out.cpu().numpy()
+        assert torch.equal(cache.seq_lens.cpu(), lens + 1)
+        k1f, v1f = T.as_f32(k1), T.as_f32(v1)
+        for b, h in picks:
+            refs[(b, h)].append(k1f[b, h], v1f[b, h])
+        contents = T.CacheContents(cache)
+        for b, h in picks:
+            T.assert_cache_matches(contents, b, h, refs[(b, h)], w)
+        _log("  fused step: sampled pairs bit-exact after the append")
+    else:
+        out = cache.decode(q, sm).cpu().numpy()
     qf = T.as_f32(q)
     g = w.n_q_heads // w.n_kv_heads
     worst = (0.0, 0.0)
