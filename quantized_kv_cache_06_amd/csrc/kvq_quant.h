@@ -227,17 +227,50 @@ __device__ __forceinline__ uint32_t asym_code(float x, float s, float mn, float 
   return uint32_t(qv);
 }
 
+// 8 consecutive input elements (bf16 or fp32) from element i of p (i a
+// multiple of 8, rows 16-byte aligned) as fp32, in 16-byte loads.
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* p, size_t i, float* x) {
+  if constexpr (BF16) {
+    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
+    const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = bf16_lo(a[k]);
+      x[2 * k + 1] = bf16_hi(a[k]);
+    }
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+    const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+}
+
 // Stages tokens [grp*G, grp*G + G) of one pair: a token below n (already in
 // the cache) comes from its residual ring slot, token t >= n from row t - n
-// of the pair's T new input rows. No barrier.
+// of the pair's T new input rows. Every thread issues all its 16-byte loads
+// before it stores to LDS. No barrier.
 template <bool BF16, int G, int D>
 __device__ __forceinline__ void flush_stage(FlushSmem<G, D>& f, const CacheView& cv, size_t pair, int grp, int n,
                                             const void* in, int T, const uint8_t* ring) {
-  for (int e = threadIdx.x; e < G * D; e += kQuantThreads) {
+  constexpr int PER = G * D / (8 * kQuantThreads);  // 8-element loads per thread
+  static_assert(PER * 8 * kQuantThreads == G * D, "staging tiles the group");
+  float x[PER][8];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = (u * kQuantThreads + int(threadIdx.x)) * 8;
     const int i = e / D, c = e % D;
     const int t = grp * G + i;
-    f.xs[i][c] = t < n ? load_elem<BF16>(ring, (pair * cv.C + (t % cv.C)) * D + c)
-                       : load_elem<BF16>(in, (pair * T + (t - n)) * D + c);
+    if (t < n) load8<BF16>(ring, (pair * cv.C + (t % cv.C)) * D + c, x[u]);
+    else load8<BF16>(in, (pair * T + (t - n)) * D + c, x[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = (u * kQuantThreads + int(threadIdx.x)) * 8;
+    const int i = e / D, c = e % D;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) f.xs[i][c + k] = x[u][k];
   }
 }
 
