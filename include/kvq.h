@@ -53,7 +53,10 @@
  *     0, 2^bits - 1); s == 0 -> code 0. Signed zeros in s and z become +0.
  *     A sequence of n tokens keeps its first n_q = G * floor(max(n - R, 0) / G)
  *     tokens quantized and tokens [n_q, n) bit-unchanged in a residual ring.
- *  Dequantized value: code * s (FP8, INT8) or code * s + z (KIVI).
+ *  Dequantized value: code * s (FP8, INT8) or code * s + z (KIVI). The
+ *  further formats (group-wise INT4, its Hadamard-rotated variant, KIVI with
+ *  binary16 metadata, static-scale FP8 and the bf16 baseline) are defined
+ *  with kvq_config below.
  *  Attention is fp32 with an online softmax: for query head h of sequence
  *  b, kv = h / (n_q_heads / n_kv_heads),
  *    out[b,h,:] = sum_t softmax_t(sm_scale * <q[b,h,:], K^[b,kv,t,:]>) V^[b,kv,t,:]
@@ -94,9 +97,10 @@ typedef enum kvq_dtype {
 } kvq_dtype;
 
 /* Shape and format of one layer's cache. Supported: head_dim 64 or 128;
- * n_q_heads = g * n_kv_heads with g in 1..8; bits 8 for FP8/INT8 and 16 for
- * BF16 (group and residual must be 0), bits 4 or 2 for KIVI with group 32
- * or 64 dividing head_dim and 0 <= residual <= 4096; 1 <= max_tokens <= 2^24.
+ * n_q_heads = g * n_kv_heads with g in 1..8; bits 8 for FP8/INT8/FP8_STATIC
+ * and 16 for BF16 (group and residual must be 0), bits 4 or 2 for KIVI and
+ * KIVI_F16 with group 32 or 64 dividing head_dim and 0 <= residual <= 4096,
+ * bits 4 for INT4 and INT4_HADAMARD (below); 1 <= max_tokens <= 2^24.
  * KVQ_FMT_INT4 ([LLMS] "2. INT8 and INT4 Uniform Group-Wise Quantization"):
  * bits 4, group 32, 64 or 128 dividing head_dim, residual 0; Key and Value
  * alike, per token and per group of `group` consecutive channels, s = max|x|
