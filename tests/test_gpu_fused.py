@@ -111,12 +111,24 @@ def test_fused_step_equals_append_then_decode(idx):
     _log(f"  byte-identical caches; outputs differ by at most {worst:.3g}")
 
 
-@pytest.mark.parametrize("fmt", ["kivi", "fp8"])
+EDGE_FORMATS = {
+    "kivi": lambda: SMALL[5],
+    "fp8": lambda: SMALL[2],
+    "int8": lambda: SMALL[3],
+    "kivi16": lambda: SMALL[4].scaled(fmt="kivi16"),
+    "int4": lambda: SMALL[3].scaled(fmt="int4", bits=4, group=32, residual=0),
+    "int4h": lambda: SMALL[2].scaled(fmt="int4h", bits=4, group=128, residual=0),
+    "fp8s": lambda: SMALL[2].scaled(fmt="fp8s"),
+    "bf16": lambda: SMALL[2].scaled(fmt="bf16", bits=16, group=0, residual=0),
+}
+
+
+@pytest.mark.parametrize("fmt", sorted(EDGE_FORMATS))
 def test_fused_capacity_and_empty_sequences(fmt):
     """Ragged lengths 0, 1, cap - 1 and cap: the first three take the token
     (an empty sequence then attends to the new token alone), the full one is
     left unchanged and attended as it is."""
-    base = SMALL[5] if fmt == "kivi" else SMALL[2]
+    base = EDGE_FORMATS[fmt]()
     cap = 300
     w = base.scaled(batch=4, context=cap, context_min=cap)
     _log(f"[fused capacity edges, {fmt}]")
