@@ -339,3 +339,39 @@ def test_full_size_workload_sampled(idx):
 @pytest.mark.parametrize("layer", [0, 79])
 def test_full_size_long_context_layer_sampled(layer):
     _sampled_full(5, pairs=2, n_decode_pairs=2, layer=layer)
+
+
+# --- GQA group sizes the other cases do not use (1, 5, 7) -----------------
+@pytest.mark.parametrize("fmt", ["fp8", "kivi", "int4"])
+@pytest.mark.parametrize("g", [1, 5, 7])
+def test_gqa_group_sizes(fmt, g):
+    base = {"fp8": SMALL[2], "kivi": SMALL[5], "int4": SMALL[3].scaled(fmt="int4", bits=4, group=64, residual=0)}[fmt]
+    w = base.scaled(batch=2, n_kv_heads=2, n_q_heads=2 * g, context=400, context_min=250)
+    _log(f"[GQA g={g} {fmt}]")
+    cache = T.GpuCache(T.config(w, w.context + 8))
+    k, v = kv_tokens(w, w.context, device="cuda")
+    lens = _lens(w)
+    cache.append(k, v, lens if w.ragged else None)
+    torch.cuda.synchronize()
+    seqs = _oracle_all(w, k, v, lens)
+    contents = T.CacheContents(cache)
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            T.assert_cache_matches(contents, b, h, seqs[b][h], w)
+    q = queries(w, device="cuda")
+    sm = O.default_sm_scale(w.head_dim)
+    for st in (0, 64):
+        _check_decode(w, cache, seqs, q, sm, st, f"g{g}-split{st}")
+    # one fused step
+    k1, v1 = kv_tokens(w, 1, stream=2, device="cuda")
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    kvq.kvq_append_decode(cache.cfg, cache.buf, cache.seq_lens, k1.contiguous(), v1.contiguous(), q.contiguous(),
+                          float(sm), out, cache.ws)
+    out = out.cpu().numpy()
+    k1f, v1f, qf = T.as_f32(k1), T.as_f32(v1), T.as_f32(q)
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            seqs[b][h].append(k1f[b, h], v1f[b, h])
+        ref = O.decode_attention(seqs[b], qf[b], sm)
+        ma, rel = T.attention_errors(out[b], ref)
+        assert ma <= T.MAX_ABS_TOL and rel <= T.REL_L2_TOL, f"fused b={b}: {ma:.3g} {rel:.3g}"
