@@ -195,3 +195,38 @@ def test_fused_steps_in_a_graph_replay():
         assert torch.equal(caches[0].buf, caches[1].buf), f"replay {s}"
         assert float((out_g - out_e).abs().max()) <= 1e-6, f"replay {s}"
     assert caches[0].seq_lens.cpu().tolist() == (lens + steps).tolist()
+
+
+@pytest.mark.parametrize("split", [64, 512])
+@pytest.mark.parametrize("idx", [2, 5, 6])
+def test_fused_steps_with_explicit_split_lengths(idx, split):
+    """The fused step with a caller-chosen split length (more, shorter splits;
+    some sequences then hold fewer splits than the grid has): attention
+    in tolerance, cache bit-exact, counters back to zero."""
+    w = CASES[idx]
+    steps = 35
+    _log(f"[fused steps, case {idx}, split {split}]")
+    cache = T.GpuCache(T.config(w, w.context + steps + 8), split_tokens=split)
+    k, v = kv_tokens(w, w.context, device="cuda")
+    lens = _lens(w)
+    cache.append(k, v, lens if w.ragged else None)
+    seqs = _oracle_all(w, k, v, lens)
+    kk, vv = kv_tokens(w, steps, stream=7, device="cuda")
+    kf, vf = T.as_f32(kk), T.as_f32(vv)
+    sm = O.default_sm_scale(w.head_dim)
+    for s in range(steps):
+        q = queries(w, step=s + 1, device="cuda")
+        out = _fused(cache, kk[:, :, s:s + 1], vv[:, :, s:s + 1], q, sm).cpu().numpy()
+        qf = T.as_f32(q)
+        for b in range(w.batch):
+            for h in range(w.n_kv_heads):
+                seqs[b][h].append(kf[b, h, s:s + 1], vf[b, h, s:s + 1])
+            ref = O.decode_attention(seqs[b], qf[b], sm)
+            ma, rel = T.attention_errors(out[b], ref)
+            assert ma <= T.MAX_ABS_TOL and rel <= T.REL_L2_TOL, f"step {s} b={b}: {ma:.3g} {rel:.3g}"
+    torch.cuda.synchronize()
+    assert _counters_zero(cache)
+    contents = T.CacheContents(cache)
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            T.assert_cache_matches(contents, b, h, seqs[b][h], w)
