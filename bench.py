@@ -14,7 +14,9 @@ bytes read by decode + q + out, plus append input and cache writes) per
 second of the timed region; "roofline" covers the decode-attention call
 (one launch of the split-K kernel, whose last split per (sequence, KV head)
 merges the partials) timed with HIP events on its stream;
-"cpu_baseline" times the CPU oracle on a bounded sample of the same work.
+"cpu_baseline" times the CPU oracle on a bounded sample of the same work;
+"stream_read_ceiling" is the read rate of a plain streaming kernel on the
+same device, measured first, for context.
 """
 from __future__ import annotations
 
@@ -215,6 +217,31 @@ def stream_reference(torch, gib):
     print(json.dumps({"stream_reference": res, "gib": gib}), flush=True)
 
 
+def stream_ceiling(torch, gib=2.0):
+    """Read rate of a plain streaming kernel over gib GiB of fp32 in HBM
+    (more than the Infinity Cache holds), timed with events over 10 runs, as
+    the attainable read rate the decode kernel is set against. The kernel is
+    torch's row sum over rows of 4096 floats: one block per row streams the
+    buffer once; a full sum to one scalar streams markedly slower on this
+    device. Taken before the caches are allocated; the buffer is freed again."""
+    n = int(gib * (1 << 30)) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    rows = src.view(-1, 4096)
+    rows.sum(1)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        rows.sum(1)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    del src, rows
+    torch.cuda.empty_cache()
+    return {"kernel": f"torch row sum over {gib:g} GiB fp32, rows of 4096 (plain streaming read)", "bytes": 4 * n,
+            "us": round(ms * 1e3, 2), "gbps": round(4 * n / (ms * 1e-3) / 1e9, 1)}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -237,6 +264,7 @@ def main():
     if args.stream_ref > 0:
         stream_reference(torch, args.stream_ref)
         return
+    ceiling = stream_ceiling(torch)
 
     w = WORKLOADS[args.config]
     if args.cache_format == "bf16":
@@ -432,6 +460,8 @@ def main():
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE, WRITE_SIZE scaled by a 1 GiB copy)",
                      "traffic_source": traffic_src},
     }
+    ceiling["decode_frac_of_ceiling"] = round(achieved / ceiling["gbps"], 4)
+    result["stream_read_ceiling"] = ceiling
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, k_host, v_host, qs[0].float().cpu().numpy(), lens0.numpy(),
                                               args.cpu_seconds)
