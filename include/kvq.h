@@ -208,10 +208,12 @@ int32_t kvq_get_layout(const kvq_config* cfg, kvq_layout* layout);
  *  t_new        tokens per sequence in k_new/v_new, >= 0 (0 is a no-op).
  *  append_lens  device int32 [B] or NULL: sequence b appends only its first
  *               append_lens[b] tokens (ragged batches); NULL = t_new for all.
- * FP8/INT8/INT4/FP8_STATIC quantize each token on arrival (BF16 rounds it). KIVI writes new tokens to the
- * residual ring and quantizes (and packs) every whole group of G tokens
- * that the flush rule admits, Key per channel and Value per token; a group
- * may mix older residual tokens with new ones. The result depends only on
+ * The per-token formats (FP8, INT8, INT4, FP8_STATIC, and INT4_HADAMARD
+ * after rotating the Key row) quantize each token on arrival; BF16 rounds
+ * it. KIVI and KIVI_F16 write new tokens to the residual ring and quantize
+ * (and pack) every whole group of G tokens that the flush rule admits, Key
+ * per channel and Value per token; a group may mix older residual tokens
+ * with new ones. The result depends only on
  * the token sequence, not on how it was split into calls.
  * A sequence with seq_lens[b] < 0, an append length outside [0, t_new], or
  * seq_lens[b] + append length > max_tokens is left entirely unchanged
@@ -230,8 +232,9 @@ int32_t kvq_quantize_append(const kvq_config* cfg, void* cache, int32_t* seq_len
  * workspace starts with batch * (n_kv_heads + 1) uint32 arrival counters
  * (see kvq_decode_attention for the zero-fill rule), then per (sequence,
  * query head) n + 1 partial rows of head_dim + 2 fp32, each array 256-byte
- * aligned. kvq_append_decode takes the same workspace. Errors: KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED (split_tokens not a
- * positive multiple of 64, or more than 128 splits of max_tokens). */
+ * aligned. kvq_append_decode takes the same workspace. Errors:
+ * KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED (split_tokens not a positive
+ * multiple of 64, or more than 128 splits of max_tokens). */
 int32_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t split_tokens, uint64_t* bytes);
 
 /* Single-token decode attention that reads the quantized cache directly and
@@ -288,11 +291,13 @@ int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache, const int
  *  q, sm_scale, out, workspace, workspace_bytes, split_tokens: as in
  *               kvq_decode_attention (the same workspace size and zero-fill
  *               rule). q must not alias cache, k_new or v_new.
- * FP8/INT8: the new token is quantized by the slot that also attends to
- * it. KIVI: the residual-window workgroup writes the token to its ring slot
- * (or, with a zero window, straight into the group it completes) and, when a
- * group completes, quantizes and packs it and attends over its dequantized
- * codes. Calls that overlap in time on one cache or one workspace race.
+ * Per-token formats (FP8, INT8, INT4, FP8_STATIC, INT4_HADAMARD, BF16):
+ * the workgroup of the sequence's first split quantizes the new token,
+ * stores it and attends to it. KIVI and KIVI_F16: the residual-window
+ * workgroup writes the token to its ring slot (or, with a zero window,
+ * straight into the group it completes) and, when a group completes,
+ * quantizes and packs it and attends over its dequantized codes. Calls
+ * that overlap in time on one cache or one workspace race.
  * Errors: KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE,
  * KVQ_ERR_HIP. */
 int32_t kvq_append_decode(const kvq_config* cfg, void* cache, int32_t* seq_lens, const void* k_new,

@@ -459,7 +459,7 @@ template <int D>
 struct SmemQuant {
   float q[8][D];              // query of the GQA group (KIVI)
   // each wave's unnormalized output, maximum and sum; piece kWaves is the
-  // new token of a fused FP8/INT8 step
+  // new token of a fused step of a per-token format
   float o[kWaves + 1][8][D];
   float m[kWaves + 1][8];
   float l[kWaves + 1][8];
@@ -556,7 +556,8 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // ---------------------------------------------------------------------------
-// Fused append + decode, FP8/INT8: the sequence's new token t (its length
+// Fused append + decode, per-token formats (FP8, INT8, INT4, static FP8,
+// rotated INT4, bf16): the sequence's new token t (its length
 // before the call) is quantized by the append's own steps (wave 0 the Key
 // row, wave 1 the Value row) and stored at position t; it enters attention
 // as one more piece of the workgroup's wave merge: maximum = its score, sum
@@ -656,7 +657,7 @@ __device__ __forceinline__ float half_at(const uint32_t (&w)[N], int j) {
 // computes the current one; metadata is re-laid out through the wave's own
 // LDS area.
 // ---------------------------------------------------------------------------
-// With FUSED and t_new >= 0 (FP8/INT8), the fused step's new token t_new
+// With FUSED and t_new >= 0 (the per-token formats), the fused step's new token t_new
 // joins the wave merge as a fifth piece (new_token_piece).
 template <int FMT, int BITS, int D, int G, bool BF16, bool FUSED>
 __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int h, int s, int t0, int t1,
@@ -1581,7 +1582,7 @@ __global__ __launch_bounds__(kThreads, (min_wg_per_cu<FMT, BITS, D, G, FUSED>())
   const int per = (nq + wk.S - 2) / (wk.S - 1);
   const int len = (per + kUnit - 1) / kUnit * kUnit;
   int nsq = len > 0 ? (nq + len - 1) / len : 0;
-  // FP8/INT8 fused step: split 0 also takes the new token (for an empty
+  // fused step of a per-token format: split 0 also takes the new token (for an empty
   // sequence, split 0 holds it alone)
   const int t_new = (FUSED && !KIVI && app) ? n_cache : -1;
   if (t_new >= 0 && nsq == 0) nsq = 1;
