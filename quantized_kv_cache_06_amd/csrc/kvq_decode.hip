@@ -16,16 +16,19 @@
 // softmax state; the waves are merged through LDS at the end. Per tile:
 //
 //  scores (QK): S^T[32 tokens x 16 cols] = K[32 x d] * Qt[d x 16] with
-//    v_mfma_f32_16x16x32_bf16. Column c = 8 * term + head: every query
-//    head of the GQA group (up to 8) appears twice, as the bf16 "hi" part
-//    of its query and as the bf16 "lo" remainder, so the products keep
-//    about 16 significant bits of the fp32 query; the two columns are added
-//    with one DPP row rotation. Codes enter the matrix core exactly as bf16:
-//    E4M3 and INT8 codes convert exactly; INT4/INT2 codes c become 128 + c by
-//    OR-ing them under the bf16 pattern of 128 (the 128 * sum(q) this adds is
-//    subtracted again per group). Per-token scales multiply the finished
-//    scores; KIVI per-channel Key scales are folded into the query once per
-//    group (score = sum_c (q_c s_c) code_c + sum_c q_c z_c).
+//    v_mfma_f32_16x16x32_bf16 (KIVI: _f16). Column c = 8 * term + head:
+//    every query head of the GQA group (up to 8) appears twice, as the
+//    "hi" part of its query and as the "lo" remainder, so the products keep
+//    about 16 (bf16) or 22 (f16) significant bits of the fp32 query; the two
+//    columns are added with one DPP row rotation. Codes enter the matrix
+//    core exactly: E4M3 and INT8 codes convert to bf16 exactly; group-wise
+//    INT4 nibbles (code + 8) become the bf16 128 + nibble by OR-ing them
+//    under the bf16 pattern of 128 (136 * sum(q) comes off per channel
+//    group); KIVI codes become f16 code * 2^k by masking them in place under
+//    the f16 pattern of 1024 and subtracting 1024. Per-token scales multiply
+//    the finished scores; KIVI per-channel Key scales are folded into the
+//    query once per group (score = sum_c (q_c s_c) code_c + sum_c q_c z_c),
+//    with 2^-k taken into the query as well.
 //  softmax: running maximum and sum per head in the log2 domain (exp2).
 //  values (PV): O^T[d x 16] += V^T[d x 32] * P^T[32 x 16], again with the
 //    probabilities (times the per-token Value scale) split into bf16 hi and
