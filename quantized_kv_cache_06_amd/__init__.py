@@ -90,9 +90,22 @@ def _check(status: int, where: str) -> None:
         raise KvqError(status, where)
 
 
+def _check_types(*args) -> None:
+    """(tensor, element type, name) triples: raises ValueError for a tensor
+    of another element type. None and raw integer addresses pass. Every
+    entry point runs this before it takes any address, so a wrong type is
+    reported whatever the device."""
+    for x, dtype, what in args:
+        if x is None or isinstance(x, int):
+            continue
+        if x.dtype != dtype:
+            raise ValueError(f"{what} must be {dtype}, got {x.dtype}")
+
+
 def _addr(x, min_bytes: Optional[int] = None, what: str = "buffer") -> Optional[int]:
     """Device address of a tensor or integer; None stays NULL. For tensors,
-    checks device residency, contiguity and (when given) the byte size."""
+    checks device residency, contiguity and (when given) the byte size. Raw
+    integer addresses are passed unchecked."""
     if x is None:
         return None
     if isinstance(x, int):
@@ -133,13 +146,32 @@ def _elem(cfg: KvqConfig) -> int:
     return 2 if cfg.in_dtype == DT_BF16 else 4
 
 
+def _in_dtype(cfg: KvqConfig):
+    """torch element type of K/V inputs and q for cfg.in_dtype."""
+    import torch
+    return torch.bfloat16 if cfg.in_dtype == DT_BF16 else torch.float32
+
+
+def _i32():
+    import torch
+    return torch.int32
+
+
+def _f32():
+    import torch
+    return torch.float32
+
+
 def kvq_quantize_append(cfg: KvqConfig, cache, seq_lens, k_new, v_new, t_new: int,
                         append_lens=None, stream=None) -> None:
     """Quantize and append t_new tokens per sequence (see include/kvq.h)."""
+    _check_types((seq_lens, _i32(), "seq_lens"), (k_new, _in_dtype(cfg), "k_new"),
+                 (v_new, _in_dtype(cfg), "v_new"), (append_lens, _i32(), "append_lens"))
     lay = kvq_get_layout(cfg)
     n_in = cfg.batch * cfg.n_kv_heads * t_new * cfg.head_dim * _elem(cfg)
     st = lib().kvq_quantize_append(
-        ctypes.byref(cfg), _addr(cache, lay.total_bytes, "cache"), _addr(seq_lens, 4 * cfg.batch, "seq_lens"),
+        ctypes.byref(cfg), _addr(cache, lay.total_bytes, "cache"),
+        _addr(seq_lens, 4 * cfg.batch, "seq_lens"),
         _addr(k_new, n_in, "k_new"), _addr(v_new, n_in, "v_new"), int(t_new),
         _addr(append_lens, 4 * cfg.batch, "append_lens"), _stream(stream))
     _check(st, "kvq_quantize_append")
@@ -157,14 +189,17 @@ def kvq_decode_attention(cfg: KvqConfig, cache, seq_lens, q, sm_scale: float, ou
     """Decode attention of one query token per sequence over the cache.
     The workspace must be zero-filled before its first use (its leading
     arrival counters are left zero by every call)."""
+    _check_types((seq_lens, _i32(), "seq_lens"), (q, _in_dtype(cfg), "q"), (out, _f32(), "out"))
     lay = kvq_get_layout(cfg)
     if workspace_bytes is None:
         workspace_bytes = (workspace.numel() * workspace.element_size()
                            if not isinstance(workspace, int) else kvq_decode_workspace_bytes(cfg, split_tokens))
     n_q = cfg.batch * cfg.n_q_heads * cfg.head_dim
     st = lib().kvq_decode_attention(
-        ctypes.byref(cfg), _addr(cache, lay.total_bytes, "cache"), _addr(seq_lens, 4 * cfg.batch, "seq_lens"),
-        _addr(q, n_q * _elem(cfg), "q"), ctypes.c_float(sm_scale), _addr(out, n_q * 4, "out"),
+        ctypes.byref(cfg), _addr(cache, lay.total_bytes, "cache"),
+        _addr(seq_lens, 4 * cfg.batch, "seq_lens"),
+        _addr(q, n_q * _elem(cfg), "q"), ctypes.c_float(sm_scale),
+        _addr(out, n_q * 4, "out"),
         _addr(workspace, workspace_bytes, "workspace"), int(workspace_bytes), int(split_tokens),
         _stream(stream))
     _check(st, "kvq_decode_attention")
@@ -176,6 +211,8 @@ def kvq_append_decode(cfg: KvqConfig, cache, seq_lens, k_new, v_new, q, sm_scale
     sequence (k_new, v_new shaped [B, Hkv, 1, d]) and attend over the grown
     cache; seq_lens advances on the device. Same workspace rules as
     kvq_decode_attention."""
+    _check_types((seq_lens, _i32(), "seq_lens"), (k_new, _in_dtype(cfg), "k_new"),
+                 (v_new, _in_dtype(cfg), "v_new"), (q, _in_dtype(cfg), "q"), (out, _f32(), "out"))
     lay = kvq_get_layout(cfg)
     if workspace_bytes is None:
         workspace_bytes = (workspace.numel() * workspace.element_size()
@@ -183,8 +220,10 @@ def kvq_append_decode(cfg: KvqConfig, cache, seq_lens, k_new, v_new, q, sm_scale
     n_q = cfg.batch * cfg.n_q_heads * cfg.head_dim
     n_in = cfg.batch * cfg.n_kv_heads * cfg.head_dim * _elem(cfg)
     st = lib().kvq_append_decode(
-        ctypes.byref(cfg), _addr(cache, lay.total_bytes, "cache"), _addr(seq_lens, 4 * cfg.batch, "seq_lens"),
-        _addr(k_new, n_in, "k_new"), _addr(v_new, n_in, "v_new"), _addr(q, n_q * _elem(cfg), "q"),
-        ctypes.c_float(sm_scale), _addr(out, n_q * 4, "out"), _addr(workspace, workspace_bytes, "workspace"),
+        ctypes.byref(cfg), _addr(cache, lay.total_bytes, "cache"),
+        _addr(seq_lens, 4 * cfg.batch, "seq_lens"),
+        _addr(k_new, n_in, "k_new"), _addr(v_new, n_in, "v_new"),
+        _addr(q, n_q * _elem(cfg), "q"), ctypes.c_float(sm_scale),
+        _addr(out, n_q * 4, "out"), _addr(workspace, workspace_bytes, "workspace"),
         int(workspace_bytes), int(split_tokens), _stream(stream))
     _check(st, "kvq_append_decode")

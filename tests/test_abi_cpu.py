@@ -251,3 +251,37 @@ def test_value_slot_permutation_matches_header(d, word_bytes):
         chunk, inner = divmod(c, 16 * W)
         m, x = inner % 16, inner // 16
         assert slots[c] == chunk * 16 * W + W * m + x
+
+
+def test_binding_checks_element_types_before_the_device():
+    """The Python binding refuses tensors of the wrong element type (int64
+    lengths, fp32 inputs under a bf16 config, a non-fp32 output) with a
+    ValueError naming the argument, before it looks at the device, so the
+    check runs without a GPU; right types then fail only on residency."""
+    import torch
+    w = WORKLOADS[2]  # bf16 inputs
+    cfg = _cfg(w)
+    assert cfg.in_dtype == kvq.DT_BF16
+    B, H, Hq, d = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.head_dim
+    cache = torch.zeros(kvq.kvq_get_layout(cfg).total_bytes, dtype=torch.uint8)
+    ws = torch.zeros(kvq.kvq_decode_workspace_bytes(cfg, 0), dtype=torch.uint8)
+    lens32, lens64 = torch.zeros(B, dtype=torch.int32), torch.zeros(B, dtype=torch.int64)
+    kv16, kv32 = torch.zeros(B, H, 1, d, dtype=torch.bfloat16), torch.zeros(B, H, 1, d, dtype=torch.float32)
+    q16, q32 = torch.zeros(B, Hq, d, dtype=torch.bfloat16), torch.zeros(B, Hq, d, dtype=torch.float32)
+    out32, out16 = torch.zeros(B, Hq, d, dtype=torch.float32), torch.zeros(B, Hq, d, dtype=torch.bfloat16)
+
+    def raises(match, fn, *args, **kw):
+        with pytest.raises(ValueError, match=match):
+            fn(*args, **kw)
+
+    raises("seq_lens must be torch.int32", kvq.kvq_quantize_append, cfg, cache, lens64, kv16, kv16, 1)
+    raises("k_new must be torch.bfloat16", kvq.kvq_quantize_append, cfg, cache, lens32, kv32, kv16, 1)
+    raises("append_lens must be torch.int32", kvq.kvq_quantize_append, cfg, cache, lens32, kv16, kv16, 1,
+           append_lens=lens64)
+    raises("q must be torch.bfloat16", kvq.kvq_decode_attention, cfg, cache, lens32, q32, 0.1, out32, ws)
+    raises("out must be torch.float32", kvq.kvq_decode_attention, cfg, cache, lens32, q16, 0.1, out16, ws)
+    raises("v_new must be torch.bfloat16", kvq.kvq_append_decode, cfg, cache, lens32, kv16, kv32, q16, 0.1,
+           out32, ws)
+    # correct element types: the next check is residency
+    raises("must be a GPU tensor", kvq.kvq_decode_attention, cfg, cache, lens32, q16, 0.1, out32, ws)
+    raises("must be a GPU tensor", kvq.kvq_append_decode, cfg, cache, lens32, kv16, kv16, q16, 0.1, out32, ws)
