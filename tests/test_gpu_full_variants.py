@@ -24,9 +24,18 @@ def test_full_size_format_variant_sampled(name):
     _sampled_full(idx, pairs=2, n_decode_pairs=1, w=WORKLOADS[idx].scaled(**kw))
 
 
-@pytest.mark.parametrize("idx", [2, 4])
+@pytest.mark.parametrize("idx", [2, 3, 4])
 def test_full_size_fused_step_sampled(idx):
     _sampled_full(idx, pairs=2, n_decode_pairs=2, fused=True)
+
+
+@pytest.mark.parametrize("name", sorted(VARIANTS))
+def test_full_size_format_variant_fused_step_sampled(name):
+    """One fused append + decode step on each variant at its full workload
+    size: the appended token's codes (and, for KIVI, a completed group)
+    bit-exact on the sampled pairs, attention in tolerance."""
+    idx, kw = VARIANTS[name]
+    _sampled_full(idx, pairs=2, n_decode_pairs=1, w=WORKLOADS[idx].scaled(**kw), fused=True)
 
 
 def test_full_size_long_context_fused_step_sampled():
