@@ -202,6 +202,23 @@ __device__ __forceinline__ float sum_rows(float x) {
   x += __shfl_xor(x, 16, kWave);
   return x + __shfl_xor(x, 32, kWave);
 }
+// Maximum over lanes 0-31, wave-uniform, without LDS traffic: quad swaps,
+// the half-row and row mirrors leave each 16-lane row holding its maximum;
+// lanes 0 and 16 then give the two rows' maxima.
+template <int CTRL>
+__device__ __forceinline__ float max_dpp(float v) {
+  const int y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false);
+  return fmaxf(v, __builtin_bit_cast(float, y));
+}
+__device__ __forceinline__ float max_lanes32(float x) {
+  x = max_dpp<0xb1>(x);   // quad_perm [1, 0, 3, 2]
+  x = max_dpp<0x4e>(x);   // quad_perm [2, 3, 0, 1]
+  x = max_dpp<0x141>(x);  // row_half_mirror
+  x = max_dpp<0x140>(x);  // row_mirror
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+  return fmaxf(r0, r1);
+}
 
 // FP8 E4M3 byte pair (bytes 2*sel, 2*sel+1 of w) to a bf16 pair, exact.
 template <int SEL>
@@ -1030,9 +1047,7 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
           float ms = 0.0f;
 #pragma unroll
           for (int j = 0; j < KGL; ++j) ms = fmaxf(ms, gv[j]);
-#pragma unroll
-          for (int o = 1; o < 32; o <<= 1) ms = fmaxf(ms, __shfl_xor(ms, o, kWave));
-          ms = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, ms)));
+          ms = max_lanes32(ms);
           kes = ms > 0.0f ? 7 - __builtin_amdgcn_frexp_expf(ms) : 0;
           float* gdst = sm.kgrp[wave][part] + qi * KGL;
 #pragma unroll
