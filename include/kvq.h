@@ -34,9 +34,11 @@
  *  - Streams: `stream` is a hipStream_t (NULL = the default stream). Calls
  *    are asynchronous and ordered on that stream; none synchronizes.
  *  - One cache buffer holds one layer (the `layer_idx` of [N4N] Step 3 is
- *    the caller's choice of buffer). A zero-filled buffer with all
- *    seq_lens == 0 is an empty cache; codes and scales of tokens beyond a
- *    sequence's length are never read.
+ *    the caller's choice of buffer). A buffer with all seq_lens == 0 is an
+ *    empty cache whatever bytes it holds (zero-filling it is customary, not
+ *    required): codes, scales and zero-points stored at positions at or
+ *    beyond a sequence's length may be loaded with the last, partial tile of
+ *    a sequence, but they are masked and never change a result.
  *
  * Numerics
  * --------
@@ -100,7 +102,11 @@ typedef enum kvq_dtype {
  * n_q_heads = g * n_kv_heads with g in 1..8; bits 8 for FP8/INT8/FP8_STATIC
  * and 16 for BF16 (group and residual must be 0), bits 4 or 2 for KIVI and
  * KIVI_F16 with group 32 or 64 dividing head_dim and 0 <= residual <= 4096,
- * bits 4 for INT4 and INT4_HADAMARD (below); 1 <= max_tokens <= 2^24.
+ * bits 4 for INT4 and INT4_HADAMARD (below); 1 <= max_tokens <= 2^24, and
+ * one (sequence, kv head) pair's Key code region, token_capacity *
+ * row_bytes bytes, below 2^32 (the kernels address it with 32-bit offsets;
+ * this bounds only BF16 at head_dim 128 to max_tokens <= 2^24 - 32);
+ * KVQ_ERR_UNSUPPORTED otherwise.
  * KVQ_FMT_INT4 ([LLMS] "2. INT8 and INT4 Uniform Group-Wise Quantization"):
  * bits 4, group 32, 64 or 128 dividing head_dim, residual 0; Key and Value
  * alike, per token and per group of `group` consecutive channels, s = max|x|
@@ -208,6 +214,13 @@ int32_t kvq_get_layout(const kvq_config* cfg, kvq_layout* layout);
  *  t_new        tokens per sequence in k_new/v_new, >= 0 (0 is a no-op).
  *  append_lens  device int32 [B] or NULL: sequence b appends only its first
  *               append_lens[b] tokens (ragged batches); NULL = t_new for all.
+ *  skipped      device int32 [B] or NULL (caller-owned, 4-byte aligned): when
+ *               given and t_new > 0, the call sets skipped[b] = 1 for every
+ *               sequence it leaves unchanged (rule below: capacity overflow
+ *               or a malformed length) and 0 for every other, in stream
+ *               order with the append; with t_new == 0 it is not written.
+ *               A caller sees an overflow here without a host
+ *               synchronization or an allocation.
  * The per-token formats (FP8, INT8, INT4, FP8_STATIC, and INT4_HADAMARD
  * after rotating the Key row) quantize each token on arrival; BF16 rounds
  * it. KIVI and KIVI_F16 write new tokens to the residual ring and quantize
@@ -216,13 +229,12 @@ int32_t kvq_get_layout(const kvq_config* cfg, kvq_layout* layout);
  * with new ones. The result depends only on
  * the token sequence, not on how it was split into calls.
  * A sequence with seq_lens[b] < 0, an append length outside [0, t_new], or
- * seq_lens[b] + append length > max_tokens is left entirely unchanged
- * (callers detect this by reading seq_lens). Calls that overlap in time on
- * the same cache race. Errors: KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED,
- * KVQ_ERR_HIP. */
+ * seq_lens[b] + append length > max_tokens is left entirely unchanged and
+ * reported in `skipped`. Calls that overlap in time on the same cache race.
+ * Errors: KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED, KVQ_ERR_HIP. */
 int32_t kvq_quantize_append(const kvq_config* cfg, void* cache, int32_t* seq_lens,
                             const void* k_new, const void* v_new, int32_t t_new,
-                            const int32_t* append_lens, void* stream);
+                            const int32_t* append_lens, int32_t* skipped, void* stream);
 
 /* Workspace bytes that kvq_decode_attention needs for split_tokens (0 =
  * the library's choice for cfg). Host only; the result does not depend on
@@ -291,6 +303,9 @@ int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache, const int
  *  q, sm_scale, out, workspace, workspace_bytes, split_tokens: as in
  *               kvq_decode_attention (the same workspace size and zero-fill
  *               rule). q must not alias cache, k_new or v_new.
+ *  skipped      device int32 [B] or NULL (caller-owned, 4-byte aligned): when
+ *               given, set to 1 for every sequence that takes no token
+ *               (seq_lens[b] < 0 or >= max_tokens) and 0 for every other.
  * Per-token formats (FP8, INT8, INT4, FP8_STATIC, INT4_HADAMARD, BF16):
  * the workgroup of the sequence's first split quantizes the new token,
  * stores it and attends to it. KIVI and KIVI_F16: the residual-window
@@ -302,7 +317,7 @@ int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache, const int
  * KVQ_ERR_HIP. */
 int32_t kvq_append_decode(const kvq_config* cfg, void* cache, int32_t* seq_lens, const void* k_new,
                           const void* v_new, const void* q, float sm_scale, float* out, void* workspace,
-                          uint64_t workspace_bytes, int32_t split_tokens, void* stream);
+                          uint64_t workspace_bytes, int32_t split_tokens, int32_t* skipped, void* stream);
 
 #ifdef __cplusplus
 }

@@ -66,7 +66,7 @@ def lib() -> ctypes.CDLL:
         L.kvq_version.restype = ctypes.c_int32
         L.kvq_get_layout.argtypes = [cfgp, ctypes.POINTER(KvqLayout)]
         L.kvq_get_layout.restype = ctypes.c_int32
-        L.kvq_quantize_append.argtypes = [cfgp, P, P, P, P, ctypes.c_int32, P, P]
+        L.kvq_quantize_append.argtypes = [cfgp, P, P, P, P, ctypes.c_int32, P, P, P]
         L.kvq_quantize_append.restype = ctypes.c_int32
         L.kvq_decode_workspace_bytes.argtypes = [cfgp, ctypes.c_int32, ctypes.POINTER(ctypes.c_uint64)]
         L.kvq_decode_workspace_bytes.restype = ctypes.c_int32
@@ -74,7 +74,7 @@ def lib() -> ctypes.CDLL:
                                            ctypes.c_int32, P]
         L.kvq_decode_attention.restype = ctypes.c_int32
         L.kvq_append_decode.argtypes = [cfgp, P, P, P, P, P, ctypes.c_float, P, P, ctypes.c_uint64,
-                                        ctypes.c_int32, P]
+                                        ctypes.c_int32, P, P]
         L.kvq_append_decode.restype = ctypes.c_int32
         _lib = L
     return _lib
@@ -163,17 +163,21 @@ def _f32():
 
 
 def kvq_quantize_append(cfg: KvqConfig, cache, seq_lens, k_new, v_new, t_new: int,
-                        append_lens=None, stream=None) -> None:
-    """Quantize and append t_new tokens per sequence (see include/kvq.h)."""
+                        append_lens=None, skipped=None, stream=None) -> None:
+    """Quantize and append t_new tokens per sequence (see include/kvq.h).
+    skipped: optional int32 [B] device tensor, set to 1 for each sequence the
+    append leaves unchanged (over capacity or a malformed length), else 0."""
     _check_types((seq_lens, _i32(), "seq_lens"), (k_new, _in_dtype(cfg), "k_new"),
-                 (v_new, _in_dtype(cfg), "v_new"), (append_lens, _i32(), "append_lens"))
+                 (v_new, _in_dtype(cfg), "v_new"), (append_lens, _i32(), "append_lens"),
+                 (skipped, _i32(), "skipped"))
     lay = kvq_get_layout(cfg)
     n_in = cfg.batch * cfg.n_kv_heads * t_new * cfg.head_dim * _elem(cfg)
     st = lib().kvq_quantize_append(
         ctypes.byref(cfg), _addr(cache, lay.total_bytes, "cache"),
         _addr(seq_lens, 4 * cfg.batch, "seq_lens"),
         _addr(k_new, n_in, "k_new"), _addr(v_new, n_in, "v_new"), int(t_new),
-        _addr(append_lens, 4 * cfg.batch, "append_lens"), _stream(stream))
+        _addr(append_lens, 4 * cfg.batch, "append_lens"), _addr(skipped, 4 * cfg.batch, "skipped"),
+        _stream(stream))
     _check(st, "kvq_quantize_append")
 
 
@@ -206,13 +210,17 @@ def kvq_decode_attention(cfg: KvqConfig, cache, seq_lens, q, sm_scale: float, ou
 
 
 def kvq_append_decode(cfg: KvqConfig, cache, seq_lens, k_new, v_new, q, sm_scale: float, out, workspace,
-                      workspace_bytes: Optional[int] = None, split_tokens: int = 0, stream=None) -> None:
+                      workspace_bytes: Optional[int] = None, split_tokens: int = 0, skipped=None,
+                      stream=None) -> None:
     """One decode step in one launch: append the one new K/V token per
     sequence (k_new, v_new shaped [B, Hkv, 1, d]) and attend over the grown
     cache; seq_lens advances on the device. Same workspace rules as
-    kvq_decode_attention."""
+    kvq_decode_attention. skipped: optional int32 [B] device tensor, set to
+    1 for each sequence that takes no token (at capacity or a negative
+    length), else 0."""
     _check_types((seq_lens, _i32(), "seq_lens"), (k_new, _in_dtype(cfg), "k_new"),
-                 (v_new, _in_dtype(cfg), "v_new"), (q, _in_dtype(cfg), "q"), (out, _f32(), "out"))
+                 (v_new, _in_dtype(cfg), "v_new"), (q, _in_dtype(cfg), "q"), (out, _f32(), "out"),
+                 (skipped, _i32(), "skipped"))
     lay = kvq_get_layout(cfg)
     if workspace_bytes is None:
         workspace_bytes = (workspace.numel() * workspace.element_size()
@@ -225,5 +233,5 @@ def kvq_append_decode(cfg: KvqConfig, cache, seq_lens, k_new, v_new, q, sm_scale
         _addr(k_new, n_in, "k_new"), _addr(v_new, n_in, "v_new"),
         _addr(q, n_q * _elem(cfg), "q"), ctypes.c_float(sm_scale),
         _addr(out, n_q * 4, "out"), _addr(workspace, workspace_bytes, "workspace"),
-        int(workspace_bytes), int(split_tokens), _stream(stream))
+        int(workspace_bytes), int(split_tokens), _addr(skipped, 4 * cfg.batch, "skipped"), _stream(stream))
     _check(st, "kvq_append_decode")

@@ -53,6 +53,12 @@ int32_t validate(const kvq_config* c) {
     default:
       return KVQ_ERR_INVALID;
   }
+  // The kernels address one (sequence, kv head) pair's Key or Value code
+  // region (token_capacity * row_bytes bytes) with 32-bit offsets.
+  const bool kivi = c->format == KVQ_FMT_KIVI || c->format == KVQ_FMT_KIVI_F16;
+  const uint64_t unit = kivi ? uint64_t(c->group) : 32;
+  const uint64_t cap = (uint64_t(c->max_tokens) + unit - 1) / unit * unit;
+  if (cap * uint64_t(c->head_dim) * uint64_t(c->bits) / 8 >= (uint64_t(1) << 32)) return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;
 }
 
@@ -258,20 +264,22 @@ int32_t kvq_get_layout(const kvq_config* cfg, kvq_layout* layout) {
 }
 
 int32_t kvq_quantize_append(const kvq_config* cfg, void* cache, int32_t* seq_lens, const void* k_new,
-                            const void* v_new, int32_t t_new, const int32_t* append_lens, void* stream) {
+                            const void* v_new, int32_t t_new, const int32_t* append_lens, int32_t* skipped,
+                            void* stream) {
   const int32_t st = validate(cfg);
   if (st != KVQ_OK) return st;
   if (!cache || !seq_lens || t_new < 0) return KVQ_ERR_INVALID;
   if (t_new == 0) return KVQ_OK;
   if (!k_new || !v_new) return KVQ_ERR_INVALID;
   if (!aligned16(cache) || !aligned16(k_new) || !aligned16(v_new) ||
-      (reinterpret_cast<uintptr_t>(seq_lens) & 3) || (reinterpret_cast<uintptr_t>(append_lens) & 3))
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3) || (reinterpret_cast<uintptr_t>(append_lens) & 3) ||
+      (reinterpret_cast<uintptr_t>(skipped) & 3))
     return KVQ_ERR_INVALID;
   if (int64_t(t_new) > kMaxTokens) return KVQ_ERR_UNSUPPORTED;
   kvq_layout L;
   make_layout(cfg, &L);
   const kvq::CacheView v = make_view(cfg, L, cache);
-  const hipError_t e = kvq::launch_append(v, seq_lens, k_new, v_new, t_new, append_lens,
+  const hipError_t e = kvq::launch_append(v, seq_lens, k_new, v_new, t_new, append_lens, skipped,
                                           static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
@@ -295,9 +303,10 @@ int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache, const int
 
 int32_t kvq_append_decode(const kvq_config* cfg, void* cache, int32_t* seq_lens, const void* k_new,
                           const void* v_new, const void* q, float sm_scale, float* out, void* workspace,
-                          uint64_t ws_bytes, int32_t split_tokens, void* stream) {
+                          uint64_t ws_bytes, int32_t split_tokens, int32_t* skipped, void* stream) {
   if (!k_new || !v_new || !seq_lens) return KVQ_ERR_INVALID;
-  const kvq::AppendIn app{seq_lens, k_new, v_new};
+  if (reinterpret_cast<uintptr_t>(skipped) & 3) return KVQ_ERR_INVALID;
+  const kvq::AppendIn app{seq_lens, k_new, v_new, skipped};
   return decode_call(cfg, cache, seq_lens, q, sm_scale, out, workspace, ws_bytes, split_tokens, &app, stream);
 }
 

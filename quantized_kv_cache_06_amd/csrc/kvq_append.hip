@@ -159,10 +159,13 @@ template <bool KIVI>
 __global__ __launch_bounds__(kThreads) void append_finish(CacheView cv, int32_t* __restrict__ seq_lens,
                                                          const void* __restrict__ kin,
                                                          const void* __restrict__ vin, int T,
-                                                         const int32_t* __restrict__ append_lens) {
+                                                         const int32_t* __restrict__ append_lens,
+                                                         int32_t* __restrict__ skipped) {
   const int b = blockIdx.x;
   int n, tb;
-  if (!append_range(cv, seq_lens, append_lens, T, b, &n, &tb)) return;
+  const bool ok = append_range(cv, seq_lens, append_lens, T, b, &n, &tb);
+  if (skipped != nullptr && threadIdx.x == 0) skipped[b] = ok ? 0 : 1;
+  if (!ok) return;
   const int n1 = n + tb;
   if constexpr (KIVI) {
     const int q1 = kivi_quantized(n1, cv.G, cv.R);
@@ -248,7 +251,7 @@ void flush_gd(const CacheView& cv, int32_t* sl, const void* k, const void* v, in
 }  // namespace
 
 hipError_t launch_append(const CacheView& cv, int32_t* seq_lens, const void* k_new, const void* v_new, int T,
-                         const int32_t* append_lens, hipStream_t stream) {
+                         const int32_t* append_lens, int32_t* skipped, hipStream_t stream) {
   if (cv.fmt == KVQ_FMT_KIVI || cv.fmt == KVQ_FMT_KIVI_F16) {
     if (cv.bits == 4) {
       if (cv.bf16) flush_gd<4, true>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
@@ -257,7 +260,7 @@ hipError_t launch_append(const CacheView& cv, int32_t* seq_lens, const void* k_n
       if (cv.bf16) flush_gd<2, true>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
       else flush_gd<2, false>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
     }
-    append_finish<true><<<cv.B, kThreads, 0, stream>>>(cv, seq_lens, k_new, v_new, T, append_lens);
+    append_finish<true><<<cv.B, kThreads, 0, stream>>>(cv, seq_lens, k_new, v_new, T, append_lens, skipped);
   } else {
     if (cv.fmt == KVQ_FMT_FP8_E4M3) {
       if (cv.bf16) per_token_d<KVQ_FMT_FP8_E4M3, true>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
@@ -278,7 +281,7 @@ hipError_t launch_append(const CacheView& cv, int32_t* seq_lens, const void* k_n
       if (cv.bf16) per_token_d<KVQ_FMT_INT8, true>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
       else per_token_d<KVQ_FMT_INT8, false>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
     }
-    append_finish<false><<<cv.B, kThreads, 0, stream>>>(cv, seq_lens, k_new, v_new, T, append_lens);
+    append_finish<false><<<cv.B, kThreads, 0, stream>>>(cv, seq_lens, k_new, v_new, T, append_lens, skipped);
   }
   return hipGetLastError();
 }

@@ -1237,7 +1237,11 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const float vsc = vsf[t][u * NVG + jg];
-            pv[t][u] = ps[t][u] * vsc;
+            // group-wise INT4: a token past the end of the last, partial
+            // tile contributes exactly 0, whatever its stored scale holds
+            // (KIVI tiles are always whole)
+            if constexpr (INT4G) pv[t][u] = tok<BITS>(t, r, ja + u) < valid ? ps[t][u] * vsc : 0.0f;
+            else pv[t][u] = ps[t][u] * vsc;
             if constexpr (KIVI) zs = fmaf(ps[t][u], fmaf(kCenter, vsc, vzf[t][u * NVG + jg]), zs);
           }
         if constexpr (KIVI) zb[jg] += zs;
@@ -1588,6 +1592,9 @@ __global__ __launch_bounds__(kThreads, (min_wg_per_cu<FMT, BITS, D, G, FUSED>())
   const int raw = seq_lens[b];
   bool app = false;
   if constexpr (FUSED) app = raw >= 0 && raw < cv.max_tokens;
+  if constexpr (FUSED) {
+    if (ap.skipped != nullptr && s == 0 && h == 0 && tid == 0) ap.skipped[b] = app ? 0 : 1;
+  }
   const int n_cache = min(max(raw, 0), cv.max_tokens);
   const int n = n_cache + (app ? 1 : 0);  // tokens attended
   // quantized tokens the splits read (KIVI: the new token, and a group it

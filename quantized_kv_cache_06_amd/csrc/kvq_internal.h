@@ -46,8 +46,11 @@ struct DecodeWork {
   int S;            // split slots per (b, q head): S - 1 quantized splits + 1
 };
 
+// skipped: NULL, or [B] set to 1 for each sequence the append leaves
+// unchanged (malformed or over capacity) and 0 for the others.
 hipError_t launch_append(const CacheView& cv, int32_t* seq_lens, const void* k_new,
-                         const void* v_new, int T, const int32_t* append_lens, hipStream_t stream);
+                         const void* v_new, int T, const int32_t* append_lens, int32_t* skipped,
+                         hipStream_t stream);
 
 // The one new token per sequence of a fused append + decode call: K and V
 // rows [B][Hkv][1][D] in the input dtype; seq_lens is advanced in place.
@@ -55,6 +58,7 @@ struct AppendIn {
   int32_t* seq_lens;
   const void* k;
   const void* v;
+  int32_t* skipped;  // NULL, or [B]: 1 for a sequence that takes no token, else 0
 };
 
 // Decode attention; with app != nullptr, the fused step that first appends

@@ -34,10 +34,11 @@ class GpuCache:
         self.ws = torch.zeros(kvq.kvq_decode_workspace_bytes(cfg, split_tokens), dtype=torch.uint8,
                               device=device)
 
-    def append(self, k, v, append_lens=None):
+    def append(self, k, v, append_lens=None, skipped=None):
         t = k.shape[2]
         al = None if append_lens is None else append_lens.to(device=self.buf.device, dtype=torch.int32)
-        kvq.kvq_quantize_append(self.cfg, self.buf, self.seq_lens, k.contiguous(), v.contiguous(), t, al)
+        kvq.kvq_quantize_append(self.cfg, self.buf, self.seq_lens, k.contiguous(), v.contiguous(), t, al,
+                                skipped=skipped)
 
     def decode(self, q, sm_scale, split_tokens=None):
         st = self.split_tokens if split_tokens is None else split_tokens

@@ -161,16 +161,18 @@ def test_append_argument_errors_need_no_gpu():
     L = kvq.lib()
     cfg = _cfg(WORKLOADS[1])
     P = FAKE
-    assert L.kvq_quantize_append(ctypes.byref(cfg), None, P, P, P, 4, None, None) == kvq.ERR_INVALID
-    assert L.kvq_quantize_append(ctypes.byref(cfg), P, None, P, P, 4, None, None) == kvq.ERR_INVALID
-    assert L.kvq_quantize_append(ctypes.byref(cfg), P, P, None, P, 4, None, None) == kvq.ERR_INVALID
-    assert L.kvq_quantize_append(ctypes.byref(cfg), P, P, P, P, -1, None, None) == kvq.ERR_INVALID
-    assert L.kvq_quantize_append(ctypes.byref(cfg), P + 8, P, P, P, 4, None, None) == kvq.ERR_INVALID
-    assert L.kvq_quantize_append(ctypes.byref(cfg), P, P + 2, P, P, 4, None, None) == kvq.ERR_INVALID
-    assert L.kvq_quantize_append(ctypes.byref(cfg), P, P, P, P, (1 << 24) + 1, None, None) == kvq.ERR_UNSUPPORTED
-    assert L.kvq_quantize_append(None, P, P, P, P, 4, None, None) == kvq.ERR_INVALID
+    assert L.kvq_quantize_append(ctypes.byref(cfg), None, P, P, P, 4, None, None, None) == kvq.ERR_INVALID
+    assert L.kvq_quantize_append(ctypes.byref(cfg), P, None, P, P, 4, None, None, None) == kvq.ERR_INVALID
+    assert L.kvq_quantize_append(ctypes.byref(cfg), P, P, None, P, 4, None, None, None) == kvq.ERR_INVALID
+    assert L.kvq_quantize_append(ctypes.byref(cfg), P, P, P, P, -1, None, None, None) == kvq.ERR_INVALID
+    assert L.kvq_quantize_append(ctypes.byref(cfg), P + 8, P, P, P, 4, None, None, None) == kvq.ERR_INVALID
+    assert L.kvq_quantize_append(ctypes.byref(cfg), P, P + 2, P, P, 4, None, None, None) == kvq.ERR_INVALID
+    assert L.kvq_quantize_append(ctypes.byref(cfg), P, P, P, P, (1 << 24) + 1, None, None, None) == kvq.ERR_UNSUPPORTED
+    assert L.kvq_quantize_append(None, P, P, P, P, 4, None, None, None) == kvq.ERR_INVALID
+    # a misaligned skipped array
+    assert L.kvq_quantize_append(ctypes.byref(cfg), P, P, P, P, 4, None, P + 2, None) == kvq.ERR_INVALID
     # appending nothing is a no-op that launches nothing
-    assert L.kvq_quantize_append(ctypes.byref(cfg), P, P, P, P, 0, None, None) == kvq.OK
+    assert L.kvq_quantize_append(ctypes.byref(cfg), P, P, P, P, 0, None, None, None) == kvq.OK
 
 
 def test_decode_argument_errors_need_no_gpu():
@@ -195,7 +197,7 @@ def test_append_decode_argument_errors_need_no_gpu():
     need = kvq.kvq_decode_workspace_bytes(cfg, 0)
     P = FAKE
     f = ctypes.c_float(0.125)
-    ok = (P, P, P, P, P, f, P, P, need, 0, None)
+    ok = (P, P, P, P, P, f, P, P, need, 0, None, None)
 
     def call(*args):
         return L.kvq_append_decode(ctypes.byref(cfg), *args)
@@ -206,8 +208,9 @@ def test_append_decode_argument_errors_need_no_gpu():
     assert call(P, P, P + 8, *ok[3:]) == kvq.ERR_INVALID               # misaligned k_new
     assert call(P, P, P, P, None, *ok[5:]) == kvq.ERR_INVALID          # q
     assert call(*ok[:5], ctypes.c_float(float("inf")), *ok[6:]) == kvq.ERR_INVALID
-    assert call(*ok[:8], need - 1, 0, None) == kvq.ERR_WORKSPACE
-    assert call(*ok[:8], need, 96, None) == kvq.ERR_UNSUPPORTED        # split not a multiple of 64
+    assert call(*ok[:8], need - 1, 0, None, None) == kvq.ERR_WORKSPACE
+    assert call(*ok[:8], need, 96, None, None) == kvq.ERR_UNSUPPORTED  # split not a multiple of 64
+    assert call(*ok[:10], P + 2, None) == kvq.ERR_INVALID              # misaligned skipped
     assert L.kvq_append_decode(None, *ok) == kvq.ERR_INVALID
 
 
@@ -285,3 +288,21 @@ def test_binding_checks_element_types_before_the_device():
     # correct element types: the next check is residency
     raises("must be a GPU tensor", kvq.kvq_decode_attention, cfg, cache, lens32, q16, 0.1, out32, ws)
     raises("must be a GPU tensor", kvq.kvq_append_decode, cfg, cache, lens32, kv16, kv16, q16, 0.1, out32, ws)
+
+
+@pytest.mark.parametrize("fmt,bits,d,max_tokens,status", [
+    (4, 16, 128, (1 << 24) - 32, 0),        # bf16 rows of 256 bytes: 2^32 - 8192 bytes per pair
+    (4, 16, 128, (1 << 24) - 31, 2),        # rounds up to a capacity of 2^24 tokens: 2^32 bytes
+    (4, 16, 128, 1 << 24, 2),
+    (4, 16, 64, 1 << 24, 0),                # rows of 128 bytes: 2^31
+    (1, 8, 128, 1 << 24, 0),                # FP8 rows of 128 bytes
+])
+def test_code_region_stays_below_4_gib(fmt, bits, d, max_tokens, status):
+    """The kernels address one (sequence, kv head) pair's code region with
+    32-bit offsets: a configuration whose region would reach 2^32 bytes is
+    refused on the host instead of wrapping to an empty buffer."""
+    cfg = kvq.make_config(fmt, bits, 0, 0, 1, 1, 1, d, max_tokens, 1)
+    lay = kvq.KvqLayout()
+    assert kvq.lib().kvq_get_layout(ctypes.byref(cfg), ctypes.byref(lay)) == status
+    if status == 0:
+        assert lay.token_capacity * lay.row_bytes < (1 << 32)

@@ -24,11 +24,11 @@ def _log(msg):
     sys.stdout.flush()
 
 
-def _fused(cache, k1, v1, q, sm):
+def _fused(cache, k1, v1, q, sm, skipped=None):
     out = torch.empty((cache.cfg.batch, cache.cfg.n_q_heads, cache.cfg.head_dim), dtype=torch.float32,
                       device=cache.buf.device)
     kvq.kvq_append_decode(cache.cfg, cache.buf, cache.seq_lens, k1.contiguous(), v1.contiguous(), q.contiguous(),
-                          float(sm), out, cache.ws, split_tokens=cache.split_tokens)
+                          float(sm), out, cache.ws, split_tokens=cache.split_tokens, skipped=skipped)
     return out
 
 
@@ -140,9 +140,12 @@ def test_fused_capacity_and_empty_sequences(fmt):
     sm = O.default_sm_scale(w.head_dim)
     kk, vv = kv_tokens(w, 2, stream=5, device="cuda")
     kf, vf = T.as_f32(kk), T.as_f32(vv)
+    skipped = torch.full((w.batch,), 7, dtype=torch.int32, device="cuda")
     for s in range(2):
         q = queries(w, step=s + 1, device="cuda")
-        out = _fused(cache, kk[:, :, s:s + 1], vv[:, :, s:s + 1], q, sm).cpu().numpy()
+        out = _fused(cache, kk[:, :, s:s + 1], vv[:, :, s:s + 1], q, sm, skipped).cpu().numpy()
+        # the full sequence (and, after the first step, the one at cap - 1) takes no token
+        assert skipped.cpu().tolist() == ([0, 0, 0, 1] if s == 0 else [0, 0, 1, 1])
         qf = T.as_f32(q)
         for b in range(w.batch):
             if seqs[b][0].n < cap:

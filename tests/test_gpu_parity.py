@@ -154,7 +154,9 @@ def test_edge_cases_empty_single_residual_only_and_overflow():
     k, v = kv_tokens(w, 300, device="cuda")
     # ragged: 0 tokens, 1 token, fewer than R (all residual), exactly R + G
     lens = torch.tensor([0, 1, 100, w.residual + w.group], dtype=torch.int32)
-    cache.append(k, v, lens)
+    skipped = torch.full((w.batch,), 7, dtype=torch.int32, device="cuda")
+    cache.append(k, v, lens, skipped=skipped)
+    assert skipped.cpu().tolist() == [0, 0, 0, 0]
     seqs = _oracle_all(w, k, v, lens)
     contents = T.CacheContents(cache)
     for b in range(w.batch):
@@ -169,9 +171,12 @@ def test_edge_cases_empty_single_residual_only_and_overflow():
     # overflow for sequence 3 (capacity 300) and malformed lengths leave sequences unchanged
     before = cache.seq_lens.clone()
     k2, v2 = kv_tokens(w, 250, stream=2, device="cuda")
-    cache.append(k2, v2, torch.tensor([0, -1, 251, 250], dtype=torch.int32))
+    cache.append(k2, v2, torch.tensor([0, -1, 251, 250], dtype=torch.int32), skipped=skipped)
     torch.cuda.synchronize()
     assert torch.equal(cache.seq_lens.cpu(), before.cpu())
+    # the caller sees which sequences were left unchanged: a malformed length
+    # (-1, 251 > t_new) or no room (100 + 250 > 300); appending 0 tokens is fine
+    assert skipped.cpu().tolist() == [0, 1, 1, 1]
     contents = T.CacheContents(cache)
     for b in range(w.batch):
         for h in range(w.n_kv_heads):
@@ -364,6 +369,51 @@ def test_gqa_group_sizes(fmt, g):
         _check_decode(w, cache, seqs, q, sm, st, f"g{g}-split{st}")
     # one fused step
     k1, v1 = kv_tokens(w, 1, stream=2, device="cuda")
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    kvq.kvq_append_decode(cache.cfg, cache.buf, cache.seq_lens, k1.contiguous(), v1.contiguous(), q.contiguous(),
+                          float(sm), out, cache.ws)
+    out = out.cpu().numpy()
+    k1f, v1f, qf = T.as_f32(k1), T.as_f32(v1), T.as_f32(q)
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            seqs[b][h].append(k1f[b, h], v1f[b, h])
+        ref = O.decode_attention(seqs[b], qf[b], sm)
+        ma, rel = T.attention_errors(out[b], ref)
+        assert ma <= T.MAX_ABS_TOL and rel <= T.REL_L2_TOL, f"fused b={b}: {ma:.3g} {rel:.3g}"
+
+
+# --- a cache buffer whose unused bytes are not zero --------------------------
+@pytest.mark.parametrize("fmt", ["fp8", "int8", "int4", "int4h", "fp8s", "bf16", "kivi", "kivi16"])
+def test_cache_prefilled_with_nan_bytes(fmt):
+    """Every byte of the cache buffer starts as 0xFF (a NaN pattern for fp32
+    scales, E4M3 codes and bf16 values); lengths are not multiples of the
+    32-token tile. Positions past each sequence's end are loaded with its
+    last, partial tile but must not change the result: appends, plain
+    decode at two split lengths and one fused step agree with the oracle."""
+    base = {"fp8": SMALL[2], "int8": SMALL[3], "kivi": SMALL[5],
+            "int4": SMALL[3].scaled(fmt="int4", bits=4, group=32, residual=0),
+            "int4h": SMALL[3].scaled(fmt="int4h", bits=4, group=128, residual=0),
+            "fp8s": SMALL[2].scaled(fmt="fp8s"),
+            "bf16": SMALL[2].scaled(fmt="bf16", bits=16, group=0, residual=0),
+            "kivi16": SMALL[4].scaled(fmt="kivi16")}[fmt]
+    w = base.scaled(batch=3, context=301, context_min=301)
+    _log(f"[0xFF-prefilled cache, {fmt}]")
+    cache = T.GpuCache(T.config(w, 400))
+    cache.buf.fill_(0xFF)
+    k, v = kv_tokens(w, 301, device="cuda")
+    lens = torch.tensor([301, 45, 263], dtype=torch.int32)
+    cache.append(k, v, lens)
+    seqs = _oracle_all(w, k, v, lens)
+    contents = T.CacheContents(cache)
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            T.assert_cache_matches(contents, b, h, seqs[b][h], w)
+    q = queries(w, device="cuda")
+    sm = O.default_sm_scale(w.head_dim)
+    for st in (0, 64):
+        out = _check_decode(w, cache, seqs, q, sm, st, f"0xFF-{fmt}")
+        assert np.all(np.isfinite(out))
+    k1, v1 = kv_tokens(w, 1, stream=3, device="cuda")
     out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
     kvq.kvq_append_decode(cache.cfg, cache.buf, cache.seq_lens, k1.contiguous(), v1.contiguous(), q.contiguous(),
                           float(sm), out, cache.ws)
