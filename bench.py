@@ -440,6 +440,7 @@ def run_workload(torch, kvq, w, args, copies_override=0, want_host=False):
             else:
                 host = (k.cpu().numpy(), v.cpu().numpy())
         del k, v
+        torch.cuda.empty_cache()  # the 4 GB input temporaries would otherwise fragment HBM
         caches.append(buf)
         seq_lens.append(sl)
         qs.append(queries(w, layer=c, device=dev))
