@@ -30,7 +30,9 @@
  *    crosses this interface.
  *  - Memory: every buffer is owned by the caller. Pointers named "device"
  *    point to GPU memory of the current device and must be 16-byte aligned.
- *    The library allocates nothing and keeps no global state.
+ *    The library allocates nothing. Its only global state is the fixed
+ *    device workspace of kvq_append_decode_noalloc (one array of
+ *    KVQ_STATIC_WORKSPACE_BYTES per device, held until the process ends).
  *  - Streams: `stream` is a hipStream_t (NULL = the default stream). Calls
  *    are asynchronous and ordered on that stream; none synchronizes.
  *  - One cache buffer holds one layer (the `layer_idx` of [N4N] Step 3 is
@@ -318,6 +320,37 @@ int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache, const int
 int32_t kvq_append_decode(const kvq_config* cfg, void* cache, int32_t* seq_lens, const void* k_new,
                           const void* v_new, const void* q, float sm_scale, float* out, void* workspace,
                           uint64_t workspace_bytes, int32_t split_tokens, int32_t* skipped, void* stream);
+
+/* Bytes of the fixed device workspace behind kvq_append_decode_noalloc. */
+#define KVQ_STATIC_WORKSPACE_BYTES (64ull << 20)
+
+/* kvq_append_decode without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. It calls no hipMalloc, hipFree or other
+ * allocating routine: the arrival counters and partial states live in a
+ * file-scope device array of KVQ_STATIC_WORKSPACE_BYTES (64 MiB), one per
+ * device the library runs on, kept until the process ends; its device
+ * address is looked up on the entry point's first call on a device, with
+ * that device current. Each call first zeroes the counters with a small fill
+ * kernel on `stream` (not a memset), then makes the same launch as
+ * kvq_append_decode with the same split plan, so the cache, seq_lens,
+ * skipped and out are bit for bit those of kvq_append_decode.
+ *  Arguments: as kvq_append_decode, without workspace and workspace_bytes.
+ *  Limit: the call's workspace (kvq_decode_workspace_bytes' layout for the
+ *         planned number of splits: batch * (n_kv_heads + 1) counters, then
+ *         batch * n_q_heads * (splits + 1) partial rows of head_dim + 2
+ *         fp32, each array 256-byte aligned) must fit
+ *         KVQ_STATIC_WORKSPACE_BYTES; otherwise the call
+ *         returns KVQ_ERR_WORKSPACE and launches nothing (with split_tokens
+ *         > 0 this is decided before any HIP call).
+ *  Concurrency: every call on one device shares that device's array, which
+ *         keeps the last call's contents; calls that overlap in time on one
+ *         device (two streams, two threads) race, even on different caches.
+ * Errors: KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE,
+ * KVQ_ERR_HIP. */
+int32_t kvq_append_decode_noalloc(const kvq_config* cfg, void* cache, int32_t* seq_lens, const void* k_new,
+                                  const void* v_new, const void* q, float sm_scale, float* out,
+                                  int32_t split_tokens, int32_t* skipped, void* stream);
 
 #ifdef __cplusplus
 }

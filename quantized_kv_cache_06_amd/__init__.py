@@ -17,7 +17,8 @@ __all__ = [
     "DT_BF16",
     "KvqConfig", "KvqLayout", "KvqError", "LIB_PATH", "lib", "make_config",
     "kvq_status_string", "kvq_version", "kvq_get_layout", "kvq_quantize_append",
-    "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_append_decode",
+    "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_append_decode", "kvq_append_decode_noalloc",
+    "STATIC_WORKSPACE_BYTES",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -26,6 +27,7 @@ LIB_PATH = os.path.join(HERE, "libkvq.so")
 FMT_FP8_E4M3, FMT_INT8, FMT_KIVI, FMT_BF16, FMT_INT4, FMT_FP8_STATIC, FMT_INT4_HADAMARD, FMT_KIVI_F16 = range(1, 9)
 DT_F32, DT_BF16 = 0, 1
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+STATIC_WORKSPACE_BYTES = 64 << 20  # KVQ_STATIC_WORKSPACE_BYTES of include/kvq.h
 
 
 class KvqConfig(ctypes.Structure):
@@ -76,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_append_decode.argtypes = [cfgp, P, P, P, P, P, ctypes.c_float, P, P, ctypes.c_uint64,
                                         ctypes.c_int32, P, P]
         L.kvq_append_decode.restype = ctypes.c_int32
+        L.kvq_append_decode_noalloc.argtypes = [cfgp, P, P, P, P, P, ctypes.c_float, P, ctypes.c_int32, P, P]
+        L.kvq_append_decode_noalloc.restype = ctypes.c_int32
         _lib = L
     return _lib
 
@@ -235,3 +239,26 @@ def kvq_append_decode(cfg: KvqConfig, cache, seq_lens, k_new, v_new, q, sm_scale
         _addr(out, n_q * 4, "out"), _addr(workspace, workspace_bytes, "workspace"),
         int(workspace_bytes), int(split_tokens), _addr(skipped, 4 * cfg.batch, "skipped"), _stream(stream))
     _check(st, "kvq_append_decode")
+
+
+def kvq_append_decode_noalloc(cfg: KvqConfig, cache, seq_lens, k_new, v_new, q, sm_scale: float, out,
+                              split_tokens: int = 0, skipped=None, stream=None) -> None:
+    """kvq_append_decode with the library's fixed device workspace instead of
+    a caller's (for callers that cannot allocate): same arguments without
+    the workspace; raises KvqError(ERR_WORKSPACE) when the call's split plan
+    does not fit STATIC_WORKSPACE_BYTES. Calls that overlap in time on one
+    device race (they share the device's array)."""
+    _check_types((seq_lens, _i32(), "seq_lens"), (k_new, _in_dtype(cfg), "k_new"),
+                 (v_new, _in_dtype(cfg), "v_new"), (q, _in_dtype(cfg), "q"), (out, _f32(), "out"),
+                 (skipped, _i32(), "skipped"))
+    lay = kvq_get_layout(cfg)
+    n_q = cfg.batch * cfg.n_q_heads * cfg.head_dim
+    n_in = cfg.batch * cfg.n_kv_heads * cfg.head_dim * _elem(cfg)
+    st = lib().kvq_append_decode_noalloc(
+        ctypes.byref(cfg), _addr(cache, lay.total_bytes, "cache"),
+        _addr(seq_lens, 4 * cfg.batch, "seq_lens"),
+        _addr(k_new, n_in, "k_new"), _addr(v_new, n_in, "v_new"),
+        _addr(q, n_q * _elem(cfg), "q"), ctypes.c_float(sm_scale),
+        _addr(out, n_q * 4, "out"), int(split_tokens), _addr(skipped, 4 * cfg.batch, "skipped"),
+        _stream(stream))
+    _check(st, "kvq_append_decode_noalloc")

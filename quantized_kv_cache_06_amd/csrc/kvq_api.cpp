@@ -196,15 +196,19 @@ uint64_t workspace_bytes(const kvq_config* c, int S) {
 
 namespace {
 
-// Shared by kvq_decode_attention and kvq_append_decode: checks the decode
-// arguments, plans the splits, lays out the workspace and launches.
+// Shared by kvq_decode_attention, kvq_append_decode and
+// kvq_append_decode_noalloc: checks the decode arguments, plans the splits,
+// lays out the workspace and launches. fixed_ws: the workspace is the
+// library's fixed device array (workspace and ws_bytes are ignored); it
+// must hold the planned splits, and its arrival counters are zeroed by a
+// fill kernel before the decode launch.
 int32_t decode_call(const kvq_config* cfg, const void* cache, const int32_t* seq_lens, const void* q, float sm_scale,
                     float* out, void* workspace, uint64_t ws_bytes, int32_t split_tokens, const kvq::AppendIn* app,
-                    void* stream) {
+                    bool fixed_ws, void* stream) {
   const int32_t st = validate(cfg);
   if (st != KVQ_OK) return st;
-  if (!cache || !seq_lens || !q || !out || !workspace) return KVQ_ERR_INVALID;
-  if (!aligned16(cache) || !aligned16(q) || !aligned16(out) || !aligned16(workspace) ||
+  if (!cache || !seq_lens || !q || !out || (!fixed_ws && !workspace)) return KVQ_ERR_INVALID;
+  if (!aligned16(cache) || !aligned16(q) || !aligned16(out) || (!fixed_ws && !aligned16(workspace)) ||
       (reinterpret_cast<uintptr_t>(seq_lens) & 3))
     return KVQ_ERR_INVALID;
   if (app && (!app->k || !app->v || !aligned16(app->k) || !aligned16(app->v))) return KVQ_ERR_INVALID;
@@ -212,7 +216,10 @@ int32_t decode_call(const kvq_config* cfg, const void* cache, const int32_t* seq
   int n;
   const int32_t sp = split_bound(cfg, split_tokens, &n);
   if (sp != KVQ_OK) return sp;
-  if (ws_bytes < workspace_bytes(cfg, n + 1)) return KVQ_ERR_WORKSPACE;
+  if (!fixed_ws && ws_bytes < workspace_bytes(cfg, n + 1)) return KVQ_ERR_WORKSPACE;
+  // an explicit split length fixes the plan: checked before any HIP call
+  if (fixed_ws && split_tokens > 0 && workspace_bytes(cfg, n + 1) > kvq::kStaticWorkspaceBytes)
+    return KVQ_ERR_WORKSPACE;
   kvq_layout lay;
   make_layout(cfg, &lay);
   const kvq::CacheView v = make_view(cfg, lay, cache);
@@ -223,6 +230,14 @@ int32_t decode_call(const kvq_config* cfg, const void* cache, const int32_t* seq
     n = auto_split(cfg, resident, cus);
   }
   const int S = n + 1;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (fixed_ws) {
+    if (workspace_bytes(cfg, S) > kvq::kStaticWorkspaceBytes) return KVQ_ERR_WORKSPACE;
+    if (kvq::static_workspace(&workspace) != hipSuccess) return KVQ_ERR_HIP;
+    // the array keeps the last call's contents: clear the arrival counters
+    const int words = int((uint64_t(cfg->batch) * cfg->n_kv_heads + uint64_t(cfg->batch)));
+    if (kvq::launch_clear_words(static_cast<uint32_t*>(workspace), words, hs) != hipSuccess) return KVQ_ERR_HIP;
+  }
   const uint64_t rows = uint64_t(cfg->batch) * cfg->n_q_heads * S;
   uint8_t* w = static_cast<uint8_t*>(workspace);
   kvq::DecodeWork work;
@@ -233,8 +248,7 @@ int32_t decode_call(const kvq_config* cfg, const void* cache, const int32_t* seq
   work.m = reinterpret_cast<float*>(w + align256(rows * cfg->head_dim * 4));
   work.l = reinterpret_cast<float*>(w + align256(rows * cfg->head_dim * 4) + align256(rows * 4));
   work.S = S;
-  const hipError_t e =
-      kvq::launch_decode(v, seq_lens, q, sm_scale, out, work, app, static_cast<hipStream_t>(stream));
+  const hipError_t e = kvq::launch_decode(v, seq_lens, q, sm_scale, out, work, app, hs);
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
@@ -247,7 +261,7 @@ const char* kvq_status_string(int32_t s) {
     case KVQ_OK: return "ok";
     case KVQ_ERR_INVALID: return "invalid argument";
     case KVQ_ERR_UNSUPPORTED: return "unsupported configuration";
-    case KVQ_ERR_WORKSPACE: return "workspace too small";
+    case KVQ_ERR_WORKSPACE: return "decode workspace too small (the caller's, or the fixed one)";
     case KVQ_ERR_HIP: return "HIP kernel launch failed";
     default: return "unknown status";
   }
@@ -298,7 +312,8 @@ int32_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t split_tokens, 
 int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache, const int32_t* seq_lens, const void* q,
                              float sm_scale, float* out, void* workspace, uint64_t ws_bytes,
                              int32_t split_tokens, void* stream) {
-  return decode_call(cfg, cache, seq_lens, q, sm_scale, out, workspace, ws_bytes, split_tokens, nullptr, stream);
+  return decode_call(cfg, cache, seq_lens, q, sm_scale, out, workspace, ws_bytes, split_tokens, nullptr, false,
+                     stream);
 }
 
 int32_t kvq_append_decode(const kvq_config* cfg, void* cache, int32_t* seq_lens, const void* k_new,
@@ -307,7 +322,16 @@ int32_t kvq_append_decode(const kvq_config* cfg, void* cache, int32_t* seq_lens,
   if (!k_new || !v_new || !seq_lens) return KVQ_ERR_INVALID;
   if (reinterpret_cast<uintptr_t>(skipped) & 3) return KVQ_ERR_INVALID;
   const kvq::AppendIn app{seq_lens, k_new, v_new, skipped};
-  return decode_call(cfg, cache, seq_lens, q, sm_scale, out, workspace, ws_bytes, split_tokens, &app, stream);
+  return decode_call(cfg, cache, seq_lens, q, sm_scale, out, workspace, ws_bytes, split_tokens, &app, false, stream);
+}
+
+int32_t kvq_append_decode_noalloc(const kvq_config* cfg, void* cache, int32_t* seq_lens, const void* k_new,
+                                  const void* v_new, const void* q, float sm_scale, float* out,
+                                  int32_t split_tokens, int32_t* skipped, void* stream) {
+  if (!k_new || !v_new || !seq_lens) return KVQ_ERR_INVALID;
+  if (reinterpret_cast<uintptr_t>(skipped) & 3) return KVQ_ERR_INVALID;
+  const kvq::AppendIn app{seq_lens, k_new, v_new, skipped};
+  return decode_call(cfg, cache, seq_lens, q, sm_scale, out, nullptr, 0, split_tokens, &app, true, stream);
 }
 
 }  // extern "C"

@@ -47,6 +47,7 @@
 // call.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "kvq_quant.h"
@@ -1795,6 +1796,51 @@ hipError_t launch_decode(const CacheView& cv, const int32_t* seq_lens, const voi
       decode_split<V::FMT, V::BITS, V::D, V::G, V::BF16, false><<<grid, kThreads, 0, stream>>>(
           cv, seq_lens, q, sm_log2, out, work, ap);
   });
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// The fixed workspace of kvq_append_decode_noalloc: a file-scope device
+// array, so that callers that cannot allocate (graph capture, serving loops)
+// still have the arrival counters and partial states the split-K decode
+// needs. Each device the library runs on holds its own copy for the life of
+// the process. In host code `scratch` names a host-side stand-in, not device
+// memory: its device address comes from hipGetSymbolAddress, looked up once
+// per device with that device current, and only that address is passed on.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[kStaticWorkspaceBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+__global__ __launch_bounds__(256) void clear_words(uint32_t* __restrict__ p, int n) {
+  for (int i = int(blockIdx.x) * 256 + int(threadIdx.x); i < n; i += int(gridDim.x) * 256) p[i] = 0u;
+}
+}  // namespace
+
+hipError_t static_workspace(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_clear_words(uint32_t* p, int n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int blocks = (n + 255) / 256 < 64 ? (n + 255) / 256 : 64;
+  clear_words<<<blocks, 256, 0, stream>>>(p, n);
   return hipGetLastError();
 }
 

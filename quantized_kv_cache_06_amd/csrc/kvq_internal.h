@@ -75,4 +75,14 @@ int decode_resident_workgroups(const CacheView& cv);
 // Compute units of the current device; 0 when it cannot be queried.
 int decode_compute_units();
 
+// Fixed decode workspace of kvq_append_decode_noalloc: a file-scope device
+// array of kStaticWorkspaceBytes in kvq_decode.hip, one per device.
+constexpr uint64_t kStaticWorkspaceBytes = KVQ_STATIC_WORKSPACE_BYTES;
+// Device address of the current device's array (looked up once per device,
+// with that device current).
+hipError_t static_workspace(void** ptr);
+// Zeroes n uint32 words at p with a small fill kernel on `stream` (a kernel,
+// not a memset node, so that it can sit in a captured graph).
+hipError_t launch_clear_words(uint32_t* p, int n, hipStream_t stream);
+
 }  // namespace kvq

@@ -306,3 +306,40 @@ def test_code_region_stays_below_4_gib(fmt, bits, d, max_tokens, status):
     assert kvq.lib().kvq_get_layout(ctypes.byref(cfg), ctypes.byref(lay)) == status
     if status == 0:
         assert lay.token_capacity * lay.row_bytes < (1 << 32)
+
+
+def test_noalloc_step_argument_errors_and_limit_need_no_gpu():
+    """kvq_append_decode_noalloc checks its arguments on the host like
+    kvq_append_decode, and with an explicit split length refuses a call whose
+    partial states would not fit the fixed workspace before any HIP call."""
+    L = kvq.lib()
+    cfg = _cfg(WORKLOADS[1])
+    P = FAKE
+    f = ctypes.c_float(0.125)
+    ok = (P, P, P, P, P, f, P, 0, None, None)
+
+    def call(c, *args):
+        return L.kvq_append_decode_noalloc(ctypes.byref(c), *args)
+    assert call(cfg, None, *ok[1:]) == kvq.ERR_INVALID                 # cache
+    assert call(cfg, P, None, *ok[2:]) == kvq.ERR_INVALID              # seq_lens
+    assert call(cfg, P, P, None, *ok[3:]) == kvq.ERR_INVALID           # k_new
+    assert call(cfg, P, P, P, P, None, *ok[5:]) == kvq.ERR_INVALID     # q
+    assert call(cfg, *ok[:6], None, *ok[7:]) == kvq.ERR_INVALID        # out
+    assert call(cfg, *ok[:5], ctypes.c_float(float("nan")), *ok[6:]) == kvq.ERR_INVALID
+    assert call(cfg, *ok[:7], 96, None, None) == kvq.ERR_UNSUPPORTED  # split not a multiple of 64
+    assert call(cfg, *ok[:8], P + 2, None) == kvq.ERR_INVALID          # misaligned skipped
+    assert L.kvq_append_decode_noalloc(None, *ok) == kvq.ERR_INVALID
+    # 16 x 64 query heads x 129 partial rows of 128 fp32: more than 64 MiB
+    big = kvq.make_config(kvq.FMT_FP8_E4M3, 8, 0, 0, 16, 8, 64, 128, 8192, kvq.DT_BF16)
+    rows = 16 * 64 * (8192 // 64 + 1)
+    assert rows * 128 * 4 > kvq.STATIC_WORKSPACE_BYTES
+    assert call(big, *ok[:7], 64, None, None) == kvq.ERR_WORKSPACE
+    # within the limit (the same shapes with 1024-token splits) the checks pass
+    # and the call only fails where it first needs the device
+    assert kvq.kvq_decode_workspace_bytes(big, 1024) <= kvq.STATIC_WORKSPACE_BYTES
+
+
+def test_static_workspace_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define KVQ_STATIC_WORKSPACE_BYTES \((\d+)ull << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == kvq.STATIC_WORKSPACE_BYTES
