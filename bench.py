@@ -418,6 +418,18 @@ def run_workload(torch, kvq, w, args, copies_override=0, want_host=False):
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)  # arrival counters start at zero
     stream = torch.cuda.current_stream()
 
+    # one untimed append through the same kernels on a one-sequence cache of
+    # the same format first: the first launch of a kernel also loads its
+    # code, which would otherwise count against the first copy's fill
+    wcfg = kvq.make_config(fmt, w.bits, w.group, w.residual, 1, w.n_kv_heads, w.n_q_heads, w.head_dim,
+                           2 * (w.group or 32) + w.residual, cfg.in_dtype)
+    wbuf = torch.zeros(kvq.kvq_get_layout(wcfg).total_bytes, dtype=torch.uint8, device=dev)
+    wsl = torch.zeros(1, dtype=torch.int32, device=dev)
+    wk, wv = kv_tokens(w, wcfg.max_tokens, device=dev, batch=1)
+    kvq.kvq_quantize_append(wcfg, wbuf, wsl, wk, wv, wcfg.max_tokens)
+    torch.cuda.synchronize()
+    del wbuf, wsl, wk, wv
+
     caches, seq_lens, qs, outs = [], [], [], []
     fill_ms = []
     host = None

@@ -22,13 +22,24 @@
 // of old ring slots and of seq_lens happen before they are overwritten.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "kvq_quant.h"
 
 namespace kvq {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTokPerBlock = 32;  // tokens per workgroup in the per-token kernel
+// Tuning knobs of the per-token tile append (compile-time; the defaults are
+// the measured best on MI355X): the cache policy of its input loads (2:
+// non-temporal, each input byte is read once) and whether both tensors'
+// rows are requested before either is quantized.
+#ifndef KVQ_APPEND_LOAD_AUX
+#define KVQ_APPEND_LOAD_AUX 2
+#endif
+#ifndef KVQ_APPEND_PRELOAD
+#define KVQ_APPEND_PRELOAD 1
+#endif
 
 // Length checks shared by the append kernels: a sequence whose append would
 // be malformed or overflow the capacity is left unchanged.
@@ -40,33 +51,276 @@ __device__ __forceinline__ bool append_range(const CacheView& cv, const int32_t*
 }
 
 // ---------------------------------------------------------------------------
-// Per-token FP8 E4M3 / INT8 (and the unquantized BF16 cache): one wave per
-// token row, D/64 channels per lane.
+// Per-token FP8 E4M3 / INT8 / static FP8 and the unquantized BF16 cache:
+// one wave per tile of whole 8-token Value blocks, aligned to absolute token
+// positions (TPW = 32 tokens at d = 128, 64 at d = 64). Lane l takes block
+// i = l / LPR of the tile and channels [8 g, 8 g + 8), g = l % LPR, LPR =
+// d / 8: load j (j = 0..7) fetches token 8 i + j of every block, so each
+// input row is read by LPR consecutive lanes in 16-byte pieces, and each
+// lane ends up holding an 8 x 8 (token, channel) tile of its block:
+//  - the row maximum is a DPP maximum over the LPR lanes of the row;
+//  - Key rows are stored as 8-byte (bf16: 16-byte) pieces of each row;
+//  - Value words (one per channel, the block's 8 tokens) come from a byte
+//    transpose in registers; lanes g and g ^ 2 then swap half of their
+//    words so that each writes 64 contiguous bytes of the permuted slots.
+// A block that already holds tokens below the sequence length (an append
+// that starts inside a block) keeps their bytes with a read-modify-write of
+// its words; each word has one writer per call. Positions past the new
+// length are written with codes of zero rows; no reader looks at them.
 // ---------------------------------------------------------------------------
 template <int FMT, int D, bool BF16>
-__global__ __launch_bounds__(kThreads) void append_per_token(CacheView cv, const int32_t* __restrict__ seq_lens,
-                                                            const void* __restrict__ kin,
-                                                            const void* __restrict__ vin, int T,
-                                                            const int32_t* __restrict__ append_lens) {
-  constexpr int CPL = D / kWave;  // channels per lane
+__global__ __launch_bounds__(kThreads, 3) void append_tiles(CacheView cv, const int32_t* __restrict__ seq_lens,
+                                                        const void* __restrict__ kin, const void* __restrict__ vin,
+                                                        int T, const int32_t* __restrict__ append_lens) {
+#pragma clang fp contract(off)
+  constexpr int LPR = D / 8;              // lanes per token row
+  constexpr int TPW = 8 * (kWave / LPR);  // tokens per wave tile
+  constexpr bool CACHE16 = FMT == KVQ_FMT_BF16;
+  constexpr bool SCALED = FMT == KVQ_FMT_FP8_E4M3 || FMT == KVQ_FMT_INT8;
   const int b = blockIdx.z, h = blockIdx.y;
   int n, tb;
   if (!append_range(cv, seq_lens, append_lens, T, b, &n, &tb)) return;
+  if (tb == 0) return;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int tile = n / TPW + int(blockIdx.x) * (kThreads / kWave) + wave;
+  if (tile * TPW >= n + tb) return;  // wave-uniform
+  const int i = lane / LPR, g = lane % LPR;
+  const int tblk = tile * TPW + 8 * i;               // first token of the lane's block
+  const int v_lo = max(n - tblk, 0);                 // tokens [v_lo, v_hi) of the block are new
+  const int v_hi = min(n + tb - tblk, 8);
+  const bool any = v_lo < v_hi;                      // uniform over the LPR lanes of the block
   const size_t pair = pair_index(cv, b, h);
-  const int i_end = min(tb, int(blockIdx.x + 1) * kTokPerBlock);
-  for (int i = int(blockIdx.x) * kTokPerBlock + wave; i < i_end; i += kThreads / kWave) {
-    const int t = n + i;  // absolute token position in the sequence
+  const size_t in_row0 = pair * size_t(T);           // the pair's first input row
+
+  uint32_t kcode[8][CACHE16 ? 4 : 2];  // [token][dword]: the lane's 8 channels of each token
+  uint32_t vcode[8][CACHE16 ? 4 : 2];
+  float kscale[8], vscale[8];
+  // bf16 inputs: both tensors' rows are loaded before either is quantized,
+  // so the Value loads are in flight while the Keys are computed. The loads
+  // go through buffer resources over the tile's new input rows: a row
+  // outside them (before the old length or past the new one) lies outside
+  // the resource, reads as zero and fetches nothing, so every load is
+  // issued unconditionally and the waits stay exact.
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  u32x4_t raw[2][8];
+  if constexpr (BF16) {
+    const int r0 = max(tile * TPW, n);                       // the tile's first new token
+    const int nrows = min((tile + 1) * TPW, n + tb) - r0;    // its new tokens (>= 1)
+    const uint32_t rbytes = uint32_t(nrows) * D * 2;
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
-      const void* src = which ? vin : kin;
-      const size_t in_base = (pair * T + i) * D + lane * CPL;
-      float x[CPL];
+      const uint16_t* base = static_cast<const uint16_t*>(which ? vin : kin) + (in_row0 + size_t(r0 - n)) * D;
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, int(rbytes), 0x00020000);
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) x[j] = load_elem<BF16>(src, in_base + j);
-      float s;
-      const uint32_t codes = quantize_token_lane<FMT, CPL>(x, &s);
-      store_token_codes<FMT, CPL>(cv, pair, t, which != 0, lane, codes, s);
+      for (int j = 0; j < 8; ++j) {
+        // a row before r0 gets an offset at the top of the 32-bit range
+        // (never a wrapped negative one); a row past the new length lies
+        // past the resource's end
+        const int rel = tblk + j - r0;
+        const uint32_t off = rel < 0 ? 0xfffffff0u : uint32_t(rel) * uint32_t(D * 2) + uint32_t(16 * g);
+        raw[which][j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, KVQ_APPEND_LOAD_AUX);
+      }
+      if constexpr (KVQ_APPEND_PRELOAD == 0) {
+        if (which == 0) asm volatile("" ::: "memory");
+      }
+    }
+  }
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const void* src = which ? vin : kin;
+    uint32_t (&code)[8][CACHE16 ? 4 : 2] = which ? vcode : kcode;
+    float (&scale)[8] = which ? vscale : kscale;
+    float x[8][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool live = j >= v_lo && j < v_hi;
+      const size_t row = in_row0 + size_t(tblk + j - n);
+      if constexpr (BF16) {
+        (void)live;
+        (void)row;
+        const uint32_t a[4] = {raw[which][j][0], raw[which][j][1], raw[which][j][2], raw[which][j][3]};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          x[j][2 * k] = bf16_lo(a[k]);
+          x[j][2 * k + 1] = bf16_hi(a[k]);
+        }
+        if constexpr (CACHE16) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) code[j][k] = a[k];  // bf16 inputs are stored as they are
+        }
+      } else {
+        float4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
+        if (live) {
+          const float* r = static_cast<const float*>(src) + row * D + 8 * g;
+          p0 = *reinterpret_cast<const float4*>(r);
+          p1 = *reinterpret_cast<const float4*>(r + 4);
+        }
+        x[j][0] = p0.x; x[j][1] = p0.y; x[j][2] = p0.z; x[j][3] = p0.w;
+        x[j][4] = p1.x; x[j][5] = p1.y; x[j][6] = p1.z; x[j][7] = p1.w;
+        if constexpr (CACHE16) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) code[j][k] = bf16_pair_rne(x[j][2 * k], x[j][2 * k + 1]);
+        }
+      }
+    }
+    if constexpr (!CACHE16) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float sc = 1.0f;
+        if constexpr (SCALED) {
+          float a = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(x[j][e]));
+          a = run_absmax<LPR>(a);
+          sc = a / (FMT == KVQ_FMT_FP8_E4M3 ? 448.0f : 127.0f);
+        }
+        scale[j] = sc;
+        // divide by a positive stand-in where the scale is 0 and select the 0
+        // code afterwards: no branch around each division. The quotient is
+        // the refined-reciprocal one when every scale of the wave is in
+        // range (a wave-uniform test), else a true division.
+        const bool pos = sc > 0.0f;
+        const float den = pos ? sc : 1.0f;
+        const bool fast = __all(in_div_range(den));
+        const float rden = recip_refined(den);
+        auto quot = [&](float xv) { return fast ? div_refined(xv, den, rden) : xv / den; };
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float xv = x[j][4 * k + e];
+            if constexpr (FMT == KVQ_FMT_FP8_STATIC) {
+              y[e] = fminf(fmaxf(xv, -448.0f), 448.0f);
+            } else if constexpr (FMT == KVQ_FMT_FP8_E4M3) {
+              const float q = __builtin_amdgcn_fmed3f(quot(xv), -448.0f, 448.0f);
+              y[e] = pos ? q : 0.0f;
+            } else {
+              const float q = __builtin_amdgcn_fmed3f(rintf(quot(xv)), -127.0f, 127.0f);
+              y[e] = pos ? q : 0.0f;
+            }
+          }
+          uint32_t w;
+          if constexpr (FMT == KVQ_FMT_INT8) {
+            w = (uint32_t(int32_t(y[0])) & 0xffu) | ((uint32_t(int32_t(y[1])) & 0xffu) << 8) |
+                ((uint32_t(int32_t(y[2])) & 0xffu) << 16) | (uint32_t(int32_t(y[3])) << 24);
+          } else {
+            // OCP E4M3, round to nearest even; inputs are already within +-448
+            w = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false));
+            w = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], int(w), true));
+          }
+          code[j][k] = w;
+        }
+      }
+    }
+  }
+  if (!any) return;  // nothing of this lane's block is appended (after every DPP step)
+
+  // ---- Key rows and per-token scales ----
+  constexpr int RB = CACHE16 ? 2 * D : D;  // bytes per Key row
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j < v_lo || j >= v_hi) continue;
+    uint8_t* dst = cv.k_codes + (pair * cv.cap + size_t(tblk + j)) * RB + (CACHE16 ? 16 : 8) * g;
+    if constexpr (CACHE16) *reinterpret_cast<uint4*>(dst) = make_uint4(kcode[j][0], kcode[j][1], kcode[j][2], kcode[j][3]);
+    else *reinterpret_cast<uint2*>(dst) = make_uint2(kcode[j][0], kcode[j][1]);
+  }
+  if constexpr (SCALED) {
+    // lane g < 8 of the block stores token g's scales (picked without an
+    // indexed register access)
+    if (g < 8 && g >= v_lo && g < v_hi) {
+      float ks = kscale[0], vs = vscale[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) {
+        ks = g == j ? kscale[j] : ks;
+        vs = g == j ? vscale[j] : vs;
+      }
+      cv.k_scale[pair * cv.cap + size_t(tblk + g)] = ks;
+      cv.v_scale[pair * cv.cap + size_t(tblk + g)] = vs;
+    }
+  }
+
+  // ---- Value words: one per channel, the block's 8 tokens ----
+  const size_t blk = size_t(tblk / 8);
+  if constexpr (CACHE16) {
+    // word of channel 8 g + e: 16 bytes, token pair p in dword p; no slot
+    // permutation (one word per 16-byte load)
+    uint4* dst = reinterpret_cast<uint4*>(cv.v_codes + (pair * (cv.cap / 8) + blk) * (size_t(D) * 16)) + 8 * g;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t w[4];
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low half of each token's dword
+#pragma unroll
+      for (int p = 0; p < 4; ++p) w[p] = __builtin_amdgcn_perm(vcode[2 * p + 1][e >> 1], vcode[2 * p][e >> 1], sel);
+      if (v_lo > 0) {
+        // keep the halves of tokens below the old length
+        const uint4 old = dst[e];
+        const uint32_t o[4] = {old.x, old.y, old.z, old.w};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t keep = (2 * p < v_lo ? 0x0000ffffu : 0u) | (2 * p + 1 < v_lo ? 0xffff0000u : 0u);
+          w[p] = (o[p] & keep) | (w[p] & ~keep);
+        }
+      }
+      dst[e] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  } else {
+    // word of channel 8 g + e: token j in byte j (tokens 0-3 in the low
+    // dword); lo[e], hi[e]
+    uint32_t lo[8], hi[8];
+    {
+      uint32_t a[4], t[4];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {      // channels 4 half .. 4 half + 3
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {             // tokens 4 q .. 4 q + 3
+#pragma unroll
+          for (int r = 0; r < 4; ++r) a[r] = vcode[4 * q + r][half];
+          transpose4x4_bytes(a, t);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) (q ? hi : lo)[4 * half + e] = t[e];
+        }
+      }
+    }
+    // Slots: channel 8 g + e lies in slot 2 e + odd of the lane's run of 16
+    // slots (odd = bit 1 of g; the run starts at slot 32 (g / 4) + 16 (g & 1)).
+    // The even lane writes slots [0, 8) of the run (its words e < 4 and the
+    // partner's), the odd lane slots [8, 16) (words e >= 4).
+    const bool odd = (g & 2) != 0;
+    uint32_t mine[8], theirs[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      // send the words the partner writes: the even lane its e >= 4, the odd lane its e < 4
+      const uint32_t slo = odd ? lo[k] : lo[4 + k];
+      const uint32_t shi = odd ? hi[k] : hi[4 + k];
+      theirs[2 * k] = quad_swap2(slo);
+      theirs[2 * k + 1] = quad_swap2(shi);
+      mine[2 * k] = odd ? lo[4 + k] : lo[k];
+      mine[2 * k + 1] = odd ? hi[4 + k] : hi[k];
+    }
+    const int run = 32 * (g / 4) + 16 * (g & 1) + (odd ? 8 : 0);
+    uint4* dst = reinterpret_cast<uint4*>(cv.v_codes + (pair * (cv.cap / 8) + blk) * (size_t(D) * 8) + size_t(run) * 8);
+    // 16-byte piece k: slots 2k, 2k + 1 of the half-run = (even word, odd word) of channel e = k (+4)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t w[4];
+      if (odd) {
+        w[0] = theirs[2 * k]; w[1] = theirs[2 * k + 1]; w[2] = mine[2 * k]; w[3] = mine[2 * k + 1];
+      } else {
+        w[0] = mine[2 * k]; w[1] = mine[2 * k + 1]; w[2] = theirs[2 * k]; w[3] = theirs[2 * k + 1];
+      }
+      if (v_lo > 0) {
+        // keep the bytes of tokens below the old length (bytes 0..v_lo-1 of each word)
+        const uint4 old = dst[k];
+        const uint32_t o[4] = {old.x, old.y, old.z, old.w};
+        const uint32_t klo = v_lo >= 4 ? 0xffffffffu : (1u << (8 * v_lo)) - 1u;
+        const uint32_t khi = v_lo <= 4 ? 0u : (1u << (8 * (v_lo - 4))) - 1u;
+        const uint32_t keep[4] = {klo, khi, klo, khi};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = (o[q] & keep[q]) | (w[q] & ~keep[q]);
+      }
+      dst[k] = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
 }
@@ -151,6 +405,207 @@ __global__ __launch_bounds__(kThreads) void kivi_flush(CacheView cv, const int32
 }
 
 // ---------------------------------------------------------------------------
+// KIVI group flush for head_dim 128 and bf16 inputs (the benchmark shapes):
+// one wave per 64 flushed tokens (one group of 64, or two of 32), no LDS and
+// no barrier. Lane l takes quarter q = l / 16 of the tokens (16 consecutive
+// rows, whole Value blocks) and channels [8 g, 8 g + 8), g = l % 16: load j
+// fetches row 16 q + j of every quarter in 16-byte pieces, from the residual
+// ring (tokens below the old length) or the new input.
+//  - Key: per-channel minimum and maximum over the lane's 16 rows, combined
+//    across the quarters of the group with lane exchanges;
+//  - Value: per-token, per-channel-group minimum and maximum over the
+//    G / 8 lanes of the group within the row, by DPP steps;
+//  - codes from the refined-reciprocal quotient (div_refined) where every
+//    scale of the wave is in_div_range (else true divisions), packed in
+//    registers into Key row pieces and whole Value words.
+// The arithmetic of each code, scale and zero-point is that of flush_key /
+// flush_value (and of the oracle): fp32, true quotients, round half to even.
+// ---------------------------------------------------------------------------
+template <int BITS, int G, bool M16>
+__global__ __launch_bounds__(kThreads, 2) void kivi_flush_waves(CacheView cv, const int32_t* __restrict__ seq_lens,
+                                                            const void* __restrict__ kin,
+                                                            const void* __restrict__ vin, int T,
+                                                            const int32_t* __restrict__ append_lens) {
+#pragma clang fp contract(off)
+  constexpr int D = 128;
+  constexpr float QMAX = float((1 << BITS) - 1);
+  constexpr int NVG = D / G;   // Value channel groups per token
+  constexpr int LPG = G / 8;   // lanes of one Value channel group within a row
+  constexpr int QPG = G / 16;  // quarters (16-row lane groups) of one Key group
+  constexpr int TB = BITS == 2 ? 16 : 8;  // tokens per Value word
+  const int b = blockIdx.z, h = blockIdx.y;
+  int n, tb;
+  if (!append_range(cv, seq_lens, append_lens, T, b, &n, &tb)) return;
+  const int q0 = kivi_quantized(n, G, cv.R);
+  const int q1 = kivi_quantized(n + tb, G, cv.R);
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int T0 = q0 + 64 * (int(blockIdx.x) * (kThreads / kWave) + wave);
+  if (T0 >= q1) return;  // wave-uniform
+  const int q = lane / 16, g = lane % 16;
+  const int tq = T0 + 16 * q;                              // the lane's first token
+  const int gstart = T0 + 16 * (q - q % QPG);             // first token of the lane's Key group
+  const bool ok = gstart + G <= q1;                        // the group is flushed by this call
+  const size_t pair = pair_index(cv, b, h);
+  const int C = cv.C;
+
+  // ---- loads: 16 rows of Key (then Value), 8 channels each ----
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  auto load_rows = [&](const uint8_t* ring, const void* in, u32x4_t (&r)[16]) {
+    if (T0 >= n) {
+      // every row is new input: one scalar base for the wave, and the
+      // lane's rows at fixed 256-byte steps from its offset
+      const uint8_t* base = static_cast<const uint8_t*>(in) + (pair * T + size_t(T0 - n)) * (D * 2);
+      const uint32_t lo = uint32_t(16 * q * D * 2 + 16 * g);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        r[j] = u32x4_t{0u, 0u, 0u, 0u};
+        if (ok) r[j] = *reinterpret_cast<const u32x4_t*>(base + lo + j * (D * 2));
+      }
+    } else {
+      // the first flushed tokens of a call: rows from the residual ring
+      // (tokens below the old length) and from the input
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int t = tq + j;
+        const uint16_t* p = t < n ? reinterpret_cast<const uint16_t*>(ring) + (pair * C + size_t(t % C)) * D + 8 * g
+                                  : static_cast<const uint16_t*>(in) + (pair * T + size_t(t - n)) * D + 8 * g;
+        r[j] = u32x4_t{0u, 0u, 0u, 0u};
+        if (ok) r[j] = *reinterpret_cast<const u32x4_t*>(p);
+      }
+    }
+  };
+  auto elem = [](const u32x4_t& w, int e) { return (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]); };
+  // clamp(rint(q), 0, qmax) as an integer (q is finite)
+  auto clamp_code = [](float qv) { return uint32_t(__builtin_amdgcn_fmed3f(rintf(qv), 0.0f, QMAX)); };
+  u32x4_t kr[16], vr[16];
+  load_rows(cv.k_resid, kin, kr);
+
+  // ---- Key: per-channel statistics over the group ----
+  float ks[8], kz[8];
+  {
+    float kmn[8], kmx[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kmn[e] = INFINITY;
+      kmx[e] = -INFINITY;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = elem(kr[j], e);
+        kmn[e] = fminf(kmn[e], x);
+        kmx[e] = fmaxf(kmx[e], x);
+      }
+#pragma unroll
+    for (int o = 16; o < 16 * QPG; o <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        kmn[e] = fminf(kmn[e], __shfl_xor(kmn[e], o, kWave));
+        kmx[e] = fmaxf(kmx[e], __shfl_xor(kmx[e], o, kWave));
+      }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ks[e] = stored_meta<M16>((kmx[e] - kmn[e]) / QMAX + 0.0f);
+      kz[e] = stored_meta<M16>(kmn[e] + 0.0f);
+    }
+  }
+  if (ok && q % QPG == 0) {
+    const size_t si = (pair * (cv.cap / G) + size_t(gstart / G)) * D + 8 * g;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      store_meta<M16>(cv.k_scale, si + e, ks[e]);
+      store_meta<M16>(cv.k_zero, si + e, kz[e]);
+    }
+  }
+
+  // ---- Key codes and stores ----
+  constexpr int KRB = D * BITS / 8;  // Key row bytes
+  {
+    // divisor stand-in 1 for a degenerate channel (s == 0), whose code is 0
+    float kdv[8], ky[8];
+    bool fast = true;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kdv[e] = ks[e] > 0.0f ? ks[e] : 1.0f;
+      fast = fast && in_div_range(kdv[e]);
+      ky[e] = recip_refined(kdv[e]);
+    }
+    fast = __all(fast);  // wave-uniform
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      uint32_t w = 0;
+      if (fast) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          w |= (ks[e] > 0.0f ? clamp_code(div_refined<false>(elem(kr[j], e) - kz[e], kdv[e], ky[e])) : 0u) << (BITS * e);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          w |= (ks[e] > 0.0f ? clamp_code((elem(kr[j], e) - kz[e]) / kdv[e]) : 0u) << (BITS * e);
+      }
+      if (ok) {
+        uint8_t* row = cv.k_codes + (pair * cv.cap + size_t(tq + j)) * KRB;
+        if constexpr (BITS == 4) *reinterpret_cast<uint32_t*>(row + 4 * g) = w;
+        else *reinterpret_cast<uint16_t*>(row + 2 * g) = uint16_t(w);
+      }
+    }
+  }
+
+  // ---- Value: per-token statistics over each channel group, codes ----
+  // (its loads are not hoisted above the Key work: that would hold both
+  // tensors' rows in registers at once)
+  asm volatile("" ::: "memory");
+  load_rows(cv.v_resid, vin, vr);
+  uint32_t vword[16 / TB][8];  // [block][channel]
+#pragma unroll
+  for (int k = 0; k < 16 / TB; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vword[k][e] = 0u;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    float mn = elem(vr[j], 0), mx = mn;
+#pragma unroll
+    for (int e = 1; e < 8; ++e) {
+      mn = fminf(mn, elem(vr[j], e));
+      mx = fmaxf(mx, elem(vr[j], e));
+    }
+    uint32_t kmin = float_key(mn), kmax = float_key(mx);
+    run_minmax_keys<LPG>(kmin, kmax);
+    mn = key_float(kmin);
+    mx = key_float(kmax);
+    const float vsc = stored_meta<M16>((mx - mn) / QMAX + 0.0f);
+    const float vzr = stored_meta<M16>(mn + 0.0f);
+    const float vdv = vsc > 0.0f ? vsc : 1.0f;
+    if (__all(in_div_range(vdv))) {  // wave-uniform
+      const float vy = recip_refined(vdv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        vword[j / TB][e] |=
+            (vsc > 0.0f ? clamp_code(div_refined<false>(elem(vr[j], e) - vzr, vdv, vy)) : 0u) << (BITS * (j % TB));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        vword[j / TB][e] |= (vsc > 0.0f ? clamp_code((elem(vr[j], e) - vzr) / vdv) : 0u) << (BITS * (j % TB));
+    }
+    if (ok && g % LPG == 0) {
+      const size_t vi = (pair * cv.cap + size_t(tq + j)) * NVG + g / LPG;
+      store_meta<M16>(cv.v_scale, vi, vsc);
+      store_meta<M16>(cv.v_zero, vi, vzr);
+    }
+  }
+  if (!ok) return;
+
+  uint32_t* vblocks = reinterpret_cast<uint32_t*>(cv.v_codes);
+#pragma unroll
+  for (int k = 0; k < 16 / TB; ++k) {
+    const size_t blk = size_t((tq + k * TB) / TB);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vblocks[(pair * (cv.cap / TB) + blk) * D + value_slot<4>(8 * g + e)] = vword[k][e];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Second launch: one workgroup per sequence. KIVI: copy the tokens that end
 // in the residual window into their ring slots (bit copy, 16-byte vectors).
 // Then advance seq_lens[b] once every thread has read it.
@@ -193,8 +648,11 @@ __global__ __launch_bounds__(kThreads) void append_finish(CacheView cv, int32_t*
 template <int FMT, int D, bool BF16>
 void launch_per_token(const CacheView& cv, int32_t* seq_lens, const void* k, const void* v, int T,
                       const int32_t* al, hipStream_t st) {
-  const dim3 grid((T + kTokPerBlock - 1) / kTokPerBlock, cv.Hkv, cv.B);
-  append_per_token<FMT, D, BF16><<<grid, kThreads, 0, st>>>(cv, seq_lens, k, v, T, al);
+  // tiles touched by T tokens starting anywhere: at most T / TPW + 2
+  constexpr int TPW = 8 * (kWave / (D / 8));
+  const int ntile = T / TPW + 2;
+  const dim3 grid((ntile + kThreads / kWave - 1) / (kThreads / kWave), cv.Hkv, cv.B);
+  append_tiles<FMT, D, BF16><<<grid, kThreads, 0, st>>>(cv, seq_lens, k, v, T, al);
 }
 
 template <int D, int G, bool BF16, bool ROT>
@@ -222,6 +680,16 @@ void int4_dg(const CacheView& cv, int32_t* sl, const void* k, const void* v, int
 template <int BITS, int G, int D, bool BF16>
 void launch_flush(const CacheView& cv, int32_t* seq_lens, const void* k, const void* v, int T,
                   const int32_t* al, hipStream_t st) {
+  if constexpr (D == 128 && BF16) {
+    // one wave per 64 flushed tokens: at most T + G flushed tokens per pair
+    const int waves = (T + G + 63) / 64;
+    const dim3 grid((waves + kThreads / kWave - 1) / (kThreads / kWave), cv.Hkv, cv.B);
+    if (cv.fmt == KVQ_FMT_KIVI_F16)
+      kivi_flush_waves<BITS, G, true><<<grid, kThreads, 0, st>>>(cv, seq_lens, k, v, T, al);
+    else
+      kivi_flush_waves<BITS, G, false><<<grid, kThreads, 0, st>>>(cv, seq_lens, k, v, T, al);
+    return;
+  }
   const dim3 grid(T / G + 1, cv.Hkv, cv.B);
   if (cv.fmt == KVQ_FMT_KIVI_F16)
     kivi_flush<BITS, G, D, BF16, true><<<grid, kThreads, 0, st>>>(cv, seq_lens, k, v, T, al);

@@ -82,6 +82,114 @@ __device__ __forceinline__ uint32_t quantize_token_lane(const float (&x)[CPL], f
   return codes;
 }
 
+// ---------------------------------------------------------------------------
+// Cross-lane steps without LDS: DPP moves within 16-lane rows.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_max_step(float v) {
+  const int y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false);
+  return fmaxf(v, __builtin_bit_cast(float, y));
+}
+// Maximum over each aligned run of L lanes (L = 8 or 16) of a non-negative
+// float (an absolute maximum), left in every lane of the run: quad swaps,
+// then the half-row mirror (lane k <-> 7 - k) and for 16 the row mirror
+// (k <-> 15 - k), each pairing runs already reduced. Non-negative floats
+// order as their bit patterns, so each step is one unsigned maximum with a
+// DPP operand (no NaN canonicalization).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_umax_step(uint32_t v) {
+  return max(v, uint32_t(__builtin_amdgcn_mov_dpp(int(v), CTRL, 0xf, 0xf, true)));
+}
+template <int L>
+__device__ __forceinline__ float run_absmax(float a) {
+  static_assert(L == 8 || L == 16, "runs of 8 or 16 lanes");
+  uint32_t v = __builtin_bit_cast(uint32_t, a);
+  v = dpp_umax_step<0xb1>(v);   // quad_perm [1, 0, 3, 2]
+  v = dpp_umax_step<0x4e>(v);   // quad_perm [2, 3, 0, 1]
+  v = dpp_umax_step<0x141>(v);  // row_half_mirror
+  if constexpr (L == 16) v = dpp_umax_step<0x140>(v);  // row_mirror
+  return __builtin_bit_cast(float, v);
+}
+// ---------------------------------------------------------------------------
+// Quotients rounded to nearest even without the full division sequence. For
+// a divisor b in [2^-60, 2^60] (in_div_range), the reciprocal seed of the
+// hardware (within 1 ulp of 1/b) is refined once by Newton's step, and the
+// quotient a * y is corrected twice with exact fused-multiply-add residuals
+// a - b q. These are the steps of the library's correctly rounded division
+// once its range scaling is the identity, which it is for such b and any a
+// whose quotient can change a code (|a / b| >= 2^-12: a and every residual
+// stay normal); for smaller quotients the result is still within an ulp and
+// carries the sign of a, which is all a code of such a value depends on. The
+// reciprocal part depends on b alone and is shared by all quotients by b.
+// ---------------------------------------------------------------------------
+// Callers use it where every divisor of a wave is in range (a wave-uniform
+// test) and take true divisions otherwise.
+__device__ __forceinline__ bool in_div_range(float b) {
+  return b >= 0x1p-60f && b <= 0x1p60f;
+}
+__device__ __forceinline__ float recip_refined(float b) {
+  const float y0 = __builtin_amdgcn_rcpf(b);
+  return __builtin_fmaf(__builtin_fmaf(-b, y0, 1.0f), y0, y0);
+}
+// SIGNED: also carry the sign of a onto the result (needed where the code of
+// a tiny quotient keeps its sign, as E4M3's signed zero does; an integer
+// code of a tiny quotient is 0 whatever its sign).
+template <bool SIGNED = true>
+__device__ __forceinline__ float div_refined(float a, float b, float y) {
+#pragma clang fp contract(off)
+  float q = a * y;
+  float r = __builtin_fmaf(-b, q, a);
+  q = __builtin_fmaf(r, y, q);
+  r = __builtin_fmaf(-b, q, a);
+  q = __builtin_fmaf(r, y, q);
+  return SIGNED ? __builtin_copysignf(q, a) : q;
+}
+
+// Order-preserving map of a float to an unsigned integer (finite values;
+// -0 sorts just below +0) and its inverse, so that run minima and maxima of
+// signed values are single unsigned DPP steps.
+__device__ __forceinline__ uint32_t float_key(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  return u ^ (uint32_t(int32_t(u) >> 31) | 0x80000000u);
+}
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __builtin_bit_cast(float, k ^ (uint32_t(int32_t(~k) >> 31) | 0x80000000u));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_umin_step(uint32_t v) {
+  return min(v, uint32_t(__builtin_amdgcn_mov_dpp(int(v), CTRL, 0xf, 0xf, true)));
+}
+// Minimum and maximum keys over each aligned run of L lanes (L = 4 or 8).
+template <int L>
+__device__ __forceinline__ void run_minmax_keys(uint32_t& kmin, uint32_t& kmax) {
+  static_assert(L == 4 || L == 8, "runs of 4 or 8 lanes");
+  kmin = dpp_umin_step<0xb1>(kmin);
+  kmax = dpp_umax_step<0xb1>(kmax);
+  kmin = dpp_umin_step<0x4e>(kmin);
+  kmax = dpp_umax_step<0x4e>(kmax);
+  if constexpr (L == 8) {
+    kmin = dpp_umin_step<0x141>(kmin);
+    kmax = dpp_umax_step<0x141>(kmax);
+  }
+}
+
+// The value of lane l ^ 2 (the other half of each quad).
+__device__ __forceinline__ uint32_t quad_swap2(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x4e, 0xf, 0xf, false));
+}
+
+// 4x4 byte transpose: out[e] byte j = in[j] byte e.
+__device__ __forceinline__ void transpose4x4_bytes(const uint32_t (&in)[4], uint32_t (&out)[4]) {
+  const uint32_t p0 = __builtin_amdgcn_perm(in[1], in[0], 0x05010400u);  // in0.b0 in1.b0 in0.b1 in1.b1
+  const uint32_t p1 = __builtin_amdgcn_perm(in[1], in[0], 0x07030602u);  // in0.b2 in1.b2 in0.b3 in1.b3
+  const uint32_t q0 = __builtin_amdgcn_perm(in[3], in[2], 0x05010400u);
+  const uint32_t q1 = __builtin_amdgcn_perm(in[3], in[2], 0x07030602u);
+  out[0] = __builtin_amdgcn_perm(q0, p0, 0x05040100u);
+  out[1] = __builtin_amdgcn_perm(q0, p0, 0x07060302u);
+  out[2] = __builtin_amdgcn_perm(q1, p1, 0x05040100u);
+  out[3] = __builtin_amdgcn_perm(q1, p1, 0x07060302u);
+}
+
 // Stores one lane's codes and (lane 0) the scale of token t of pair `pair`:
 // Key rows token-major, Value codes in 8-token blocks with one 8-byte word
 // per (permuted) channel slot; BF16: 2-byte codes, 16-byte Value words in

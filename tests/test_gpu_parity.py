@@ -425,3 +425,62 @@ def test_cache_prefilled_with_nan_bytes(fmt):
         ref = O.decode_attention(seqs[b], qf[b], sm)
         ma, rel = T.attention_errors(out[b], ref)
         assert ma <= T.MAX_ABS_TOL and rel <= T.REL_L2_TOL, f"fused b={b}: {ma:.3g} {rel:.3g}"
+
+
+# --- the long-context workload across all 80 layers --------------------------
+@pytest.mark.parametrize("first", list(range(0, 80, 10)))
+def test_long_context_every_layer_sampled(first):
+    """Workload 5 at full size, one layer at a time (each with its own seed
+    and outlier channels): two seeded (sequence, KV head) pairs per layer
+    bit-exact against the oracle (codes, scales, zero-points, residual ring,
+    seq_lens), one pair's query heads within the attention tolerance, and in
+    the middle layer one fused append + decode step checked the same way."""
+    w = WORKLOADS[5]
+    g = w.n_q_heads // w.n_kv_heads
+    sm = O.default_sm_scale(w.head_dim)
+    for layer in range(first, first + 10):
+        lens = context_lengths(w, layer)
+        n_max = int(lens.max())
+        cache = T.GpuCache(T.config(w, n_max + 64))
+        k, v = kv_tokens(w, n_max, layer=layer, device="cuda")
+        cache.append(k, v, lens)
+        torch.cuda.synchronize()
+        assert torch.equal(cache.seq_lens.cpu(), lens)
+        rng = np.random.default_rng(5000 + layer)
+        picks = [(int(rng.integers(w.batch)), int(rng.integers(w.n_kv_heads))) for _ in range(2)]
+        contents = T.CacheContents(cache)
+        refs = {}
+        for b, h in picks:
+            n = int(lens[b])
+            refs[(b, h)] = T.oracle_sequence(w, [T.as_f32(k[b, h, :n])], [T.as_f32(v[b, h, :n])])
+            T.assert_cache_matches(contents, b, h, refs[(b, h)], w)
+        q = queries(w, layer=layer, device="cuda")
+        fused = layer == 40
+        if fused:
+            k1, v1 = kv_tokens(w, 1, layer=layer, stream=1, device="cuda")
+            out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+            kvq.kvq_append_decode(cache.cfg, cache.buf, cache.seq_lens, k1.contiguous(), v1.contiguous(),
+                                  q.contiguous(), float(sm), out, cache.ws)
+            out = out.cpu().numpy()
+            assert torch.equal(cache.seq_lens.cpu(), lens + 1)
+            k1f, v1f = T.as_f32(k1), T.as_f32(v1)
+            contents = T.CacheContents(cache)
+            for b, h in picks:
+                refs[(b, h)].append(k1f[b, h], v1f[b, h])
+                T.assert_cache_matches(contents, b, h, refs[(b, h)], w)
+        else:
+            out = cache.decode(q, sm).cpu().numpy()
+        assert np.all(np.isfinite(out))
+        b, h = picks[0]
+        K, V = refs[(b, h)].dequantized()
+        qf = T.as_f32(q)
+        worst = (0.0, 0.0)
+        for j in range(g):
+            ref = O.attention_one_head(qf[b, h * g + j], K, V, sm)
+            ma, rel = T.attention_errors(out[b, h * g + j], ref)
+            worst = (max(worst[0], ma), max(worst[1], rel))
+            assert ma <= T.MAX_ABS_TOL and rel <= T.REL_L2_TOL, f"layer {layer} b={b} h={h}: {ma:.3g} {rel:.3g}"
+        _log(f"  layer {layer}{' (fused step)' if fused else ''}: pairs {picks} bit-exact, "
+             f"attention max-abs {worst[0]:.3g} rel-L2 {worst[1]:.3g}")
+        del cache, k, v, contents
+        torch.cuda.empty_cache()
