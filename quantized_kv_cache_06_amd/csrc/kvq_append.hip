@@ -15,11 +15,11 @@
 // Quantization arithmetic is fp32 with true IEEE division, round-half-even
 // (rintf) and, because this file is compiled with -ffp-contract=off, no
 // fused multiply-add, so codes, scales and zero-points are reproducible bit
-// for bit. An append is two launches on the caller's stream: the first
-// quantizes (per-token formats) or flushes whole groups (KIVI); the second,
-// one workgroup per sequence, writes the tokens that stay in the KIVI
-// residual ring and then advances seq_lens. Stream order makes every read
-// of old ring slots and of seq_lens happen before they are overwritten.
+// for bit. An append is a few launches on the caller's stream: the first
+// quantizes (per-token formats) or flushes whole groups (KIVI); for KIVI a
+// second writes the tokens that stay in the residual ring; the last
+// advances seq_lens. Stream order makes every read of old ring slots and of
+// seq_lens happen before they are overwritten.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -173,7 +173,9 @@ __global__ __launch_bounds__(kThreads, 3) void append_tiles(CacheView cv, const 
 #pragma unroll
           for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(x[j][e]));
           a = run_absmax<LPR>(a);
-          sc = a / (FMT == KVQ_FMT_FP8_E4M3 ? 448.0f : 127.0f);
+          // a / 448 (or / 127)
+          constexpr float kDen = FMT == KVQ_FMT_FP8_E4M3 ? 448.0f : 127.0f;
+          sc = quot_nonneg(a, kDen, recip_refined(kDen));
         }
         scale[j] = sc;
         // divide by a positive stand-in where the scale is 0 and select the 0
@@ -184,7 +186,10 @@ __global__ __launch_bounds__(kThreads, 3) void append_tiles(CacheView cv, const 
         const float den = pos ? sc : 1.0f;
         const bool fast = __all(in_div_range(den));
         const float rden = recip_refined(den);
-        auto quot = [&](float xv) { return fast ? div_refined(xv, den, rden) : xv / den; };
+        // FP8 keeps the quotient's sign (E4M3 has a signed zero); an INT8 code
+        // of a tiny quotient is 0 whatever its sign
+        constexpr bool SIGNED = FMT == KVQ_FMT_FP8_E4M3;
+        auto quot = [&](float xv) { return fast ? div_refined<SIGNED>(xv, den, rden) : xv / den; };
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           float y[4];
@@ -197,8 +202,8 @@ __global__ __launch_bounds__(kThreads, 3) void append_tiles(CacheView cv, const 
               const float q = __builtin_amdgcn_fmed3f(quot(xv), -448.0f, 448.0f);
               y[e] = pos ? q : 0.0f;
             } else {
-              const float q = __builtin_amdgcn_fmed3f(rintf(quot(xv)), -127.0f, 127.0f);
-              y[e] = pos ? q : 0.0f;
+              // a zero scale means a zero row: its quotients are zeros, code 0
+              y[e] = __builtin_amdgcn_fmed3f(rintf(quot(xv)), -127.0f, 127.0f);
             }
           }
           uint32_t w;
@@ -475,8 +480,28 @@ __global__ __launch_bounds__(kThreads, 2) void kivi_flush_waves(CacheView cv, co
     }
   };
   auto elem = [](const u32x4_t& w, int e) { return (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]); };
-  // clamp(rint(q), 0, qmax) as an integer (q is finite)
-  auto clamp_code = [](float qv) { return uint32_t(__builtin_amdgcn_fmed3f(rintf(qv), 0.0f, QMAX)); };
+  // clamp(rint(q), 0, qmax) for a finite q, carried in the low bits of the
+  // pattern of q' + 1.5 * 2^23 with q' = med3(q, -0.49, qmax + 0.49): the
+  // addition rounds q' to the nearest integer, ties to even (the same as
+  // rint, and q' only moves q within the interval that rounds to the same
+  // clamped code), and leaves it in the mantissa above kRoundBits. Codes are
+  // packed by adding such patterns shifted into place; the sum of the
+  // shifted kRoundBits is taken off once per word (pack_offset).
+  constexpr float kRound = 12582912.0f;  // 1.5 * 2^23
+  constexpr uint32_t kRoundBits = 0x4B400000u;
+  auto code_bits = [](float qv) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_fmed3f(qv, -0.49f, QMAX + 0.49f) + kRound);
+  };
+  auto pack_offset = [](int count) {
+    uint32_t o = 0;
+    for (int i = 0; i < count; ++i) o += kRoundBits << (BITS * i);
+    return o;
+  };
+  // A zero scale (a degenerate group) has code 0. With fp32 metadata it
+  // means max == min, so every difference x - z is 0 and its quotient by the
+  // stand-in divisor 1 is already 0; a binary16 zero-point need not equal
+  // the minimum, so there the code is selected.
+  auto degen = [](float s_, uint32_t c) { return (!M16 || s_ > 0.0f) ? c : kRoundBits; };
   u32x4_t kr[16], vr[16];
   load_rows(cv.k_resid, kin, kr);
 
@@ -504,9 +529,10 @@ __global__ __launch_bounds__(kThreads, 2) void kivi_flush_waves(CacheView cv, co
         kmn[e] = fminf(kmn[e], __shfl_xor(kmn[e], o, kWave));
         kmx[e] = fmaxf(kmx[e], __shfl_xor(kmx[e], o, kWave));
       }
+    const float rq = recip_refined(QMAX);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      ks[e] = stored_meta<M16>((kmx[e] - kmn[e]) / QMAX + 0.0f);
+      ks[e] = stored_meta<M16>(quot_nonneg(kmx[e] - kmn[e], QMAX, rq) + 0.0f);
       kz[e] = stored_meta<M16>(kmn[e] + 0.0f);
     }
   }
@@ -538,12 +564,13 @@ __global__ __launch_bounds__(kThreads, 2) void kivi_flush_waves(CacheView cv, co
       if (fast) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          w |= (ks[e] > 0.0f ? clamp_code(div_refined<false>(elem(kr[j], e) - kz[e], kdv[e], ky[e])) : 0u) << (BITS * e);
+          w += degen(ks[e], code_bits(div_refined<false>(elem(kr[j], e) - kz[e], kdv[e], ky[e]))) << (BITS * e);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          w |= (ks[e] > 0.0f ? clamp_code((elem(kr[j], e) - kz[e]) / kdv[e]) : 0u) << (BITS * e);
+          w += degen(ks[e], code_bits((elem(kr[j], e) - kz[e]) / kdv[e])) << (BITS * e);
       }
+      w -= pack_offset(8);
       if (ok) {
         uint8_t* row = cv.k_codes + (pair * cv.cap + size_t(tq + j)) * KRB;
         if constexpr (BITS == 4) *reinterpret_cast<uint32_t*>(row + 4 * g) = w;
@@ -562,6 +589,8 @@ __global__ __launch_bounds__(kThreads, 2) void kivi_flush_waves(CacheView cv, co
   for (int k = 0; k < 16 / TB; ++k)
 #pragma unroll
     for (int e = 0; e < 8; ++e) vword[k][e] = 0u;
+  float vsc[16], vzr[16], vdv[16];
+  bool vfast = true;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     float mn = elem(vr[j], 0), mx = mn;
@@ -574,26 +603,36 @@ __global__ __launch_bounds__(kThreads, 2) void kivi_flush_waves(CacheView cv, co
     run_minmax_keys<LPG>(kmin, kmax);
     mn = key_float(kmin);
     mx = key_float(kmax);
-    const float vsc = stored_meta<M16>((mx - mn) / QMAX + 0.0f);
-    const float vzr = stored_meta<M16>(mn + 0.0f);
-    const float vdv = vsc > 0.0f ? vsc : 1.0f;
-    if (__all(in_div_range(vdv))) {  // wave-uniform
-      const float vy = recip_refined(vdv);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        vword[j / TB][e] |=
-            (vsc > 0.0f ? clamp_code(div_refined<false>(elem(vr[j], e) - vzr, vdv, vy)) : 0u) << (BITS * (j % TB));
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        vword[j / TB][e] |= (vsc > 0.0f ? clamp_code((elem(vr[j], e) - vzr) / vdv) : 0u) << (BITS * (j % TB));
-    }
+    vsc[j] = stored_meta<M16>(quot_nonneg(mx - mn, QMAX, recip_refined(QMAX)) + 0.0f);
+    vzr[j] = stored_meta<M16>(mn + 0.0f);
+    vdv[j] = vsc[j] > 0.0f ? vsc[j] : 1.0f;
+    vfast = vfast && in_div_range(vdv[j]);
     if (ok && g % LPG == 0) {
       const size_t vi = (pair * cv.cap + size_t(tq + j)) * NVG + g / LPG;
-      store_meta<M16>(cv.v_scale, vi, vsc);
-      store_meta<M16>(cv.v_zero, vi, vzr);
+      store_meta<M16>(cv.v_scale, vi, vsc[j]);
+      store_meta<M16>(cv.v_zero, vi, vzr[j]);
     }
   }
+  if (__all(vfast)) {  // wave-uniform
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float vy = recip_refined(vdv[j]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        vword[j / TB][e] +=
+            degen(vsc[j], code_bits(div_refined<false>(elem(vr[j], e) - vzr[j], vdv[j], vy))) << (BITS * (j % TB));
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        vword[j / TB][e] += degen(vsc[j], code_bits((elem(vr[j], e) - vzr[j]) / vdv[j])) << (BITS * (j % TB));
+  }
+#pragma unroll
+  for (int k = 0; k < 16 / TB; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vword[k][e] -= pack_offset(TB);
   if (!ok) return;
 
   uint32_t* vblocks = reinterpret_cast<uint32_t*>(cv.v_codes);
@@ -606,43 +645,57 @@ __global__ __launch_bounds__(kThreads, 2) void kivi_flush_waves(CacheView cv, co
 }
 
 // ---------------------------------------------------------------------------
-// Second launch: one workgroup per sequence. KIVI: copy the tokens that end
-// in the residual window into their ring slots (bit copy, 16-byte vectors).
-// Then advance seq_lens[b] once every thread has read it.
+// KIVI, second launch: one workgroup per (kv head, sequence) copies the new
+// tokens that stay in the residual window into their ring slots (bit copy,
+// 16-byte vectors, four in flight per thread). It runs after the flush
+// launch, whose reads of old ring slots it may overwrite.
 // ---------------------------------------------------------------------------
-template <bool KIVI>
-__global__ __launch_bounds__(kThreads) void append_finish(CacheView cv, int32_t* __restrict__ seq_lens,
-                                                         const void* __restrict__ kin,
-                                                         const void* __restrict__ vin, int T,
-                                                         const int32_t* __restrict__ append_lens,
-                                                         int32_t* __restrict__ skipped) {
-  const int b = blockIdx.x;
+__global__ __launch_bounds__(kThreads) void ring_copy(CacheView cv, const int32_t* __restrict__ seq_lens,
+                                                     const void* __restrict__ kin, const void* __restrict__ vin,
+                                                     int T, const int32_t* __restrict__ append_lens) {
+  const int h = blockIdx.x, b = blockIdx.y;
   int n, tb;
-  const bool ok = append_range(cv, seq_lens, append_lens, T, b, &n, &tb);
-  if (skipped != nullptr && threadIdx.x == 0) skipped[b] = ok ? 0 : 1;
-  if (!ok) return;
+  if (!append_range(cv, seq_lens, append_lens, T, b, &n, &tb)) return;
   const int n1 = n + tb;
-  if constexpr (KIVI) {
-    const int q1 = kivi_quantized(n1, cv.G, cv.R);
-    const int start = max(n, q1);
-    const int rows = n1 - start;
-    const int row_bytes = cv.D * (cv.bf16 ? 2 : 4);
-    const int vec_per_row = row_bytes / 16;
-    const int total = cv.Hkv * rows * vec_per_row;
-    for (int e = threadIdx.x; e < total; e += kThreads) {
-      const int v = e % vec_per_row;
-      const int r = (e / vec_per_row) % rows;
-      const int h = e / (vec_per_row * rows);
-      const int t = start + r;
-      const size_t pair = pair_index(cv, b, h);
-      const size_t src = (pair * T + (t - n)) * row_bytes + size_t(v) * 16;
-      const size_t dst = (pair * cv.C + (t % cv.C)) * row_bytes + size_t(v) * 16;
-      *reinterpret_cast<uint4*>(cv.k_resid + dst) = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(kin) + src);
-      *reinterpret_cast<uint4*>(cv.v_resid + dst) = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(vin) + src);
+  const int start = max(n, kivi_quantized(n1, cv.G, cv.R));
+  const int row_bytes = cv.D * (cv.bf16 ? 2 : 4);
+  const int vpr = row_bytes / 16;              // 16-byte vectors per row
+  const int total = (n1 - start) * vpr;
+  const size_t pair = pair_index(cv, b, h);
+  constexpr int U = 4;
+  for (int e0 = int(threadIdx.x); e0 < total; e0 += U * kThreads) {
+    uint4 kx[U], vx[U];
+    size_t dst[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = min(e0 + u * kThreads, total - 1);  // a clamped index re-copies the last vector
+      const int t = start + e / vpr, v = e % vpr;
+      const size_t src = (pair * T + size_t(t - n)) * row_bytes + size_t(v) * 16;
+      dst[u] = (pair * cv.C + size_t(t % cv.C)) * row_bytes + size_t(v) * 16;
+      kx[u] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(kin) + src);
+      vx[u] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(vin) + src);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      *reinterpret_cast<uint4*>(cv.k_resid + dst[u]) = kx[u];
+      *reinterpret_cast<uint4*>(cv.v_resid + dst[u]) = vx[u];
     }
   }
-  __syncthreads();
-  if (threadIdx.x == 0) seq_lens[b] = n1;
+}
+
+// ---------------------------------------------------------------------------
+// Last launch: one workgroup per sequence advances seq_lens[b] (every
+// earlier launch of the append has read it) and reports a skipped sequence.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void append_finish(CacheView cv, int32_t* __restrict__ seq_lens, int T,
+                                                   const int32_t* __restrict__ append_lens,
+                                                   int32_t* __restrict__ skipped) {
+  const int b = int(blockIdx.x) * 64 + int(threadIdx.x);
+  if (b >= cv.B) return;
+  int n, tb;
+  const bool ok = append_range(cv, seq_lens, append_lens, T, b, &n, &tb);
+  if (skipped != nullptr) skipped[b] = ok ? 0 : 1;
+  if (ok) seq_lens[b] = n + tb;
 }
 
 template <int FMT, int D, bool BF16>
@@ -728,7 +781,8 @@ hipError_t launch_append(const CacheView& cv, int32_t* seq_lens, const void* k_n
       if (cv.bf16) flush_gd<2, true>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
       else flush_gd<2, false>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
     }
-    append_finish<true><<<cv.B, kThreads, 0, stream>>>(cv, seq_lens, k_new, v_new, T, append_lens, skipped);
+    ring_copy<<<dim3(cv.Hkv, cv.B), kThreads, 0, stream>>>(cv, seq_lens, k_new, v_new, T, append_lens);
+    append_finish<<<(cv.B + 63) / 64, 64, 0, stream>>>(cv, seq_lens, T, append_lens, skipped);
   } else {
     if (cv.fmt == KVQ_FMT_FP8_E4M3) {
       if (cv.bf16) per_token_d<KVQ_FMT_FP8_E4M3, true>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
@@ -749,7 +803,7 @@ hipError_t launch_append(const CacheView& cv, int32_t* seq_lens, const void* k_n
       if (cv.bf16) per_token_d<KVQ_FMT_INT8, true>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
       else per_token_d<KVQ_FMT_INT8, false>(cv, seq_lens, k_new, v_new, T, append_lens, stream);
     }
-    append_finish<false><<<cv.B, kThreads, 0, stream>>>(cv, seq_lens, k_new, v_new, T, append_lens, skipped);
+    append_finish<<<(cv.B + 63) / 64, 64, 0, stream>>>(cv, seq_lens, T, append_lens, skipped);
   }
   return hipGetLastError();
 }

@@ -173,6 +173,17 @@ __device__ __forceinline__ void run_minmax_keys(uint32_t& kmin, uint32_t& kmax) 
   }
 }
 
+// a / c for a >= 0 and a constant divisor c in [2^-60, 2^60] (a scale from a
+// range or an absolute maximum): the refined-reciprocal quotient where a is
+// zero or at least 2^-90 (a, the quotient and every residual stay normal),
+// a true division for the rest (lanes that take it branch around it).
+__device__ __forceinline__ float quot_nonneg(float a, float c, float rc) {
+  float q;
+  if (a == 0.0f || a >= 0x1p-90f) q = div_refined<false>(a, c, rc);
+  else q = a / c;
+  return q;
+}
+
 // The value of lane l ^ 2 (the other half of each quad).
 __device__ __forceinline__ uint32_t quad_swap2(uint32_t v) {
   return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x4e, 0xf, 0xf, false));
