@@ -1148,11 +1148,14 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
         tmax = fmaxf(tmax, x);
       }
     }
-    tmax = max_rows(tmax);
     // Lazy rescale: the running maximum moves only when a score exceeds it
     // by more than kLazyLog2, so the accumulators are rescaled on few tiles
-    // and every probability stays below 2^kLazyLog2.
+    // and every probability stays below 2^kLazyLog2. The four lanes of a
+    // column share m_run, so a lane's own maximum decides whether any column
+    // needs it; the column maximum across the lanes (two lane exchanges) is
+    // taken only on the tiles that rescale.
     if (__any(tmax > m_run + kLazyLog2)) {
+      tmax = max_rows(tmax);
       const float m_new = fmaxf(m_run, tmax);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
