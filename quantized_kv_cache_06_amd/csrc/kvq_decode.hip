@@ -24,16 +24,21 @@
 //    core exactly: E4M3 and INT8 codes convert to bf16 exactly; group-wise
 //    INT4 nibbles (code + 8) become the bf16 128 + nibble by OR-ing them
 //    under the bf16 pattern of 128 (136 * sum(q) comes off per channel
-//    group); KIVI codes become f16 code * 2^k by masking them in place under
-//    the f16 pattern of 1024 and subtracting 1024. Per-token scales multiply
-//    the finished scores; KIVI per-channel Key scales are folded into the
-//    query once per group (score = sum_c (q_c s_c) code_c + sum_c q_c z_c),
-//    with 2^-k taken into the query as well.
+//    group); KIVI codes are masked into bytes, where a byte holding
+//    c * 2^k (c * 2^k <= 15) is the E4M3 pattern of c * 2^(k-9), and the
+//    scaled FP8 conversion (scale 2^9) turns two such bytes into the f16
+//    pair c * 2^k exactly. Per-token scales multiply the finished scores;
+//    KIVI per-channel Key scales are folded into the query once per group
+//    (score = sum_c (q_c s_c) code_c + sum_c q_c z_c), with 2^-k taken into
+//    the query as well.
 //  softmax: running maximum and sum per head in the log2 domain (exp2).
 //  values (PV): O^T[d x 16] += V^T[d x 32] * P^T[32 x 16], again with the
 //    probabilities (times the per-token Value scale) split into bf16 hi and
-//    lo columns; the KIVI per-token zero-points add sum_t p_t z_t per channel
-//    group on the vector ALU.
+//    lo columns. Value codes enter as the bf16 128 + c * 2^k (masked in
+//    place under the bf16 pattern of 128; INT2 k = 0, 2 or 4 with 2^-k taken
+//    into the staged Value scale); a second product with the constant -128
+//    takes 128 * p' off in the same accumulator. The KIVI per-token
+//    zero-points add sum_t p_t z_t per channel group on the vector ALU.
 // The cache layout (include/kvq.h) is chosen so that every lane loads its
 // operand bytes with 16-byte loads and no shuffles: Key rows token-major,
 // Value words per channel in blocks of 8 (16 for INT2) tokens, channel words
@@ -118,14 +123,6 @@ __device__ __forceinline__ uint32_t pack_f16(float x0, float x1) {
 }
 __device__ __forceinline__ float f16_lo(uint32_t w) { return float(__builtin_bit_cast(f16x2_t, w)[0]); }
 __device__ __forceinline__ float f16_hi(uint32_t w) { return float(__builtin_bit_cast(f16x2_t, w)[1]); }
-
-// f16 pair holding 1024 + m (m the mantissa bits) minus 1024: exactly m.
-constexpr uint32_t kMagic1024 = 0x64006400u;  // two f16 1024.0
-__device__ __forceinline__ uint32_t f16_sub1024(uint32_t w) {
-  const f16x2_t x = __builtin_bit_cast(f16x2_t, w);
-  const f16x2_t y = x - f16x2_t{_Float16(1024.0f), _Float16(1024.0f)};
-  return __builtin_bit_cast(uint32_t, y);
-}
 
 // (x & m) | c in one instruction (a three-input bitwise op; its truth table
 // is f(0xF0, 0xCC, 0xAA) = (0xF0 & 0xCC) | 0xAA).
@@ -226,6 +223,14 @@ template <int SEL>
 __device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, SEL != 0));
 }
+// Bytes 2 SEL, 2 SEL + 1 of w as an f16 pair, exact, for bytes holding an
+// integer c in 0..15: such a byte is the E4M3 pattern of c * 2^-9 (the
+// subnormals 1..7 continue evenly into the first normal binade 8..15), and
+// the conversion's scale 2^9 restores c.
+template <int SEL>
+__device__ __forceinline__ uint32_t e4m3_pair_f16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 512.0f, SEL != 0));
+}
 // Signed INT8 byte pair to a bf16 pair, exact.
 template <int SEL>
 __device__ __forceinline__ uint32_t i8x2_bf16(uint32_t w) {
@@ -257,9 +262,14 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Channel of element i of k-step kk held by row group r in the score MFMA:
 // lanes of row group r hold the contiguous channels [CPL*r, CPL*(r+1)), CPL =
 // D/4, and element i of k-step kk is the following one of them.
-template <int BITS>
+// KIVI (KBYTE set) takes its Key codes in the order the byte-wise
+// conversion of key_operand produces them; group-wise INT4 pairs nibble j
+// with nibble j + 4.
+template <int BITS, bool KBYTE = false>
 __device__ __forceinline__ constexpr int cperm(int kk, int i) {
   if constexpr (BITS >= 8) return 8 * kk + i;
+  else if constexpr (BITS == 4 && KBYTE) return 8 * kk + 2 * (i & 3) + (i >> 2);
+  else if constexpr (BITS == 2 && KBYTE) return 16 * (kk >> 1) + 8 * (kk & 1) + (i >> 1) + 4 * (i & 1);
   else if constexpr (BITS == 4) return 8 * kk + (i >> 1) + 4 * (i & 1);
   else return 16 * (kk >> 1) + 4 * (kk & 1) + (i >> 1) + 8 * (i & 1);
 }
@@ -352,18 +362,15 @@ __device__ __forceinline__ void load_elems(const void* p, size_t i, float* x) {
 
 // Key operand (16 tokens x 32 channels) of k-step kk from the lane's raw
 // Key bytes. 8-bit codes: bf16, exact. KIVI codes: f16, each element exactly
-// code * 2^kfactor_log2(kk, i): the nibble (or 2-bit field) is masked in
-// place under the f16 pattern of 1024 and 1024 is subtracted, which is exact.
-// (Subnormal f16 codes would avoid the subtraction, but the matrix cores do
-// not accumulate products of subnormal inputs exactly.)
+// code * 2^kfactor_log2(i): the codes are masked into bytes (INT4: one
+// nibble per byte; INT2: the fields at bits 0-1 (x1) or 2-3 (x4) of each
+// byte) and two bytes at a time go through the scaled E4M3 conversion (see
+// e4m3_pair_f16). The f16 results are normal numbers or zero, which the
+// matrix cores multiply exactly.
 template <int BITS>
-__device__ __forceinline__ constexpr int kfactor_log2(int kk, int i) {
-  if constexpr (BITS == 4) {
-    return ((i >> 1) & 1) ? 4 : 0;
-  } else {
-    const int j = 4 * (kk & 1) + (i >> 1);
-    return j <= 4 ? 2 * j : 2 * (j - 5);
-  }
+__device__ __forceinline__ constexpr int kfactor_log2(int i) {
+  if constexpr (BITS == 4) return 0;
+  else return ((i >> 1) & 1) ? 2 : 0;
 }
 
 template <int FMT, int BITS>
@@ -387,22 +394,25 @@ __device__ __forceinline__ u32x4 key_operand(const uint32_t* kw, int kk) {
     a[2] = byte_pair_bf16<FMT, 0>(kw[2 * kk + 1]);
     a[3] = byte_pair_bf16<FMT, 1>(kw[2 * kk + 1]);
   } else if constexpr (BITS == 4) {
-    // pairs (nibble j, nibble j+4): j = 0, 2 at bits 0-3 (x1), j = 1, 3 at bits 4-7 (x16)
-    const uint32_t w = kw[kk], w8 = w >> 8;
-    a[0] = f16_sub1024(and_or(w, 0x000F000Fu, kMagic1024));
-    a[1] = f16_sub1024(and_or(w, 0x00F000F0u, kMagic1024));
-    a[2] = f16_sub1024(and_or(w8, 0x000F000Fu, kMagic1024));
-    a[3] = f16_sub1024(and_or(w8, 0x00F000F0u, kMagic1024));
+    // even nibbles one per byte, then the odd ones: pairs (0, 2), (4, 6),
+    // (1, 3), (5, 7) of the k-step's 8
+    const uint32_t w = kw[kk], ev = w & 0x0F0F0F0Fu, od = (w >> 4) & 0x0F0F0F0Fu;
+    a[0] = e4m3_pair_f16<0>(ev);
+    a[1] = e4m3_pair_f16<1>(ev);
+    a[2] = e4m3_pair_f16<0>(od);
+    a[3] = e4m3_pair_f16<1>(od);
   } else {
-    // pairs (code j, code j+8), j = 4*(kk&1) + e: fields j <= 4 at bits 2j
-    // (x4^j), fields 5..7 shifted down by 10 (x4^(j-5))
-    const uint32_t w = kw[kk >> 1], w10 = w >> 10;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = 4 * (kk & 1) + e;
-      const uint32_t src = j <= 4 ? w : w10;
-      const int sh = j <= 4 ? 2 * j : 2 * (j - 5);
-      a[e] = f16_sub1024(and_or(src, 0x00030003u << sh, kMagic1024));
+    // word kk/2 holds 16 codes, 4 per byte; field f of every byte (bits 0-1
+    // x1, 2-3 x4, then the same of w >> 4) gives the pairs (code f, code
+    // f + 4) of bytes 0-1 (even kk) or (code 8 + f, code 12 + f) of bytes 2-3
+    const uint32_t w = kw[kk >> 1], w4 = w >> 4;
+    const uint32_t f0 = w & 0x03030303u, f1 = w & 0x0C0C0C0Cu, f2 = w4 & 0x03030303u, f3 = w4 & 0x0C0C0C0Cu;
+    if (kk & 1) {
+      a[0] = e4m3_pair_f16<1>(f0); a[1] = e4m3_pair_f16<1>(f1);
+      a[2] = e4m3_pair_f16<1>(f2); a[3] = e4m3_pair_f16<1>(f3);
+    } else {
+      a[0] = e4m3_pair_f16<0>(f0); a[1] = e4m3_pair_f16<0>(f1);
+      a[2] = e4m3_pair_f16<0>(f2); a[3] = e4m3_pair_f16<0>(f3);
     }
   }
   return a;
@@ -431,10 +441,14 @@ __device__ __forceinline__ u32x4 value_operand(const uint32_t* vw, int mt, int r
 #pragma unroll
     for (int j = 0; j < 4; ++j) a[j] = and_or(w >> (4 * j), 0x000F000Fu, kMagic128);
   } else {
-    const uint32_t w = vw[mt];
-    const int sh = 8 * (r & 1);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) a[j] = and_or(w >> (sh + 2 * j), 0x00030003u, kMagic128);
+    // fields 0-2 of the lane's byte in place (x1, x4, x16), field 3 shifted
+    // down (x1); the Value scales of the tokens of pairs 1 and 2 are staged
+    // times 1/4 and 1/16
+    const uint32_t x = vw[mt] >> (8 * (r & 1));
+    a[0] = and_or(x, 0x00030003u, kMagic128);
+    a[1] = and_or(x, 0x000C000Cu, kMagic128);
+    a[2] = and_or(x, 0x00300030u, kMagic128);
+    a[3] = and_or(x >> 6, 0x00030003u, kMagic128);
   }
   return a;
 }
@@ -688,6 +702,7 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   // KIVI with binary16 metadata: the raw halves ride in the ring (two per
   // register) and are widened when the tile is processed
   constexpr bool M16 = FMT == KVQ_FMT_KIVI_F16;
+  constexpr bool KBYTE = KIVI;  // Key codes in the byte-wise conversion's order
   constexpr int CPL = D / 4;                  // channels per row group (score MFMA)
   // 8-bit codes at d = 128: row group r holds channels [16r, 16r+16) and
   // [64+16r, 64+16r+16), so each Key load instruction covers 64 contiguous
@@ -753,11 +768,11 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   f32x4 o[NMT];
 #pragma unroll
   for (int i = 0; i < NMT; ++i) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  // KIVI: per channel group, sum_t p_t (z_t + kCenter s_t): the zero-points
-  // plus the centre the Value codes are taken about in the matrix core
-  // (group-wise INT4: the codes are stored as code + 8, so the centre 8
-  // leaves exactly code * p')
-  constexpr float kCenter = INT4G ? 8.0f : BITS == 4 ? 7.0f : 1.0f;
+  // KIVI: per channel group, sum_t p_t z_t (the zero-points). The Value
+  // codes enter the matrix core as 128 + code, and a second product with
+  // the constant -(128 + kCenter) leaves code * p' (group-wise INT4: the
+  // codes are stored as code + 8, and the centre 8 takes that off too)
+  constexpr float kCenter = INT4G ? 8.0f : 0.0f;
   const uint32_t cpair = pack_bf16(-(128.0f + kCenter), -(128.0f + kCenter));
   const u32x4 kCenterA = {cpair, cpair, cpair, cpair};
   float zb[NVG];
@@ -951,7 +966,7 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
     for (int i = 0; i < EPT; ++i) sm.q[j][c + i] = j < g ? qx[i] : 0.0f;
     __syncthreads();
     const int kk0 = lo_col ? NKW : 0;
-    fbase = CPL * r + cperm<BITS>(kk0, 0);  // the lane's elements sit at fbase + cperm(kw, i)
+    fbase = CPL * r + cperm<BITS, KBYTE>(kk0, 0);  // the lane's elements sit at fbase + cperm(kw, i)
     float mx = 0.0f;
 #pragma unroll
     for (int kw = 0; kw < NKW; ++kw)
@@ -960,8 +975,8 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const int i = 2 * e + h2;
-          const float v = __builtin_amdgcn_ldexpf(sm.q[hh][fbase + cperm<BITS>(kw, i)],
-                                                  -kfactor_log2<BITS>(kk0 + kw, i));
+          const float v = __builtin_amdgcn_ldexpf(sm.q[hh][fbase + cperm<BITS, KBYTE>(kw, i)],
+                                                  -kfactor_log2<BITS>(i));
           qn[kw][e][h2] = v;
           mx = fmaxf(mx, fabsf(v));
         }
@@ -1028,9 +1043,16 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
     {
       const int part = lane >> 5, qi = lane & 31;
       float* mdst = (part ? meta1 : meta0) + qi * NVG;
+      // KIVI-2: token qi is element qi % 4 of its Value operand pair, whose
+      // codes enter the matrix core times 1, 4, 16 or 1
+      const float fq = (KIVI && BITS == 2 && part == 0) ? ((qi & 3) == 1 ? 0.25f : (qi & 3) == 2 ? 0.0625f : 1.0f)
+                                                        : 1.0f;
       if constexpr (M16) {
 #pragma unroll
-        for (int j = 0; j < NVG; ++j) mdst[j] = half_at(sl.mh, j);
+        for (int j = 0; j < NVG; ++j) mdst[j] = KIVI && BITS == 2 ? half_at(sl.mh, j) * fq : half_at(sl.mh, j);
+      } else if constexpr (KIVI && BITS == 2) {
+#pragma unroll
+        for (int j = 0; j < NVG; ++j) mdst[j] = sl.mw[j] * fq;
       } else if constexpr (SCALED) {
 #pragma unroll
         for (int j = 0; j < NVG; ++j) mdst[j] = sl.mw[j];
@@ -1074,7 +1096,7 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
         for (int kw = 0; kw < NKW; ++kw)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int oa = cperm<BITS>(kw, 2 * e), ob = cperm<BITS>(kw, 2 * e + 1);
+            const int oa = cperm<BITS, KBYTE>(kw, 2 * e), ob = cperm<BITS, KBYTE>(kw, 2 * e + 1);
             const float x0 = qn[kw][e][0] * ksr[oa];
             const float x1 = qn[kw][e][1] * ksr[ob];
             xh[kw][e] = pack_f16(x0, x1);
@@ -1246,7 +1268,7 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
             // (KIVI tiles are always whole)
             if constexpr (INT4G) pv[t][u] = tok<BITS>(t, r, ja + u) < valid ? ps[t][u] * vsc : 0.0f;
             else pv[t][u] = ps[t][u] * vsc;
-            if constexpr (KIVI) zs = fmaf(ps[t][u], fmaf(kCenter, vsc, vzf[t][u * NVG + jg]), zs);
+            if constexpr (KIVI) zs = fmaf(ps[t][u], vzf[t][u * NVG + jg], zs);
           }
         if constexpr (KIVI) zb[jg] += zs;
         const Split2 s0 = split_pair(pv[0][0], pv[1][0]);  // pair ja
@@ -1260,7 +1282,7 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
         for (int mt = jg * MPG; mt < (jg + 1) * MPG; ++mt) {
           o[mt] = mfma_bf16(value_operand<FMT, BITS>(vc, mt, r), bp, o[mt]);
           // the codes entered as 128 + code: take (128 + kCenter) * p' off
-          // in the same accumulator every tile, leaving (code - kCenter) * p'
+          // in the same accumulator every tile
           o[mt] = mfma_bf16(kCenterA, bp, o[mt]);
         }
       }
