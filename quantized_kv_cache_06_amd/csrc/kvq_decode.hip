@@ -722,6 +722,9 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   // here the same way)
   constexpr bool INT4G = FMT == KVQ_FMT_INT4 || FMT == KVQ_FMT_INT4_HADAMARD;
   constexpr bool ROT = FMT == KVQ_FMT_INT4_HADAMARD;
+  // KIVI and group-wise INT4: each lane takes the softmax of half of its
+  // column's scores (see the scores below)
+  constexpr bool HALF = KIVI || INT4G;
   constexpr int TB = BITS == 2 ? 16 : 8;      // tokens per Value block
   constexpr int VW = 16 / VWB;                // Value words per 16-byte load
   constexpr int NVL = D / (16 * VW);          // 16-byte Value loads per lane per tile
@@ -1144,10 +1147,18 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
         vs[t] = *reinterpret_cast<const f32x4*>(meta1 + tok<BITS>(t, r, 0));
       }
     }
+    // HALF: the hi and lo lanes of a head hold the same scores after the
+    // column sum; each lane keeps the half its Value operand pairs need
+    // (elements ja, ja + 1 of each score tile) and takes the softmax of
+    // those only
+    const int ja = lo_col ? 2 : 0;
+    const uint32_t lo_mask = lo_col ? 0xffffffffu : 0u;
+    constexpr int NSC = HALF ? 2 : 4;  // scores per score tile the lane keeps
     float sc[2][4];
     float tmax = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+      float xs[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float x;
@@ -1161,12 +1172,17 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
         } else {
           x = add_ror8(acc[t][0][j]);
         }
-        if constexpr (KIVI) x = fmaf(x, kscale, kbias);
-        else if constexpr (INT4G) (void)0;
+        if constexpr (KIVI || INT4G) (void)0;
         else if constexpr (SCALED) x = x * ks[t][j] * sm_log2;
         else x = x * sm_log2;
-        if (tok<BITS>(t, r, j) >= valid) x = -INFINITY;
-        sc[t][j] = x;
+        if (!KIVI && tok<BITS>(t, r, j) >= valid) x = -INFINITY;  // KIVI tiles are whole
+        xs[j] = x;
+      }
+#pragma unroll
+      for (int u = 0; u < NSC; ++u) {
+        float x = HALF ? select_bits(lo_mask, xs[2 + u], xs[u]) : xs[u];
+        if constexpr (KIVI) x = fmaf(x, kscale, kbias);
+        sc[t][u] = x;
         tmax = fmaxf(tmax, x);
       }
     }
@@ -1177,7 +1193,7 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
     // needs it; the column maximum across the lanes (two lane exchanges) is
     // taken only on the tiles that rescale.
     if (__any(tmax > m_run + kLazyLog2)) {
-      tmax = max_rows(tmax);
+      tmax = max_rows(HALF ? max_ror8(tmax) : tmax);
       const float m_new = fmaxf(m_run, tmax);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
@@ -1193,7 +1209,7 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NSC; ++j) {
         const float p = __builtin_amdgcn_exp2f(sc[t][j] - m_run);
         sc[t][j] = p;
         psum += p;
@@ -1220,13 +1236,7 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
       // Each takes two of the four operand pairs (pair k = tokens (0, k) and
       // (1, k) of the score tiles: the hi lane k = 0, 1, the lo lane k = 2,
       // 3), splits them into both terms, and the two lanes swap halves.
-      const int ja = lo_col ? 2 : 0;
-      const uint32_t lo_mask = lo_col ? 0xffffffffu : 0u;
-      float ps[2][2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) ps[t][u] = select_bits(lo_mask, sc[t][2 + u], sc[t][u]);
+      const float(&ps)[2][4] = sc;  // the lane's probabilities of pairs ja, ja + 1
       // per-token Value scale and zero of each channel group, for the lane's
       // two tokens of each score tile
       // KIVI: meta0 Value scales, meta1 Value zero-points; group-wise INT4:
@@ -1257,7 +1267,6 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
 #pragma unroll
       for (int jg = 0; jg < NVG; ++jg) {
         float pv[2][2];
-        float zs = 0.0f;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -1268,9 +1277,8 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
             // (KIVI tiles are always whole)
             if constexpr (INT4G) pv[t][u] = tok<BITS>(t, r, ja + u) < valid ? ps[t][u] * vsc : 0.0f;
             else pv[t][u] = ps[t][u] * vsc;
-            if constexpr (KIVI) zs = fmaf(ps[t][u], vzf[t][u * NVG + jg], zs);
+            if constexpr (KIVI) zb[jg] = fmaf(ps[t][u], vzf[t][u * NVG + jg], zb[jg]);
           }
-        if constexpr (KIVI) zb[jg] += zs;
         const Split2 s0 = split_pair(pv[0][0], pv[1][0]);  // pair ja
         const Split2 s1 = split_pair(pv[0][1], pv[1][1]);  // pair ja + 1
         u32x4 bp;
@@ -1309,7 +1317,7 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   }
 
   // ---- merge the 4 waves (and the new token) through LDS ----
-  const float l_tot = sum_rows(l_run);
+  const float l_tot = sum_rows(HALF ? add_ror8(l_run) : l_run);
   float zt[NVG];
 #pragma unroll
   for (int j = 0; j < NVG; ++j) zt[j] = sum_rows(add_ror8(zb[j]));  // hi and lo lanes hold disjoint tokens
