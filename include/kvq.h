@@ -243,8 +243,8 @@ int32_t kvq_quantize_append(const kvq_config* cfg, void* cache, int32_t* seq_len
  * the device. For split_tokens > 0 it holds n = ceil(max_tokens /
  * split_tokens) splits; for 0 it holds n = min(128, max(1, max_tokens /
  * 256)) splits, the most the library's choice can take on any device. The
- * workspace starts with batch * (n_kv_heads + 1) uint32 arrival counters
- * (see kvq_decode_attention for the zero-fill rule), then per (sequence,
+ * workspace starts with batch * (n_kv_heads + 1) + 1 uint32 counters (see
+ * kvq_decode_attention for the zero-fill rule), then per (sequence,
  * query head) n + 1 partial rows of head_dim + 2 fp32, each array 256-byte
  * aligned. kvq_append_decode takes the same workspace. Errors:
  * KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED (split_tokens not a positive
@@ -254,11 +254,12 @@ int32_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t split_tokens, 
 /* Single-token decode attention that reads the quantized cache directly and
  * dequantizes in registers ([DUP] "Key takeaways"; [N4N] Step 5: no separate
  * dequantize pass). Split-K over the token axis (flash-decoding): the
- * quantized tokens of each sequence are spread evenly over n splits (whole
- * 32-token tiles, whole groups for KIVI), each producing a partial softmax
- * state (running max, running sum, unnormalized output); the KIVI residual
- * window is one more split. The last split of each (sequence, kv head) to
- * finish merges them with the log-sum-exp rule. One launch.
+ * quantized tokens of each sequence are cut into n splits at fixed
+ * fractions of its length (whole 32-token tiles, whole groups for KIVI),
+ * each producing a partial softmax state (running max, running sum,
+ * unnormalized output); the KIVI residual window is one more split. The
+ * last split of each (sequence, kv head) to finish merges them with the
+ * log-sum-exp rule. One launch.
  *  cache        device, one layer's cache; read only.
  *  seq_lens     device int32 [B]; values are clamped to [0, max_tokens].
  *  q            device [B][Hq][d] in cfg->in_dtype (the new query token).
@@ -266,18 +267,20 @@ int32_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t split_tokens, 
  *  out          device fp32 [B][Hq][d], written.
  *  workspace    device scratch of at least kvq_decode_workspace_bytes(cfg,
  *               split_tokens) bytes. Its first batch * (n_kv_heads + 1)
- *               uint32 (the arrival counters) must be zero on entry: zero-fill the
+ *               + 1 uint32 (the counters) must be zero on entry: zero-fill the
  *               workspace once after allocating it (or when batch or
  *               n_kv_heads change); every call leaves them zero when it
  *               completes. The rest is scratch. Calls that overlap in time
  *               on one workspace race.
- *  split_tokens the longest split, a positive multiple of 64 giving at most
- *               128 splits of max_tokens: n = ceil(max_tokens /
- *               split_tokens). 0 = the library's choice: for FP8 and INT8,
- *               about two workgroups per compute unit in one round; for
- *               KIVI, about four rounds of the device's resident
- *               workgroups; within the bound kvq_decode_workspace_bytes
- *               gives.
+ *  split_tokens a positive multiple of 64 giving at most 128 splits of
+ *               max_tokens: n = ceil(max_tokens / split_tokens) equal
+ *               splits of each sequence. 0 = the library's choice, within
+ *               the bound kvq_decode_workspace_bytes gives: for FP8, INT8
+ *               and the other per-token formats, equal splits for about two
+ *               workgroups per compute unit in one round; for KIVI, about
+ *               four rounds of the device's resident workgroups, cut into
+ *               large, then medium, then small splits that go out to the
+ *               workgroups in that order as they free up.
  * Errors: KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE,
  * KVQ_ERR_HIP. */
 int32_t kvq_decode_attention(const kvq_config* cfg, const void* cache, const int32_t* seq_lens,
@@ -337,7 +340,7 @@ int32_t kvq_append_decode(const kvq_config* cfg, void* cache, int32_t* seq_lens,
  * skipped and out are bit for bit those of kvq_append_decode.
  *  Arguments: as kvq_append_decode, without workspace and workspace_bytes.
  *  Limit: the call's workspace (kvq_decode_workspace_bytes' layout for the
- *         planned number of splits: batch * (n_kv_heads + 1) counters, then
+ *         planned number of splits: batch * (n_kv_heads + 1) + 1 counters, then
  *         batch * n_q_heads * (splits + 1) partial rows of head_dim + 2
  *         fp32, each array 256-byte aligned) must fit
  *         KVQ_STATIC_WORKSPACE_BYTES; otherwise the call

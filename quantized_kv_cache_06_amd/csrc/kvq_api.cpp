@@ -7,6 +7,33 @@
 #include "kvq.h"
 #include "kvq_internal.h"
 
+// Decode plan constants for KIVI (see plan_for): n = KVQ_PLAN_ROUNDS
+// rounds of the resident workgroups; of the n chunks of a pair, n /
+// KVQ_PLAN_DIV3 are small (weight KVQ_PLAN_W3), n / KVQ_PLAN_DIV2 medium
+// (KVQ_PLAN_W2) and the rest large (KVQ_PLAN_W1). For the long-context INT4
+// workload (n = 24) that is 15 chunks of 6.1 % of the pair, 3 of 2.0 % and
+// 6 of 0.5 %. Measured on MI355X against equal static splits: 349-351
+// against 356-359 us per decode call; the same weights with 5 rounds, with
+// 8 small chunks, or with large chunks of weight 16 all measured 350-354.
+#ifndef KVQ_PLAN_W1
+#define KVQ_PLAN_W1 12
+#endif
+#ifndef KVQ_PLAN_W2
+#define KVQ_PLAN_W2 4
+#endif
+#ifndef KVQ_PLAN_W3
+#define KVQ_PLAN_W3 1
+#endif
+#ifndef KVQ_PLAN_DIV2
+#define KVQ_PLAN_DIV2 8
+#endif
+#ifndef KVQ_PLAN_DIV3
+#define KVQ_PLAN_DIV3 4
+#endif
+#ifndef KVQ_PLAN_ROUNDS
+#define KVQ_PLAN_ROUNDS 4
+#endif
+
 namespace {
 
 constexpr int kVersion = 100;  // 0.1.0
@@ -14,6 +41,8 @@ constexpr int64_t kMaxTokens = int64_t(1) << 24;
 constexpr int kMaxResidual = 4096;
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+bool kivi_fmt(const kvq_config* c) { return c->format == KVQ_FMT_KIVI || c->format == KVQ_FMT_KIVI_F16; }
 
 int32_t validate(const kvq_config* c) {
   if (!c) return KVQ_ERR_INVALID;
@@ -25,8 +54,11 @@ int32_t validate(const kvq_config* c) {
   if (c->head_dim != 64 && c->head_dim != 128) return KVQ_ERR_UNSUPPORTED;
   const int g = c->n_q_heads / c->n_kv_heads;
   if (g > 8) return KVQ_ERR_UNSUPPORTED;
-  // Batch and KV heads index grid dimensions y and z (at most 65535 each).
+  // Batch and KV heads index grid dimensions y and z of the append kernels
+  // (at most 65535 each); the decode numbers its work items (at most 129
+  // per (sequence, kv head) pair) in 32 bits.
   if (c->batch > 65535 || c->n_kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
+  if (int64_t(c->batch) * c->n_kv_heads > (int64_t(1) << 24)) return KVQ_ERR_UNSUPPORTED;
   switch (c->format) {
     case KVQ_FMT_FP8_E4M3:
     case KVQ_FMT_FP8_STATIC:
@@ -146,23 +178,53 @@ int auto_split_bound(const kvq_config* c) {
   return int(n);
 }
 
-// Automatic split count for a device with `cus` compute units that holds
-// `resident` decode workgroups at once, within [1, auto_split_bound()].
-// The per-token formats stream at the memory bound in one round of two
-// workgroups per compute unit: a third co-resident workgroup gets the least
-// of the unit's memory issue (the oldest waves are served first) and ends
-// the launch late, and each further round adds a prologue and a tail.
-// KIVI's decode is bound by vector-ALU work, where about four rounds of
-// residency let workgroups in different phases (loads, group folds,
-// epilogue) share a compute unit.
-int auto_split(const kvq_config* c, int64_t resident, int64_t cus) {
+// The decode plan: how each (sequence, kv head) pair's quantized tokens are
+// cut into chunks, and whether the chunks go out through the item counter.
+//  - split_tokens > 0: n = ceil(max_tokens / split_tokens) equal chunks,
+//    workgroup x takes item x.
+//  - FP8, INT8 and the other per-token formats (split_tokens == 0): n equal
+//    chunks for about two workgroups per compute unit in one round. They
+//    stream at the memory bound; a third co-resident workgroup gets the
+//    least of the unit's memory issue (the oldest waves are served first)
+//    and ends the launch late, and each further round adds a prologue and a
+//    tail.
+//  - KIVI (split_tokens == 0): about four rounds of the device's resident
+//    workgroups (workgroups in different phases, loads, group folds and
+//    epilogue, share a compute unit), as large chunks, then medium and small
+//    ones, handed out in that order through the item counter. Equal static
+//    splits end at very different times: co-resident workgroups do not get
+//    equal shares of a unit's memory issue, and each XCD runs its own share
+//    of the grid. The small chunks at the end fill whichever units finish
+//    early.
+// n stays within [1, auto_split_bound()] for split_tokens == 0.
+struct Plan {
+  int n1, w1, n2, w2, n3, w3;  // chunk counts and weights of the three phases
+  int dynamic;
+};
+
+Plan plan_for(const kvq_config* c, int32_t split_tokens, int64_t resident, int64_t cus) {
+  Plan p{0, 1, 0, 1, 0, 1, 0};
+  if (split_tokens > 0) {
+    p.n1 = int((int64_t(c->max_tokens) + split_tokens - 1) / split_tokens);
+    return p;
+  }
   const int64_t pairs = int64_t(c->batch) * c->n_kv_heads;
-  const bool kivi = c->format == KVQ_FMT_KIVI || c->format == KVQ_FMT_KIVI_F16;
-  int64_t n = kivi ? 4 * resident / pairs : 2 * cus / pairs;
+  int64_t n = kivi_fmt(c) ? KVQ_PLAN_ROUNDS * resident / pairs : 2 * cus / pairs;
   const int bound = auto_split_bound(c);
   if (n < 1) n = 1;
   if (n > bound) n = bound;
-  return int(n);
+  if (!kivi_fmt(c)) {
+    p.n1 = int(n);
+    return p;
+  }
+  p.n3 = int(n) / KVQ_PLAN_DIV3;
+  p.n2 = int(n) / KVQ_PLAN_DIV2;
+  p.n1 = int(n) - p.n2 - p.n3;
+  p.w1 = KVQ_PLAN_W1;
+  p.w2 = KVQ_PLAN_W2;
+  p.w3 = KVQ_PLAN_W3;
+  p.dynamic = 1;
+  return p;
 }
 
 // Quantized splits per sequence the workspace must hold: ceil(max_tokens /
@@ -180,12 +242,13 @@ int32_t split_bound(const kvq_config* c, int32_t split_tokens, int* n) {
   return KVQ_OK;
 }
 
-// Workspace: [B][Hkv] uint32 arrival counters and [B] per-sequence counters
-// (fused calls) first (they must read zero on entry; each call leaves them
-// zero), then the partial states o, m, l.
-uint64_t counter_bytes(const kvq_config* c) {
-  return align256((uint64_t(c->batch) * c->n_kv_heads + uint64_t(c->batch)) * 4);
+// Workspace: [B][Hkv] uint32 arrival counters, [B] per-sequence counters
+// (fused calls) and the work-item counter first (they must read zero on
+// entry; each call leaves them zero), then the partial states o, m, l.
+uint64_t counter_words(const kvq_config* c) {
+  return uint64_t(c->batch) * c->n_kv_heads + uint64_t(c->batch) + 1;
 }
+uint64_t counter_bytes(const kvq_config* c) { return align256(counter_words(c) * 4); }
 
 uint64_t workspace_bytes(const kvq_config* c, int S) {
   const uint64_t rows = uint64_t(c->batch) * c->n_q_heads * S;
@@ -223,19 +286,18 @@ int32_t decode_call(const kvq_config* cfg, const void* cache, const int32_t* seq
   kvq_layout lay;
   make_layout(cfg, &lay);
   const kvq::CacheView v = make_view(cfg, lay, cache);
-  if (split_tokens == 0) {
-    const int resident = kvq::decode_resident_workgroups(v);
-    const int cus = kvq::decode_compute_units();
-    if (resident <= 0 || cus <= 0) return KVQ_ERR_HIP;
-    n = auto_split(cfg, resident, cus);
-  }
+  const int resident = kvq::decode_resident_workgroups(v);
+  const int cus = kvq::decode_compute_units();
+  if (resident <= 0 || cus <= 0) return KVQ_ERR_HIP;
+  const Plan plan = plan_for(cfg, split_tokens, resident, cus);
+  n = plan.n1 + plan.n2 + plan.n3;
   const int S = n + 1;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (fixed_ws) {
     if (workspace_bytes(cfg, S) > kvq::kStaticWorkspaceBytes) return KVQ_ERR_WORKSPACE;
     if (kvq::static_workspace(&workspace) != hipSuccess) return KVQ_ERR_HIP;
     // the array keeps the last call's contents: clear the arrival counters
-    const int words = int((uint64_t(cfg->batch) * cfg->n_kv_heads + uint64_t(cfg->batch)));
+    const int words = int(counter_words(cfg));
     if (kvq::launch_clear_words(static_cast<uint32_t*>(workspace), words, hs) != hipSuccess) return KVQ_ERR_HIP;
   }
   const uint64_t rows = uint64_t(cfg->batch) * cfg->n_q_heads * S;
@@ -243,11 +305,20 @@ int32_t decode_call(const kvq_config* cfg, const void* cache, const int32_t* seq
   kvq::DecodeWork work;
   work.count = reinterpret_cast<uint32_t*>(w);
   work.bcount = work.count + uint64_t(cfg->batch) * cfg->n_kv_heads;
+  work.queue = work.bcount + cfg->batch;
   w += counter_bytes(cfg);
   work.o = reinterpret_cast<float*>(w);
   work.m = reinterpret_cast<float*>(w + align256(rows * cfg->head_dim * 4));
   work.l = reinterpret_cast<float*>(w + align256(rows * cfg->head_dim * 4) + align256(rows * 4));
   work.S = S;
+  work.n1 = plan.n1;
+  work.w1 = plan.w1;
+  work.n2 = plan.n2;
+  work.w2 = plan.w2;
+  work.n3 = plan.n3;
+  work.w3 = plan.w3;
+  work.nitems = int(int64_t(cfg->batch) * cfg->n_kv_heads * (n + (kivi_fmt(cfg) ? 1 : 0)));
+  work.dynamic = plan.dynamic;
   const hipError_t e = kvq::launch_decode(v, seq_lens, q, sm_scale, out, work, app, hs);
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }

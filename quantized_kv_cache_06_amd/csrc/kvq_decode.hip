@@ -11,9 +11,10 @@
 //
 // How the work maps onto CDNA4
 // ----------------------------
-// One workgroup (4 waves) per (split, kv head, sequence); each wave owns a
-// contiguous run of 32-token tiles of the split and keeps its own online
-// softmax state; the waves are merged through LDS at the end. Per tile:
+// One workgroup (4 waves) per work item, a split of one (kv head,
+// sequence) pair (see decode_item); each wave owns a contiguous run of
+// 32-token tiles of the split and keeps its own online softmax state; the
+// waves are merged through LDS at the end. Per tile:
 //
 //  scores (QK): S^T[32 tokens x 16 cols] = K[32 x d] * Qt[d x 16] with
 //    v_mfma_f32_16x16x32_bf16 (KIVI: _f16). Column c = 8 * term + head:
@@ -1578,19 +1579,24 @@ __device__ __forceinline__ void split_residual(const CacheView& cv, int b, int h
   }
 }
 
-// Grid (S, Hkv, B). Slot s < S-1 covers quantized tokens [s*L, (s+1)*L);
-// slot S-1 covers the KIVI residual ring. A workgroup whose slot holds
-// tokens writes its partial state and takes a ticket from the (sequence, kv
-// head) counter; the workgroup that finishes last merges every partial of the
-// g query heads by the log-sum-exp rule, writes the normalized output and
-// resets the counter to zero. Slots with no tokens return at once; an empty
-// sequence gets zeros from slot 0.
-// Three resident workgroups per compute unit (12 waves, at most 168
-// registers per lane) measure fastest: more loads in flight per unit. KIVI
-// INT4 with groups of 32 at d = 128 needs a few more registers and keeps two.
-template <int FMT, int BITS, int D, int G, bool FUSED>
+// Work items. Each (sequence, kv head) pair's quantized tokens are cut into
+// NC chunks (whole 32-token tiles, whole groups for KIVI) at fixed fractions
+// of its length: n1 chunks of weight w1, then n2 of weight w2, then n3 of
+// weight w3, so that (with decreasing weights) the later chunks are smaller.
+// A KIVI pair has one more item, its residual window (slot NC). The items
+// are numbered residual items first, then the first-phase chunks of every
+// pair, the second, the third (pair by pair within a phase); one workgroup
+// runs each (see decode_split for the order they go out in). Every item
+// writes its partial state (an empty range writes an empty state) and takes
+// a ticket from its pair's counter; the item that finishes last merges the
+// pair's NC (+1) partial states of the g query heads by the log-sum-exp
+// rule, writes the normalized output and resets the counter to zero.
+template <int FMT, int BITS, int D, int G, bool FUSED, bool BF16>
 constexpr int min_wg_per_cu() {
   if constexpr (KVQ_DECODE_MIN_WG_PER_CU > 0) return KVQ_DECODE_MIN_WG_PER_CU;
+  // the fused INT2 KIVI step with fp32 inputs at d = 128 (its flush path
+  // quantizes the completed group from fp32 rows) needs a few registers more
+  if constexpr ((FMT == KVQ_FMT_KIVI || FMT == KVQ_FMT_KIVI_F16) && BITS == 2 && D == 128 && FUSED && !BF16) return 2;
   // INT2 KIVI with binary16 metadata at G = 32, d = 128 (a Key fold every
   // tile plus the half widening; the fused step also the flush path) needs
   // a few registers more than three workgroups per unit leave
@@ -1600,30 +1606,74 @@ constexpr int min_wg_per_cu() {
                                                                                                         : 3;
 }
 
+// Chunk j's first unit of nu units (j = NC gives nu): nu times the weight of
+// the chunks before j, over the total weight.
+__device__ __forceinline__ int chunk_start(const DecodeWork& wk, int j, int nu) {
+  int c;
+  if (j <= wk.n1) c = j * wk.w1;
+  else if (j <= wk.n1 + wk.n2) c = wk.n1 * wk.w1 + (j - wk.n1) * wk.w2;
+  else c = wk.n1 * wk.w1 + wk.n2 * wk.w2 + (j - wk.n1 - wk.n2) * wk.w3;
+  const int wt = wk.n1 * wk.w1 + wk.n2 * wk.w2 + wk.n3 * wk.w3;
+  return int(int64_t(nu) * c / wt);
+}
+
+// Partial state of an empty piece: output 0, maximum -inf, sum 0.
+template <int D>
+__device__ __forceinline__ void put_empty_partial(const CacheView& cv, const DecodeWork& wk, int b, int h, int s) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e < cv.g * D; e += kThreads) {
+    const int j = e / D, c = e % D;
+    put_partial(&wk.o[partial_row(cv, wk, b, h, j, s) * D + c], 0.0f);
+  }
+  if (tid < cv.g) {
+    const size_t row = partial_row(cv, wk, b, h, tid, s);
+    put_partial(&wk.m[row], -INFINITY);
+    put_partial(&wk.l[row], 0.0f);
+  }
+}
+
+// What an item needs after its token loop, parked in LDS so that it does
+// not hold scalar registers through the loop.
+struct ItemTail {
+  int b, h, n;
+  int app;
+};
+
+// One work item: item i (numbered as above) of the P = B * Hkv pairs.
 template <int FMT, int BITS, int D, int G, bool BF16, bool FUSED>
-__global__ __launch_bounds__(kThreads, (min_wg_per_cu<FMT, BITS, D, G, FUSED>())) void decode_split(CacheView cv, const int32_t* seq_lens,
-                                                        const void* __restrict__ q, float sm_log2, float* __restrict__ out,
-                                                        DecodeWork wk, AppendIn ap) {
+__device__ __forceinline__ void decode_item(const CacheView& cv, const int32_t* seq_lens, const void* __restrict__ q,
+                                            int lens, float sm_log2, float* __restrict__ out,
+                                            const DecodeWork& wk, const AppendIn& ap, int i, float* smem,
+                                            uint32_t& ticket, ItemTail& tail) {
   constexpr bool KIVI = FMT == KVQ_FMT_KIVI || FMT == KVQ_FMT_KIVI_F16;
-  __shared__ float smem[smem_floats<D, (KIVI ? G : 0), FUSED>()];
-  __shared__ uint32_t ticket;
-  // What a fused call needs after the token loop is parked in LDS, so that
-  // it does not hold scalar registers through the loop.
-  struct FusedTail {
-    int32_t* seq_lens;
-    uint32_t* bcount;
-    int n, hkv;
-    uint32_t last;  // ticket of the workgroup that merges
-    int every;
-  };
-  __shared__ FusedTail tail;
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int g = cv.g;
+  const int P = cv.B * cv.Hkv;
+  const int NC = wk.n1 + wk.n2 + wk.n3;  // = S - 1
+  int pair, s;
+  if (KIVI && i < P) {
+    pair = i;
+    s = NC;
+  } else {
+    if (KIVI) i -= P;
+    if (i < P * wk.n1) {
+      pair = i / wk.n1;
+      s = i % wk.n1;
+    } else if ((i -= P * wk.n1) < P * wk.n2) {
+      pair = i / wk.n2;
+      s = wk.n1 + i % wk.n2;
+    } else {
+      i -= P * wk.n2;
+      pair = i / wk.n3;
+      s = wk.n1 + wk.n2 + i % wk.n3;
+    }
+  }
+  const int b = pair / cv.Hkv, h = pair % cv.Hkv;
   // Tokens in the cache, and for a fused step whether this sequence takes
   // the new token (the append's rule: a valid length with room for one more;
   // otherwise the sequence is left unchanged and attention reads it as is).
-  const int raw = seq_lens[b];
+  // lens: lane l holds seq_lens[l] for l < min(B, 64)
+  const int raw = b < kWave ? __builtin_amdgcn_readlane(lens, b) : seq_lens[b];
   bool app = false;
   if constexpr (FUSED) app = raw >= 0 && raw < cv.max_tokens;
   if constexpr (FUSED) {
@@ -1631,75 +1681,54 @@ __global__ __launch_bounds__(kThreads, (min_wg_per_cu<FMT, BITS, D, G, FUSED>())
   }
   const int n_cache = min(max(raw, 0), cv.max_tokens);
   const int n = n_cache + (app ? 1 : 0);  // tokens attended
-  // quantized tokens the splits read (KIVI: the new token, and a group it
-  // completes, are handled by the residual slot)
+  // quantized tokens the chunks read (KIVI: the new token, and a group it
+  // completes, are handled by the residual item)
   const int nq = KIVI ? kivi_quantized(n_cache, G, cv.R) : n_cache;
-  // This sequence's quantized tokens spread evenly over the S - 1 split
-  // slots, in whole tiles (whole groups for KIVI, so that a Key group never
-  // straddles two splits).
-  constexpr int kUnit = KIVI ? G : kTile;
-  const int per = (nq + wk.S - 2) / (wk.S - 1);
-  const int len = (per + kUnit - 1) / kUnit * kUnit;
-  int nsq = len > 0 ? (nq + len - 1) / len : 0;
-  // fused step of a per-token format: split 0 also takes the new token (for an empty
-  // sequence, split 0 holds it alone)
-  const int t_new = (FUSED && !KIVI && app) ? n_cache : -1;
-  if (t_new >= 0 && nsq == 0) nsq = 1;
-  // slot S-1: the KIVI residual window
-  const bool extra = KIVI && n > nq;
-  const int nact = nsq + (extra ? 1 : 0);
-  // A fused step advances seq_lens[b] inside this launch, so every
-  // workgroup of the sequence (also one with no tokens) takes a ticket: the
-  // last merge of the sequence then knows that all of them have read it.
-  const bool every = FUSED && app;
-  if constexpr (FUSED) {
-    if (tid == 0) tail = {ap.seq_lens, wk.bcount, n, cv.Hkv, uint32_t(every ? int(gridDim.x) - 1 : nact - 1), every};
-  }
-  if (nact == 0) {
-    if (s == 0)
-      for (int e = tid; e < g * D; e += kThreads) out[(size_t(b) * cv.Hq + size_t(h) * g) * D + e] = 0.0f;
-    return;
-  }
-  if (s == wk.S - 1) {
-    if (!extra) {
-      if (!every) return;
-    } else if constexpr (KIVI) {
-      split_residual<D, BF16, BITS, G, FUSED, FMT == KVQ_FMT_KIVI_F16>(cv, b, h, s, nq, n, q, sm_log2, wk,
-                                              *reinterpret_cast<SmemResidT<D, G, FUSED>*>(smem), ap, app);
+  if (tid == 0) tail = {b, h, n, app ? 1 : 0};
+  if (s == NC) {
+    // the KIVI residual window
+    if constexpr (KIVI) {
+      if (n > nq)
+        split_residual<D, BF16, BITS, G, FUSED, FMT == KVQ_FMT_KIVI_F16>(
+            cv, b, h, s, nq, n, q, sm_log2, wk, *reinterpret_cast<SmemResidT<D, G, FUSED>*>(smem), ap, app);
+      else
+        put_empty_partial<D>(cv, wk, b, h, s);
     }
-  } else if (s >= nsq) {
-    if (!every) return;
   } else {
-    const int t0 = s * len;
-    const int t1 = min(t0 + len, nq);
+    // chunk s in whole tiles (whole groups for KIVI, so that a Key group
+    // never straddles two chunks); a fused step of a per-token format also
+    // takes the new token in chunk 0
+    constexpr int kUnit = KIVI ? G : kTile;
+    const int nu = (nq + kUnit - 1) / kUnit;
+    const int t0 = min(chunk_start(wk, s, nu) * kUnit, nq);
+    const int t1 = min(chunk_start(wk, s + 1, nu) * kUnit, nq);
+    const int t_new = (FUSED && !KIVI && app && s == 0) ? n_cache : -1;
     split_quantized<FMT, BITS, D, G, BF16, FUSED>(cv, b, h, s, t0, t1, q, sm_log2, wk,
-                                                  *reinterpret_cast<SmemQuant<D>*>(smem), s == 0 ? t_new : -1, ap);
+                                                  *reinterpret_cast<SmemQuant<D>*>(smem), t_new, ap);
   }
 
-  // ---- arrival: the last workgroup of this (sequence, kv head) merges ----
-  const size_t pair = pair_index(cv, b, h);
+  // ---- arrival: the last item of this (sequence, kv head) merges ----
   __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed ...
   __syncthreads();                 // ... for every thread, before the ticket is taken
-  if (tid == 0) ticket = __hip_atomic_fetch_add(&wk.count[pair], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const ItemTail it = tail;
+  const size_t pr = pair_index(cv, it.b, it.h);
+  if (tid == 0) ticket = __hip_atomic_fetch_add(&wk.count[pr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  uint32_t last;
-  if constexpr (FUSED) last = tail.last;
-  else last = uint32_t(nact - 1);
-  if (ticket != last) return;
+  const int nact = NC + (KIVI ? 1 : 0);  // pieces per pair, every one with a partial state
+  if (ticket != uint32_t(nact - 1)) return;
 
   // Merge by the log-sum-exp rule. Thread (j, c4) owns channels [4 c4,
   // 4 c4 + 4) of head j. For up to kMergeBatch pieces at a time it loads,
   // in one batch of coherent loads, its 16 bytes of every piece's partial
   // output and the piece's (max, sum) of head j, and folds them into a
   // running (max, sum, output); at most kMergeBatch pieces merge in one
-  // round trip, with no barrier. nact <= kMaxSplits + 1.
+  // round trip, with no barrier. Piece k is partial slot k.
   constexpr int kMergeBatch = 16;
   constexpr int C4 = D / 4;
-  auto slot = [&](int k) { return k < nsq ? k : wk.S - 1; };
   const int tm = fresh(tid);
   const int j = tm / C4, c4 = tm % C4;
   const int jc = min(j, g - 1);
-  const size_t row0 = partial_row(cv, wk, b, h, 0, 0);
+  const size_t row0 = partial_row(cv, wk, it.b, it.h, 0, 0);
   const size_t mrow = row0 + size_t(jc) * wk.S;
   const __amdgpu_buffer_rsrc_t orsrc = buffer_rsrc(wk.o + row0 * D, uint32_t(g * wk.S * D * 4));
   const uint32_t obase = uint32_t((size_t(jc) * wk.S * D + 4 * c4) * 4);
@@ -1711,7 +1740,7 @@ __global__ __launch_bounds__(kThreads, (min_wg_per_cu<FMT, BITS, D, G, FUSED>())
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
       if (k0 + u < nact) {
-        const int sl = slot(k0 + u);
+        const int sl = k0 + u;
         ov[u] = get_partial4(orsrc, obase + uint32_t(sl * D * 4));
         mv[u] = get_partial(&wk.m[mrow + sl]);
         lv[u] = get_partial(&wk.l[mrow + sl]);
@@ -1738,23 +1767,55 @@ __global__ __launch_bounds__(kThreads, (min_wg_per_cu<FMT, BITS, D, G, FUSED>())
     }
   }
   if (j < g)
-    *reinterpret_cast<f32x4*>(&out[(size_t(b) * cv.Hq + size_t(h) * g + j) * D + 4 * c4]) =
+    *reinterpret_cast<f32x4*>(&out[(size_t(it.b) * cv.Hq + size_t(it.h) * g + j) * D + 4 * c4]) =
         acc * (L > 0.0f ? 1.0f / L : 0.0f);
   if (tid == 0) {
-    __hip_atomic_store(&wk.count[pair], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&wk.count[pr], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if constexpr (FUSED) {
-      const FusedTail ft = tail;
-      if (ft.every) {
-        // the last (sequence, kv head) merge of sequence b: every workgroup
-        // of the sequence has read seq_lens[b]
-        const uint32_t done = __hip_atomic_fetch_add(&ft.bcount[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (done == uint32_t(ft.hkv - 1)) {
-          __hip_atomic_store(&ft.bcount[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          ft.seq_lens[b] = ft.n;
+      if (it.app) {
+        // the last (sequence, kv head) merge of sequence b: every item of
+        // the sequence has read seq_lens[b]
+        const uint32_t done = __hip_atomic_fetch_add(&wk.bcount[it.b], 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        if (done == uint32_t(cv.Hkv - 1)) {
+          __hip_atomic_store(&wk.bcount[it.b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ap.seq_lens[it.b] = it.n;
         }
       }
     }
   }
+}
+
+// One workgroup per work item. With wk.dynamic the items go out in the
+// order the workgroups draw numbers from wk.queue (not their launch index):
+// a unit that frees a slot early gets the next item of the list, whichever
+// XCD it is on (each XCD launches its own share of the grid). The workgroup
+// that draws the last number (nitems - 1) resets the counter for the next
+// call. Otherwise workgroup x takes item x. The sequence lengths (up to 64
+// of them) are loaded in the same round trip as the number.
+template <int FMT, int BITS, int D, int G, bool BF16, bool FUSED>
+__global__ __launch_bounds__(kThreads, (min_wg_per_cu<FMT, BITS, D, G, FUSED, BF16>())) void decode_split(
+    CacheView cv, const int32_t* seq_lens, const void* __restrict__ q, float sm_log2, float* __restrict__ out,
+    DecodeWork wk, AppendIn ap) {
+  constexpr bool KIVI = FMT == KVQ_FMT_KIVI || FMT == KVQ_FMT_KIVI_F16;
+  __shared__ float smem[smem_floats<D, (KIVI ? G : 0), FUSED>()];
+  __shared__ uint32_t ticket, item_sh;
+  __shared__ ItemTail tail;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int lens = lane < cv.B ? seq_lens[lane] : 0;
+  int item = blockIdx.x;
+  if (wk.dynamic) {
+    if (tid == 0) {
+      const uint32_t it = __hip_atomic_fetch_add(wk.queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (it == uint32_t(wk.nitems - 1)) __hip_atomic_store(wk.queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // a counter that was not zero on entry (a broken workspace contract)
+      // still yields item numbers in range
+      item_sh = it % uint32_t(wk.nitems);
+    }
+    __syncthreads();
+    item = __builtin_amdgcn_readfirstlane(int(item_sh));
+  }
+  decode_item<FMT, BITS, D, G, BF16, FUSED>(cv, seq_lens, q, lens, sm_log2, out, wk, ap, item, smem, ticket, tail);
 }
 
 // One kernel instantiation per (format, bits, head_dim, group, input type).
@@ -1820,8 +1881,7 @@ hipError_t launch_decode(const CacheView& cv, const int32_t* seq_lens, const voi
   const AppendIn ap = app ? *app : AppendIn{nullptr, nullptr, nullptr};
   visit_variant(cv, [&](auto v) {
     using V = decltype(v);
-    // slot S-1 (the KIVI residual window)
-    const dim3 grid(V::FMT == KVQ_FMT_KIVI || V::FMT == KVQ_FMT_KIVI_F16 ? work.S : work.S - 1, cv.Hkv, cv.B);
+    const dim3 grid(unsigned(work.nitems));  // one workgroup per item
     if (app)
       decode_split<V::FMT, V::BITS, V::D, V::G, V::BF16, true><<<grid, kThreads, 0, stream>>>(
           cv, ap.seq_lens, q, sm_log2, out, work, ap);

@@ -40,10 +40,16 @@ constexpr int kMaxDecodeSplits = 128;
 struct DecodeWork {
   uint32_t* count;  // [B][Hkv] partials finished in this call (zero between calls)
   uint32_t* bcount; // [B] (sequence, kv head) merges finished in a fused call (zero between calls)
+  uint32_t* queue;  // [1] work items handed out in this call (zero between calls)
   float* o;         // [B][Hq][S][D] unnormalized partial outputs
   float* m;         // [B][Hq][S] running maxima (log2 domain)
   float* l;         // [B][Hq][S] running sums
-  int S;            // split slots per (b, q head): S - 1 quantized splits + 1
+  int S;            // partial slots per (b, q head): S - 1 quantized chunks + the KIVI residual
+  // chunks of a pair's quantized tokens: n1 of weight w1, n2 of weight w2,
+  // n3 of weight w3 (n1 + n2 + n3 = S - 1, n1 >= 1)
+  int n1, w1, n2, w2, n3, w3;
+  int nitems;       // work items (one workgroup each): B * Hkv * (S - 1), plus B * Hkv for KIVI
+  int dynamic;      // 1: items are handed out through queue; 0: workgroup x takes item x
 };
 
 // skipped: NULL, or [B] set to 1 for each sequence the append leaves

@@ -215,14 +215,14 @@ def test_append_decode_argument_errors_need_no_gpu():
 
 
 def test_workspace_grows_with_split_count():
-    """Workspace = [B][Hkv] + [B] uint32 arrival counters, then partial (o, m, l)
+    """Workspace = [B][Hkv] + [B] + 1 uint32 counters, then partial (o, m, l)
     rows for every split slot; at most 128 quantized splits per sequence."""
     cfg = _cfg(WORKLOADS[4])
     small = kvq.kvq_decode_workspace_bytes(cfg, 4096)
     big = kvq.kvq_decode_workspace_bytes(cfg, 512)
     assert big > small > 0
     rows = cfg.batch * cfg.n_q_heads * (-(-cfg.max_tokens // 512) + 1)
-    assert big >= cfg.batch * (cfg.n_kv_heads + 1) * 4 + rows * (cfg.head_dim + 2) * 4
+    assert big >= (cfg.batch * (cfg.n_kv_heads + 1) + 1) * 4 + rows * (cfg.head_dim + 2) * 4
     # 64-token splits of this cache would be > 128 splits
     with pytest.raises(kvq.KvqError) as e:
         kvq.kvq_decode_workspace_bytes(cfg, 64)
@@ -233,7 +233,7 @@ def test_workspace_grows_with_split_count():
         def a256(x):
             return -(-x // 256) * 256
         rows = c.batch * c.n_q_heads * (nsplit + 1)
-        return a256(c.batch * (c.n_kv_heads + 1) * 4) + a256(rows * c.head_dim * 4) + 2 * a256(rows * 4)
+        return a256((c.batch * (c.n_kv_heads + 1) + 1) * 4) + a256(rows * c.head_dim * 4) + 2 * a256(rows * 4)
     for w in (WORKLOADS[1], WORKLOADS[2], WORKLOADS[4]):
         c = _cfg(w)
         assert kvq.kvq_decode_workspace_bytes(c, 0) == ws(c, min(128, max(1, c.max_tokens // 256)))

@@ -33,7 +33,8 @@ def _fused(cache, k1, v1, q, sm, skipped=None):
 
 
 def _counters_zero(cache):
-    n = cache.cfg.batch * (cache.cfg.n_kv_heads + 1)
+    # [B][Hkv] arrival counters, [B] per-sequence counters, the work-item counter
+    n = cache.cfg.batch * (cache.cfg.n_kv_heads + 1) + 1
     return torch.count_nonzero(cache.ws[:4 * n].view(torch.int32)).item() == 0
 
 

@@ -93,8 +93,9 @@ def test_small_workload_append_and_decode(idx):
     # the same call twice gives the same bits
     out1 = cache.decode(q, sm, 0).cpu().numpy()
     np.testing.assert_array_equal(out0.view(np.uint32), out1.view(np.uint32))
-    # every call leaves the workspace's arrival counters at zero
-    n_cnt = w.batch * w.n_kv_heads
+    # every call leaves the workspace's counters at zero: [B][Hkv] arrival
+    # counters, [B] per-sequence counters and the work-item counter
+    n_cnt = w.batch * (w.n_kv_heads + 1) + 1
     assert torch.count_nonzero(cache.ws[:4 * n_cnt].view(torch.int32)).item() == 0
 
     # streaming: single-token appends, crossing KIVI flush boundaries
