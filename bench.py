@@ -144,7 +144,8 @@ def workload_key(w):
     return f"{fmt}_b{w.batch}_hkv{w.n_kv_heads}_hq{w.n_q_heads}_d{w.head_dim}_n{ctx}"
 
 
-DECODE_SOURCES = ("quantized_kv_cache_06_amd/csrc/kvq_decode.hip", "quantized_kv_cache_06_amd/csrc/kvq_device.h",
+DECODE_SOURCES = ("quantized_kv_cache_06_amd/csrc/kvq_decode.hip", "quantized_kv_cache_06_amd/csrc/kvq_api.cpp",
+                  "quantized_kv_cache_06_amd/csrc/kvq_device.h",
                   "quantized_kv_cache_06_amd/csrc/kvq_quant.h",
                   "quantized_kv_cache_06_amd/csrc/kvq_internal.h", "include/kvq.h")
 
