@@ -684,8 +684,8 @@ __global__ __launch_bounds__(kThreads) void ring_copy(CacheView cv, const int32_
 }
 
 // ---------------------------------------------------------------------------
-// Last launch: one workgroup per sequence advances seq_lens[b] (every
-// earlier launch of the append has read it) and reports a skipped sequence.
+// Last launch: one thread per sequence advances seq_lens[b] (every earlier
+// launch of the append has read it) and reports a skipped sequence.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void append_finish(CacheView cv, int32_t* __restrict__ seq_lens, int T,
                                                    const int32_t* __restrict__ append_lens,
