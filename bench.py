@@ -145,7 +145,7 @@ def workload_key(w):
 
 
 DECODE_SOURCES = ("quantized_kv_cache_06_amd/csrc/kvq_decode.hip", "quantized_kv_cache_06_amd/csrc/kvq_api.cpp",
-                  "quantized_kv_cache_06_amd/csrc/kvq_device.h",
+                  "quantized_kv_cache_06_amd/csrc/kvq_device.h", "quantized_kv_cache_06_amd/csrc/kvq_wave.h",
                   "quantized_kv_cache_06_amd/csrc/kvq_quant.h",
                   "quantized_kv_cache_06_amd/csrc/kvq_internal.h", "include/kvq.h")
 

@@ -57,6 +57,7 @@
 #include <type_traits>
 
 #include "kvq_quant.h"
+#include "kvq_wave.h"
 
 namespace kvq {
 namespace {
@@ -157,13 +158,6 @@ __device__ __forceinline__ uint32_t f16_residual(uint32_t hi, float x0, float x1
   return pack_f16(__builtin_fmaf(float(h[0]), m1, x0), __builtin_fmaf(float(h[1]), m1, x1));
 }
 
-// Within each 16-lane row: the lanes of the banks in `banks` (bit b = lanes
-// 4b..4b+3) take src from the lane 8 places along; the others keep old.
-template <int BANKS>
-__device__ __forceinline__ uint32_t swap8_into(uint32_t old, uint32_t src) {
-  return uint32_t(__builtin_amdgcn_update_dpp(int(old), int(src), 0x128, 0xf, BANKS, false));
-}
-
 // Two floats to a bf16 pair, round to nearest even (x0 in the low half).
 __device__ __forceinline__ uint32_t pack_bf16(float x0, float x1) {
   const f32x2 v = {x0, x1};
@@ -183,55 +177,6 @@ __device__ __forceinline__ Split2 split_pair(float x0, float x1) {
   return s;
 }
 
-// x + (x of the lane 8 places along the same 16-lane row): adds the hi and
-// lo columns of one head.
-__device__ __forceinline__ float add_ror8(float x) {
-  const int y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false);
-  return x + __builtin_bit_cast(float, y);
-}
-__device__ __forceinline__ float max_ror8(float x) {  // max with the lane 8 places along the row
-  const int y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false);
-  return fmaxf(x, __builtin_bit_cast(float, y));
-}
-__device__ __forceinline__ float max_rows(float x) {  // max over lanes l, l^16, l^32, l^48
-  x = fmaxf(x, __shfl_xor(x, 16, kWave));
-  return fmaxf(x, __shfl_xor(x, 32, kWave));
-}
-__device__ __forceinline__ float sum_rows(float x) {
-  x += __shfl_xor(x, 16, kWave);
-  return x + __shfl_xor(x, 32, kWave);
-}
-// Maximum over lanes 0-31, wave-uniform, without LDS traffic: quad swaps,
-// the half-row and row mirrors leave each 16-lane row holding its maximum;
-// lanes 0 and 16 then give the two rows' maxima.
-template <int CTRL>
-__device__ __forceinline__ float max_dpp(float v) {
-  const int y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false);
-  return fmaxf(v, __builtin_bit_cast(float, y));
-}
-__device__ __forceinline__ float max_lanes32(float x) {
-  x = max_dpp<0xb1>(x);   // quad_perm [1, 0, 3, 2]
-  x = max_dpp<0x4e>(x);   // quad_perm [2, 3, 0, 1]
-  x = max_dpp<0x141>(x);  // row_half_mirror
-  x = max_dpp<0x140>(x);  // row_mirror
-  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
-  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
-  return fmaxf(r0, r1);
-}
-
-// FP8 E4M3 byte pair (bytes 2*sel, 2*sel+1 of w) to a bf16 pair, exact.
-template <int SEL>
-__device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, SEL != 0));
-}
-// Bytes 2 SEL, 2 SEL + 1 of w as an f16 pair, exact, for bytes holding an
-// integer c in 0..15: such a byte is the E4M3 pattern of c * 2^-9 (the
-// subnormals 1..7 continue evenly into the first normal binade 8..15), and
-// the conversion's scale 2^9 restores c.
-template <int SEL>
-__device__ __forceinline__ uint32_t e4m3_pair_f16(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 512.0f, SEL != 0));
-}
 // Signed INT8 byte pair to a bf16 pair, exact.
 template <int SEL>
 __device__ __forceinline__ uint32_t i8x2_bf16(uint32_t w) {
