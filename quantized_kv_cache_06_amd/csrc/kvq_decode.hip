@@ -176,6 +176,15 @@ __device__ __forceinline__ Split2 split_pair(float x0, float x1) {
   s.lo = pack_bf16(x0 - bf_lo(s.hi), x1 - bf_hi(s.hi));
   return s;
 }
+// The same split with each residual x - hi (exact) taken as one bf16 dot
+// product (sub_bf16_half): two instructions fewer where both terms are
+// kept. u = bf16_units().
+__device__ __forceinline__ Split2 split_pair_dot(float x0, float x1, const Bf16Units& u) {
+  Split2 s;
+  s.hi = pack_bf16(x0, x1);
+  s.lo = pack_bf16(sub_bf16_half(s.hi, u.lo, x0), sub_bf16_half(s.hi, u.hi, x1));
+  return s;
+}
 
 // Signed INT8 byte pair to a bf16 pair, exact.
 template <int SEL>
@@ -909,6 +918,7 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   float kb4[NVG];  // group-wise INT4: 136 * the query sum of each channel group
   int eq = 0, fbase = 0;
   const float m1 = KIVI ? opaque_minus_one() : -1.0f;
+  const Bf16Units bu = bf16_units();  // the probability split's dot-product units
   if constexpr (KIVI) {
     const int e0 = tid * EPT, j = e0 / D, c = e0 % D;
 #pragma unroll
@@ -1225,8 +1235,8 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
             else pv[t][u] = ps[t][u] * vsc;
             if constexpr (KIVI) zb[jg] = fmaf(ps[t][u], vzf[t][u * NVG + jg], zb[jg]);
           }
-        const Split2 s0 = split_pair(pv[0][0], pv[1][0]);  // pair ja
-        const Split2 s1 = split_pair(pv[0][1], pv[1][1]);  // pair ja + 1
+        const Split2 s0 = split_pair_dot(pv[0][0], pv[1][0], bu);  // pair ja
+        const Split2 s1 = split_pair_dot(pv[0][1], pv[1][1], bu);  // pair ja + 1
         u32x4 bp;
         bp[0] = swap8_into<0xc>(s0.hi, s0.lo);
         bp[1] = swap8_into<0xc>(s1.hi, s1.lo);

@@ -74,4 +74,26 @@ __device__ __forceinline__ uint32_t e4m3_pair_f16(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 512.0f, SEL != 0));
 }
 
+// x minus one half of a bf16 pair, exactly, in one instruction: the bf16 dot
+// product pair . unit + x, with unit the bf16 pair (-1, 0) (low half) or
+// (0, -1) (high half) held in a register. The units come from bf16_units()
+// as register values the compiler cannot see through: given as constants,
+// the compiler encodes (-1, 0) as the inline constant -1.0, which the
+// instruction reads as the 32-bit pattern of -1.0f, i.e. the pair (0, -1)
+// (every lane of a GPU probe came out wrong; with register units every lane
+// is exact).
+struct Bf16Units {
+  uint32_t lo, hi;  // (-1, 0) and (0, -1)
+};
+__device__ __forceinline__ Bf16Units bf16_units() {
+  Bf16Units u;
+  asm volatile("v_mov_b32 %0, 0x0000bf80" : "=v"(u.lo));
+  asm volatile("v_mov_b32 %0, 0xbf800000" : "=v"(u.hi));
+  return u;
+}
+__device__ __forceinline__ float sub_bf16_half(uint32_t pair, uint32_t unit, float x) {
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, pair), __builtin_bit_cast(b2, unit), x, false);
+}
+
 }  // namespace kvq

@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kOut = 24;  // results per lane
+constexpr int kOut = 26;  // results per lane
 
 __device__ __forceinline__ uint32_t fbits(float x) { return __builtin_bit_cast(uint32_t, x); }
 
@@ -67,12 +67,21 @@ __global__ __launch_bounds__(64) void lane_maps(uint32_t* __restrict__ out) {
   }
   r[22] = kvq::float_key(sx);
   r[23] = fbits(kvq::key_float(kvq::float_key(sx)));
+  {
+    // y - (a bf16 half of a pair) through the bf16 dot product with the
+    // register units: pair = (bf16 truncations of y and of -y)
+    const float y = x * 1.0078125f + 0.0009765625f;
+    const uint32_t pair = (fbits(y) >> 16) | (fbits(-y) & 0xffff0000u);
+    const kvq::Bf16Units u = kvq::bf16_units();
+    r[24] = fbits(kvq::sub_bf16_half(pair, u.lo, y));
+    r[25] = fbits(kvq::sub_bf16_half(pair, u.hi, -y));
+  }
   for (int i = 0; i < kOut; ++i) out[i * 64 + l] = r[i];
 }
 
 }  // namespace
 
-// out: device, 24 * 64 uint32 (result i of lane l at i * 64 + l). Returns a
+// out: device, 26 * 64 uint32 (result i of lane l at i * 64 + l). Returns a
 // hipError_t value.
 extern "C" int kvq_test_lane_maps(uint32_t* out, void* stream) {
   lane_maps<<<1, 64, 0, static_cast<hipStream_t>(stream)>>>(out);

@@ -3,8 +3,9 @@
 (tests/lane_maps/lane_maps.hip) and compared with their definitions:
 the DPP controls (quad_perm, row_ror by 8 under bank masks, half-row and row
 mirrors), the cross-row shuffles, the order-preserving float keys, the byte
-transpose and the FP8 E4M3 byte conversions (every byte to bf16; the
-integers 0..15 to f16 through the scale 2^9)."""
+transpose, the FP8 E4M3 byte conversions (every byte to bf16; the
+integers 0..15 to f16 through the scale 2^9) and the bf16 dot product that
+subtracts one half of a bf16 pair."""
 import ctypes
 import os
 
@@ -36,11 +37,11 @@ def out():
     lib = ctypes.CDLL(LIB)
     lib.kvq_test_lane_maps.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     lib.kvq_test_lane_maps.restype = ctypes.c_int
-    buf = torch.zeros(24 * 64, dtype=torch.int32, device="cuda")
+    buf = torch.zeros(26 * 64, dtype=torch.int32, device="cuda")
     s = torch.cuda.current_stream()
     assert lib.kvq_test_lane_maps(buf.data_ptr(), ctypes.c_void_p(s.cuda_stream)) == 0
     torch.cuda.synchronize()
-    return buf.cpu().numpy().view(np.uint32).reshape(24, 64)
+    return buf.cpu().numpy().view(np.uint32).reshape(26, 64)
 
 
 @pytest.mark.gpu
@@ -106,3 +107,15 @@ def test_small_integers_through_the_scaled_e4m3_to_f16_conversion(out):
     c = (L[:, None] + np.arange(4)[None, :]) % 16
     got = np.stack([out[20] & 0xFFFF, out[20] >> 16, out[21] & 0xFFFF, out[21] >> 16], axis=1)
     np.testing.assert_array_equal(got, c.astype(np.float16).view(np.uint16))
+
+
+@pytest.mark.gpu
+def test_bf16_half_subtraction_by_dot_product(out):
+    """y - float(bf16 half) as one bf16 dot product with the register units
+    (-1, 0) and (0, -1): exact, and each unit picks its own half."""
+    y = X * np.float32(1.0078125) + np.float32(2.0 ** -10)
+    def trunc(a):
+        return (_bits(a) & np.uint32(0xFFFF0000)).view(np.float32)
+    np.testing.assert_array_equal(out[24], _bits(y - trunc(y)))
+    np.testing.assert_array_equal(out[25], _bits(-y - trunc(-y)))
+    assert np.all(out[24] != 0)
