@@ -318,7 +318,11 @@ int32_t decode_call(const kvq_config* cfg, const void* cache, const int32_t* seq
   work.n3 = plan.n3;
   work.w3 = plan.w3;
   work.nitems = int(int64_t(cfg->batch) * cfg->n_kv_heads * (n + (kivi_fmt(cfg) ? 1 : 0)));
-  work.dynamic = plan.dynamic;
+  // with a dynamic plan, the workgroups of the first round (those the device
+  // holds at once) take their items by launch index; only the later ones
+  // draw from the counter, so the draws are spread over the call instead of
+  // all coming at its start
+  work.nstatic = plan.dynamic && resident < work.nitems ? resident : work.nitems;
   const hipError_t e = kvq::launch_decode(v, seq_lens, q, sm_scale, out, work, app, hs);
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }

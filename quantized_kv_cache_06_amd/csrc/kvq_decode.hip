@@ -1741,13 +1741,17 @@ __device__ __forceinline__ void decode_item(const CacheView& cv, const int32_t* 
   }
 }
 
-// One workgroup per work item. With wk.dynamic the items go out in the
-// order the workgroups draw numbers from wk.queue (not their launch index):
-// a unit that frees a slot early gets the next item of the list, whichever
-// XCD it is on (each XCD launches its own share of the grid). The workgroup
-// that draws the last number (nitems - 1) resets the counter for the next
-// call. Otherwise workgroup x takes item x. The sequence lengths (up to 64
-// of them) are loaded in the same round trip as the number.
+// One workgroup per work item. Workgroup x < wk.nstatic (with a dynamic
+// plan, the first round: the workgroups the device holds at once) takes
+// item x. Every later workgroup draws a number from wk.queue and takes item
+// nstatic + number, so the items after the first round go out in the order
+// slots free up (not by launch index): a unit that finishes early gets the
+// next item of the list, whichever XCD it is on (each XCD launches its own
+// share of the grid). Drawing only after the first round spreads the draws
+// over the call; all of them at its start contend on the one counter. The
+// workgroup that draws the last number resets the counter for the next
+// call. The sequence lengths (up to 64 of them) are loaded in the same
+// round trip as the number.
 template <int FMT, int BITS, int D, int G, bool BF16, bool FUSED>
 __global__ __launch_bounds__(kThreads, (min_wg_per_cu<FMT, BITS, D, G, FUSED, BF16>())) void decode_split(
     CacheView cv, const int32_t* seq_lens, const void* __restrict__ q, float sm_log2, float* __restrict__ out,
@@ -1759,13 +1763,14 @@ __global__ __launch_bounds__(kThreads, (min_wg_per_cu<FMT, BITS, D, G, FUSED, BF
   const int tid = threadIdx.x, lane = tid % kWave;
   const int lens = lane < cv.B ? seq_lens[lane] : 0;
   int item = blockIdx.x;
-  if (wk.dynamic) {
+  if (item >= wk.nstatic) {
     if (tid == 0) {
+      const uint32_t nd = uint32_t(wk.nitems - wk.nstatic);
       const uint32_t it = __hip_atomic_fetch_add(wk.queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (it == uint32_t(wk.nitems - 1)) __hip_atomic_store(wk.queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (it == nd - 1) __hip_atomic_store(wk.queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       // a counter that was not zero on entry (a broken workspace contract)
       // still yields item numbers in range
-      item_sh = it % uint32_t(wk.nitems);
+      item_sh = uint32_t(wk.nstatic) + it % nd;
     }
     __syncthreads();
     item = __builtin_amdgcn_readfirstlane(int(item_sh));

@@ -49,7 +49,7 @@ struct DecodeWork {
   // n3 of weight w3 (n1 + n2 + n3 = S - 1, n1 >= 1)
   int n1, w1, n2, w2, n3, w3;
   int nitems;       // work items (one workgroup each): B * Hkv * (S - 1), plus B * Hkv for KIVI
-  int dynamic;      // 1: items are handed out through queue; 0: workgroup x takes item x
+  int nstatic;      // workgroup x < nstatic takes item x; the later ones draw items nstatic.. from queue
 };
 
 // skipped: NULL, or [B] set to 1 for each sequence the append leaves
