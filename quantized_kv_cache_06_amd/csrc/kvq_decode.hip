@@ -1026,14 +1026,22 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
             if constexpr (M16) gv[j] = half_at(sl.gh, j);
             else gv[j] = sl.gw[j];
           }
-          float ms = 0.0f;
+          // the largest scale's bit pattern (scales are >= 0, so the
+          // unsigned order of the patterns is theirs); kes = 7 - its
+          // binary exponent e (largest in [2^(e-1), 2^e)), 0 for all zero
+          uint32_t mb = 0u;
 #pragma unroll
-          for (int j = 0; j < KGL; ++j) ms = fmaxf(ms, gv[j]);
-          ms = max_lanes32(ms);
-          kes = ms > 0.0f ? 7 - __builtin_amdgcn_frexp_expf(ms) : 0;
+          for (int j = 0; j < KGL; ++j) {
+            const uint32_t u = __builtin_bit_cast(uint32_t, gv[j]);
+            mb = mb > u ? mb : u;
+          }
+          mb = max_lanes32_bits(mb);
+          if (mb >= 0x00800000u) kes = 133 - int(mb >> 23);     // normal: e = biased exponent - 126
+          else kes = mb != 0u ? 124 + __builtin_clz(mb) : 0;  // subnormal: e = 32 - clz - 149
+          const int kl = part ? 0 : kes;
           float* gdst = sm.kgrp[wave][part] + qi * KGL;
 #pragma unroll
-          for (int j = 0; j < KGL; ++j) gdst[j] = part ? gv[j] : __builtin_amdgcn_ldexpf(gv[j], kes);
+          for (int j = 0; j < KGL; ++j) gdst[j] = __builtin_amdgcn_ldexpf(gv[j], kl);
         }
       }
     }

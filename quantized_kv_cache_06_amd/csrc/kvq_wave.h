@@ -42,22 +42,25 @@ __device__ __forceinline__ float sum_rows(float x) {
   x += __shfl_xor(x, 16, kWave);
   return x + __shfl_xor(x, 32, kWave);
 }
-// Maximum over lanes 0-31, wave-uniform, without LDS traffic: quad swaps,
-// the half-row and row mirrors leave each 16-lane row holding its maximum;
-// lanes 0 and 16 then give the two rows' maxima.
+// Maximum over lanes 0-31, wave-uniform, without LDS traffic, of the bit
+// patterns of non-negative floats (+0 included), whose unsigned order is
+// the order of the values: quad swaps, the half-row and row mirrors leave
+// each 16-lane row holding its maximum (every step one integer maximum,
+// with no NaN quieting of the exchanged values); lanes 0 and 16 then give
+// the two rows' maxima.
 template <int CTRL>
-__device__ __forceinline__ float max_dpp(float v) {
-  const int y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false);
-  return fmaxf(v, __builtin_bit_cast(float, y));
+__device__ __forceinline__ uint32_t umax_dpp(uint32_t v) {
+  const uint32_t y = uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xf, 0xf, false));
+  return v > y ? v : y;
 }
-__device__ __forceinline__ float max_lanes32(float x) {
-  x = max_dpp<0xb1>(x);   // quad_perm [1, 0, 3, 2]
-  x = max_dpp<0x4e>(x);   // quad_perm [2, 3, 0, 1]
-  x = max_dpp<0x141>(x);  // row_half_mirror
-  x = max_dpp<0x140>(x);  // row_mirror
-  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
-  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
-  return fmaxf(r0, r1);
+__device__ __forceinline__ uint32_t max_lanes32_bits(uint32_t x) {
+  x = umax_dpp<0xb1>(x);   // quad_perm [1, 0, 3, 2]
+  x = umax_dpp<0x4e>(x);   // quad_perm [2, 3, 0, 1]
+  x = umax_dpp<0x141>(x);  // row_half_mirror
+  x = umax_dpp<0x140>(x);  // row_mirror
+  const uint32_t r0 = uint32_t(__builtin_amdgcn_readlane(int(x), 0));
+  const uint32_t r1 = uint32_t(__builtin_amdgcn_readlane(int(x), 16));
+  return r0 > r1 ? r0 : r1;
 }
 
 // FP8 E4M3 byte pair (bytes 2*sel, 2*sel+1 of w) to a bf16 pair, exact.

@@ -25,7 +25,7 @@ __global__ __launch_bounds__(64) void lane_maps(uint32_t* __restrict__ out) {
   r[1] = fbits(kvq::max_ror8(x));
   r[2] = fbits(kvq::max_rows(x));
   r[3] = fbits(kvq::sum_rows(x));
-  r[4] = fbits(kvq::max_lanes32(x));
+  r[4] = kvq::max_lanes32_bits(fbits(x));
   r[5] = kvq::swap8_into<0xc>(1000u + l, 2000u + l);
   r[6] = kvq::swap8_into<0x3>(1000u + l, 2000u + l);
   r[7] = fbits(kvq::run_absmax<8>(x));
