@@ -12,9 +12,9 @@
 // How the work maps onto CDNA4
 // ----------------------------
 // One workgroup (4 waves) per work item, a split of one (kv head,
-// sequence) pair (see decode_item); each wave owns a contiguous run of
-// 32-token tiles of the split and keeps its own online softmax state; the
-// waves are merged through LDS at the end. Per tile:
+// sequence) pair (see decode_item); the waves take the split's 32-token
+// tiles (whole groups for KIVI) in turn, each keeping its own online
+// softmax state, and are merged through LDS at the end. Per tile:
 //
 //  scores (QK): S^T[32 tokens x 16 cols] = K[32 x d] * Qt[d x 16] with
 //    v_mfma_f32_16x16x32_bf16 (KIVI: _f16). Column c = 8 * term + head:
