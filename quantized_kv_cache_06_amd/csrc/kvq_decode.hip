@@ -25,13 +25,14 @@
 //    core exactly: E4M3 and INT8 codes convert to bf16 exactly; group-wise
 //    INT4 nibbles (code + 8) become the bf16 128 + nibble by OR-ing them
 //    under the bf16 pattern of 128 (136 * sum(q) comes off per channel
-//    group); KIVI codes are masked into bytes, where a byte holding
-//    c * 2^k (c * 2^k <= 15) is the E4M3 pattern of c * 2^(k-9), and the
-//    scaled FP8 conversion (scale 2^9) turns two such bytes into the f16
-//    pair c * 2^k exactly. Per-token scales multiply the finished scores;
-//    KIVI per-channel Key scales are folded into the query once per group
-//    (score = sum_c (q_c s_c) code_c + sum_c q_c z_c), with 2^-k taken into
-//    the query as well.
+//    group); KIVI 4-bit codes are masked one per byte, where a byte
+//    holding c <= 15 is the E4M3 pattern of c * 2^-9, and the scaled FP8
+//    conversion (scale 2^9) turns two such bytes into the f16 pair c
+//    exactly; KIVI 2-bit codes are masked one per nibble, the E2M1 pattern
+//    of c / 2, and the scaled FP4 conversion (scale 2) turns a byte into
+//    the f16 pair of its two codes. Per-token scales multiply the finished
+//    scores; KIVI per-channel Key scales are folded into the query once per
+//    group (score = sum_c (q_c s_c) code_c + sum_c q_c z_c).
 //  softmax: running maximum and sum per head in the log2 domain (exp2).
 //  values (PV): O^T[d x 16] += V^T[d x 32] * P^T[32 x 16], again with the
 //    probabilities (times the per-token Value scale) split into bf16 hi and
@@ -217,14 +218,14 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Channel of element i of k-step kk held by row group r in the score MFMA:
 // lanes of row group r hold the contiguous channels [CPL*r, CPL*(r+1)), CPL =
 // D/4, and element i of k-step kk is the following one of them.
-// KIVI (KBYTE set) takes its Key codes in the order the byte-wise
-// conversion of key_operand produces them; group-wise INT4 pairs nibble j
-// with nibble j + 4.
+// KIVI (KBYTE set) takes its Key codes in the order the conversions of
+// key_operand produce them; group-wise INT4 pairs nibble j with nibble
+// j + 4.
 template <int BITS, bool KBYTE = false>
 __device__ __forceinline__ constexpr int cperm(int kk, int i) {
   if constexpr (BITS >= 8) return 8 * kk + i;
   else if constexpr (BITS == 4 && KBYTE) return 8 * kk + 2 * (i & 3) + (i >> 2);
-  else if constexpr (BITS == 2 && KBYTE) return 16 * (kk >> 1) + 8 * (kk & 1) + (i >> 1) + 4 * (i & 1);
+  else if constexpr (BITS == 2 && KBYTE) return 16 * (kk >> 1) + 8 * (kk & 1) + 4 * (i >> 2) + ((i >> 1) & 1) + 2 * (i & 1);
   else if constexpr (BITS == 4) return 8 * kk + (i >> 1) + 4 * (i & 1);
   else return 16 * (kk >> 1) + 4 * (kk & 1) + (i >> 1) + 8 * (i & 1);
 }
@@ -317,16 +318,12 @@ __device__ __forceinline__ void load_elems(const void* p, size_t i, float* x) {
 
 // Key operand (16 tokens x 32 channels) of k-step kk from the lane's raw
 // Key bytes. 8-bit codes: bf16, exact. KIVI codes: f16, each element exactly
-// code * 2^kfactor_log2(i): the codes are masked into bytes (INT4: one
-// nibble per byte; INT2: the fields at bits 0-1 (x1) or 2-3 (x4) of each
-// byte) and two bytes at a time go through the scaled E4M3 conversion (see
-// e4m3_pair_f16). The f16 results are normal numbers or zero, which the
+// the code: INT4 codes are masked one nibble per byte and two bytes at a
+// time go through the scaled E4M3 conversion (e4m3_pair_f16); INT2 codes
+// are masked two per byte, one per nibble (fields 0 and 2, then 1 and 3),
+// and one byte at a time goes through the scaled E2M1 conversion
+// (e2m1_pair_f16). The f16 results are normal numbers or zero, which the
 // matrix cores multiply exactly.
-template <int BITS>
-__device__ __forceinline__ constexpr int kfactor_log2(int i) {
-  if constexpr (BITS == 4) return 0;
-  else return ((i >> 1) & 1) ? 2 : 0;
-}
 
 template <int FMT, int BITS>
 __device__ __forceinline__ u32x4 key_operand(const uint32_t* kw, int kk) {
@@ -357,17 +354,17 @@ __device__ __forceinline__ u32x4 key_operand(const uint32_t* kw, int kk) {
     a[2] = e4m3_pair_f16<0>(od);
     a[3] = e4m3_pair_f16<1>(od);
   } else {
-    // word kk/2 holds 16 codes, 4 per byte; field f of every byte (bits 0-1
-    // x1, 2-3 x4, then the same of w >> 4) gives the pairs (code f, code
-    // f + 4) of bytes 0-1 (even kk) or (code 8 + f, code 12 + f) of bytes 2-3
-    const uint32_t w = kw[kk >> 1], w4 = w >> 4;
-    const uint32_t f0 = w & 0x03030303u, f1 = w & 0x0C0C0C0Cu, f2 = w4 & 0x03030303u, f3 = w4 & 0x0C0C0C0Cu;
+    // word kk/2 holds 16 codes, 4 per byte (field f at bits 2f): m0 keeps
+    // fields 0 and 2 of every byte, m1 fields 1 and 3, one per nibble; byte
+    // b of each gives the pairs (field 0, 2) and (1, 3) of byte b, from
+    // bytes 0-1 (even kk) or 2-3 (odd kk)
+    const uint32_t w = kw[kk >> 1], m0 = w & 0x33333333u, m1 = (w >> 2) & 0x33333333u;
     if (kk & 1) {
-      a[0] = e4m3_pair_f16<1>(f0); a[1] = e4m3_pair_f16<1>(f1);
-      a[2] = e4m3_pair_f16<1>(f2); a[3] = e4m3_pair_f16<1>(f3);
+      a[0] = e2m1_pair_f16<2>(m0); a[1] = e2m1_pair_f16<2>(m1);
+      a[2] = e2m1_pair_f16<3>(m0); a[3] = e2m1_pair_f16<3>(m1);
     } else {
-      a[0] = e4m3_pair_f16<0>(f0); a[1] = e4m3_pair_f16<0>(f1);
-      a[2] = e4m3_pair_f16<0>(f2); a[3] = e4m3_pair_f16<0>(f3);
+      a[0] = e2m1_pair_f16<0>(m0); a[1] = e2m1_pair_f16<0>(m1);
+      a[2] = e2m1_pair_f16<1>(m0); a[3] = e2m1_pair_f16<1>(m1);
     }
   }
   return a;
@@ -911,8 +908,8 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
   // KIVI Key-group fold layout: lane (m, r) computes both f16 terms of the
   // operand pairs of head hh, row group r, for the NKW k-steps from kk0 (the
   // hi lanes the first half, the lo lanes the second); the two lanes of a
-  // (head, row group) then swap halves. qn = q * 2^(eq - kfactor) for those
-  // elements, eq putting the head's largest |q * 2^-kfactor| in [64, 128).
+  // (head, row group) then swap halves. qn = q * 2^eq for those elements,
+  // eq putting the head's largest |q| in [64, 128).
   constexpr int NKW = NKK / 2;
   float qn[NKW][4][2];
   float kb4[NVG];  // group-wise INT4: 136 * the query sum of each channel group
@@ -934,8 +931,7 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const int i = 2 * e + h2;
-          const float v = __builtin_amdgcn_ldexpf(sm.q[hh][fbase + cperm<BITS, KBYTE>(kw, i)],
-                                                  -kfactor_log2<BITS>(i));
+          const float v = sm.q[hh][fbase + cperm<BITS, KBYTE>(kw, i)];
           qn[kw][e][h2] = v;
           mx = fmaxf(mx, fabsf(v));
         }
@@ -1051,7 +1047,7 @@ __device__ __forceinline__ void split_quantized(const CacheView& cv, int b, int 
     // x_c = qn_c * s'_c (|x| < 2^14) split into f16 hi + lo (about 22
     // significant bits); the score of a token is then
     //   acc * 2^(-eq - kes) + sum_c q_c z_c,
-    // acc the matrix-core sum of x against the Key codes (times 2^kfactor).
+    // acc the matrix-core sum of x against the Key codes.
     if constexpr (KIVI) {
       if (grp_open) {
         const float* ksr = &sm.kgrp[wave][0][fbase];

@@ -76,6 +76,15 @@ template <int SEL>
 __device__ __forceinline__ uint32_t e4m3_pair_f16(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 512.0f, SEL != 0));
 }
+// Byte SEL of w as an f16 pair, exact, for a byte whose two nibbles hold
+// integers c in 0..3 (upper two bits of each nibble zero): such a nibble is
+// the FP4 E2M1 pattern of c / 2 (the subnormal 0.5 continues evenly into
+// 1.0 and 1.5), and the conversion's scale 2 restores c. The low half holds
+// the low nibble.
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_pair_f16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 2.0f, SEL));
+}
 
 // x minus one half of a bf16 pair, exactly, in one instruction: the bf16 dot
 // product pair . unit + x, with unit the bf16 pair (-1, 0) (low half) or

@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kOut = 26;  // results per lane
+constexpr int kOut = 30;  // results per lane
 
 __device__ __forceinline__ uint32_t fbits(float x) { return __builtin_bit_cast(uint32_t, x); }
 
@@ -76,12 +76,22 @@ __global__ __launch_bounds__(64) void lane_maps(uint32_t* __restrict__ out) {
     r[24] = fbits(kvq::sub_bf16_half(pair, u.lo, y));
     r[25] = fbits(kvq::sub_bf16_half(pair, u.hi, -y));
   }
+  {
+    // 2-bit integers in the nibbles: byte k of lane l holds (l + k) mod 4
+    // (low nibble) and (l + 2k + 1) mod 4 (high nibble)
+    uint32_t w = 0;
+    for (int k = 0; k < 4; ++k) w |= uint32_t(((l + k) % 4) | (((l + 2 * k + 1) % 4) << 4)) << (8 * k);
+    r[26] = kvq::e2m1_pair_f16<0>(w);
+    r[27] = kvq::e2m1_pair_f16<1>(w);
+    r[28] = kvq::e2m1_pair_f16<2>(w);
+    r[29] = kvq::e2m1_pair_f16<3>(w);
+  }
   for (int i = 0; i < kOut; ++i) out[i * 64 + l] = r[i];
 }
 
 }  // namespace
 
-// out: device, 26 * 64 uint32 (result i of lane l at i * 64 + l). Returns a
+// out: device, 30 * 64 uint32 (result i of lane l at i * 64 + l). Returns a
 // hipError_t value.
 extern "C" int kvq_test_lane_maps(uint32_t* out, void* stream) {
   lane_maps<<<1, 64, 0, static_cast<hipStream_t>(stream)>>>(out);

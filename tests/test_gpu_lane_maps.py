@@ -4,8 +4,9 @@
 the DPP controls (quad_perm, row_ror by 8 under bank masks, half-row and row
 mirrors), the cross-row shuffles, the order-preserving float keys, the byte
 transpose, the FP8 E4M3 byte conversions (every byte to bf16; the
-integers 0..15 to f16 through the scale 2^9) and the bf16 dot product that
-subtracts one half of a bf16 pair."""
+integers 0..15 to f16 through the scale 2^9), the FP4 E2M1 nibble
+conversion (the integers 0..3 to f16 through the scale 2) and the bf16 dot
+product that subtracts one half of a bf16 pair."""
 import ctypes
 import os
 
@@ -37,11 +38,11 @@ def out():
     lib = ctypes.CDLL(LIB)
     lib.kvq_test_lane_maps.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     lib.kvq_test_lane_maps.restype = ctypes.c_int
-    buf = torch.zeros(26 * 64, dtype=torch.int32, device="cuda")
+    buf = torch.zeros(30 * 64, dtype=torch.int32, device="cuda")
     s = torch.cuda.current_stream()
     assert lib.kvq_test_lane_maps(buf.data_ptr(), ctypes.c_void_p(s.cuda_stream)) == 0
     torch.cuda.synchronize()
-    return buf.cpu().numpy().view(np.uint32).reshape(26, 64)
+    return buf.cpu().numpy().view(np.uint32).reshape(30, 64)
 
 
 @pytest.mark.gpu
@@ -107,6 +108,19 @@ def test_small_integers_through_the_scaled_e4m3_to_f16_conversion(out):
     c = (L[:, None] + np.arange(4)[None, :]) % 16
     got = np.stack([out[20] & 0xFFFF, out[20] >> 16, out[21] & 0xFFFF, out[21] >> 16], axis=1)
     np.testing.assert_array_equal(got, c.astype(np.float16).view(np.uint16))
+
+
+@pytest.mark.gpu
+def test_two_bit_integers_through_the_scaled_e2m1_to_f16_conversion(out):
+    """A nibble c in 0..3 (the E2M1 pattern of c / 2) converts with scale 2 to
+    the f16 value c exactly; byte k of the word gives result k, its low
+    nibble in the low half."""
+    for k in range(4):
+        lo = (L + k) % 4
+        hi = (L + 2 * k + 1) % 4
+        got = np.stack([out[26 + k] & 0xFFFF, out[26 + k] >> 16], axis=1)
+        want = np.stack([lo, hi], axis=1).astype(np.float16).view(np.uint16)
+        np.testing.assert_array_equal(got, want)
 
 
 @pytest.mark.gpu
