@@ -438,8 +438,12 @@ def run_workload(torch, kvq, w, args, copies_override=0, want_host=False):
     for c in range(copies):
         buf = torch.zeros(lay.total_bytes, dtype=torch.uint8, device=dev)
         sl = torch.zeros(w.batch, dtype=torch.int32, device=dev)
-        k, v = kv_tokens(w, n_max, layer=c, device=dev)
+        # the lengths' host-to-device copy waits for the host; made before the
+        # inputs are generated, so that the device is still busy with those
+        # while the host issues the append (the window then holds device
+        # work only, not the binding's marshalling)
         al = lens0.to(dev) if w.ragged else None
+        k, v = kv_tokens(w, n_max, layer=c, device=dev)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         kvq.kvq_quantize_append(cfg, buf, sl, k, v, n_max, al)
