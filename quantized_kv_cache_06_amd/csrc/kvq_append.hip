@@ -40,6 +40,11 @@ constexpr int kThreads = 256;
 #ifndef KVQ_APPEND_PRELOAD
 #define KVQ_APPEND_PRELOAD 1
 #endif
+// Workgroups per compute unit the register allocation of the KIVI flush
+// (d = 128, bf16 inputs) must allow.
+#ifndef KVQ_FLUSH_WG_PER_CU
+#define KVQ_FLUSH_WG_PER_CU 3
+#endif
 
 // Length checks shared by the append kernels: a sequence whose append would
 // be malformed or overflow the capacity is left unchanged.
@@ -411,11 +416,13 @@ __global__ __launch_bounds__(kThreads) void kivi_flush(CacheView cv, const int32
 
 // ---------------------------------------------------------------------------
 // KIVI group flush for head_dim 128 and bf16 inputs (the benchmark shapes):
-// one wave per 64 flushed tokens (one group of 64, or two of 32), no LDS and
-// no barrier. Lane l takes quarter q = l / 16 of the tokens (16 consecutive
+// two waves per 64 flushed tokens (one group of 64, or two of 32), the even
+// wave of a pair of waves the Keys, the odd one the Values, no LDS and no
+// barrier. Lane l takes quarter q = l / 16 of the tokens (16 consecutive
 // rows, whole Value blocks) and channels [8 g, 8 g + 8), g = l % 16: load j
 // fetches row 16 q + j of every quarter in 16-byte pieces, from the residual
-// ring (tokens below the old length) or the new input.
+// ring (tokens below the old length) or the new input. A wave holds one
+// tensor's rows, so it issues all its loads at once.
 //  - Key: per-channel minimum and maximum over the lane's 16 rows, combined
 //    across the quarters of the group with lane exchanges;
 //  - Value: per-token, per-channel-group minimum and maximum over the
@@ -427,7 +434,7 @@ __global__ __launch_bounds__(kThreads) void kivi_flush(CacheView cv, const int32
 // flush_value (and of the oracle): fp32, true quotients, round half to even.
 // ---------------------------------------------------------------------------
 template <int BITS, int G, bool M16>
-__global__ __launch_bounds__(kThreads, 2) void kivi_flush_waves(CacheView cv, const int32_t* __restrict__ seq_lens,
+__global__ __launch_bounds__(kThreads, KVQ_FLUSH_WG_PER_CU) void kivi_flush_waves(CacheView cv, const int32_t* __restrict__ seq_lens,
                                                             const void* __restrict__ kin,
                                                             const void* __restrict__ vin, int T,
                                                             const int32_t* __restrict__ append_lens) {
@@ -444,7 +451,8 @@ __global__ __launch_bounds__(kThreads, 2) void kivi_flush_waves(CacheView cv, co
   const int q0 = kivi_quantized(n, G, cv.R);
   const int q1 = kivi_quantized(n + tb, G, cv.R);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int T0 = q0 + 64 * (int(blockIdx.x) * (kThreads / kWave) + wave);
+  const bool values = (wave & 1) != 0;  // the tensor this wave flushes (wave-uniform)
+  const int T0 = q0 + 64 * (int(blockIdx.x) * (kThreads / kWave / 2) + wave / 2);
   if (T0 >= q1) return;  // wave-uniform
   const int q = lane / 16, g = lane % 16;
   const int tq = T0 + 16 * q;                              // the lane's first token
@@ -502,7 +510,9 @@ __global__ __launch_bounds__(kThreads, 2) void kivi_flush_waves(CacheView cv, co
   // stand-in divisor 1 is already 0; a binary16 zero-point need not equal
   // the minimum, so there the code is selected.
   auto degen = [](float s_, uint32_t c) { return (!M16 || s_ > 0.0f) ? c : kRoundBits; };
-  u32x4_t kr[16], vr[16];
+  constexpr int KRB = D * BITS / 8;  // Key row bytes
+  if (!values) {
+  u32x4_t kr[16];
   load_rows(cv.k_resid, kin, kr);
 
   // ---- Key: per-channel statistics over the group ----
@@ -530,6 +540,10 @@ __global__ __launch_bounds__(kThreads, 2) void kivi_flush_waves(CacheView cv, co
         kmx[e] = fmaxf(kmx[e], __shfl_xor(kmx[e], o, kWave));
       }
     const float rq = recip_refined(QMAX);
+    // the rows are widened again for the codes rather than held widened
+    // through the statistics (128 registers)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) asm volatile("" : "+v"(kr[j]));
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       ks[e] = stored_meta<M16>(quot_nonneg(kmx[e] - kmn[e], QMAX, rq) + 0.0f);
@@ -546,7 +560,6 @@ __global__ __launch_bounds__(kThreads, 2) void kivi_flush_waves(CacheView cv, co
   }
 
   // ---- Key codes and stores ----
-  constexpr int KRB = D * BITS / 8;  // Key row bytes
   {
     // divisor stand-in 1 for a degenerate channel (s == 0), whose code is 0
     float kdv[8], ky[8];
@@ -578,11 +591,11 @@ __global__ __launch_bounds__(kThreads, 2) void kivi_flush_waves(CacheView cv, co
       }
     }
   }
+  return;
+  }
 
   // ---- Value: per-token statistics over each channel group, codes ----
-  // (its loads are not hoisted above the Key work: that would hold both
-  // tensors' rows in registers at once)
-  asm volatile("" ::: "memory");
+  u32x4_t vr[16];
   load_rows(cv.v_resid, vin, vr);
   uint32_t vword[16 / TB][8];  // [block][channel]
 #pragma unroll
@@ -613,6 +626,9 @@ __global__ __launch_bounds__(kThreads, 2) void kivi_flush_waves(CacheView cv, co
       store_meta<M16>(cv.v_zero, vi, vzr[j]);
     }
   }
+  // the rows are widened again for the codes (as for the Keys)
+#pragma unroll
+  for (int j = 0; j < 16; ++j) asm volatile("" : "+v"(vr[j]));
   if (__all(vfast)) {  // wave-uniform
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -734,9 +750,10 @@ template <int BITS, int G, int D, bool BF16>
 void launch_flush(const CacheView& cv, int32_t* seq_lens, const void* k, const void* v, int T,
                   const int32_t* al, hipStream_t st) {
   if constexpr (D == 128 && BF16) {
-    // one wave per 64 flushed tokens: at most T + G flushed tokens per pair
-    const int waves = (T + G + 63) / 64;
-    const dim3 grid((waves + kThreads / kWave - 1) / (kThreads / kWave), cv.Hkv, cv.B);
+    // two waves per 64 flushed tokens: at most T + G flushed tokens per pair
+    const int chunks = (T + G + 63) / 64;
+    constexpr int kChunksPerWg = kThreads / kWave / 2;
+    const dim3 grid((chunks + kChunksPerWg - 1) / kChunksPerWg, cv.Hkv, cv.B);
     if (cv.fmt == KVQ_FMT_KIVI_F16)
       kivi_flush_waves<BITS, G, true><<<grid, kThreads, 0, st>>>(cv, seq_lens, k, v, T, al);
     else
