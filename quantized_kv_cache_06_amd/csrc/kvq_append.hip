@@ -434,10 +434,9 @@ __global__ __launch_bounds__(kThreads) void kivi_flush(CacheView cv, const int32
 // flush_value (and of the oracle): fp32, true quotients, round half to even.
 // ---------------------------------------------------------------------------
 template <int BITS, int G, bool M16>
-__global__ __launch_bounds__(kThreads, KVQ_FLUSH_WG_PER_CU) void kivi_flush_waves(CacheView cv, const int32_t* __restrict__ seq_lens,
-                                                            const void* __restrict__ kin,
-                                                            const void* __restrict__ vin, int T,
-                                                            const int32_t* __restrict__ append_lens) {
+__global__ __launch_bounds__(kThreads, KVQ_FLUSH_WG_PER_CU) void kivi_flush_waves(
+    CacheView cv, const int32_t* __restrict__ seq_lens, const void* __restrict__ kin, const void* __restrict__ vin,
+    int T, const int32_t* __restrict__ append_lens) {
 #pragma clang fp contract(off)
   constexpr int D = 128;
   constexpr float QMAX = float((1 << BITS) - 1);
@@ -512,86 +511,86 @@ __global__ __launch_bounds__(kThreads, KVQ_FLUSH_WG_PER_CU) void kivi_flush_wave
   auto degen = [](float s_, uint32_t c) { return (!M16 || s_ > 0.0f) ? c : kRoundBits; };
   constexpr int KRB = D * BITS / 8;  // Key row bytes
   if (!values) {
-  u32x4_t kr[16];
-  load_rows(cv.k_resid, kin, kr);
+    u32x4_t kr[16];
+    load_rows(cv.k_resid, kin, kr);
 
-  // ---- Key: per-channel statistics over the group ----
-  float ks[8], kz[8];
-  {
-    float kmn[8], kmx[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      kmn[e] = INFINITY;
-      kmx[e] = -INFINITY;
-    }
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
+    // ---- Key: per-channel statistics over the group ----
+    float ks[8], kz[8];
+    {
+      float kmn[8], kmx[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = elem(kr[j], e);
-        kmn[e] = fminf(kmn[e], x);
-        kmx[e] = fmaxf(kmx[e], x);
+        kmn[e] = INFINITY;
+        kmx[e] = -INFINITY;
       }
 #pragma unroll
-    for (int o = 16; o < 16 * QPG; o <<= 1)
+      for (int j = 0; j < 16; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = elem(kr[j], e);
+          kmn[e] = fminf(kmn[e], x);
+          kmx[e] = fmaxf(kmx[e], x);
+        }
+#pragma unroll
+      for (int o = 16; o < 16 * QPG; o <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          kmn[e] = fminf(kmn[e], __shfl_xor(kmn[e], o, kWave));
+          kmx[e] = fmaxf(kmx[e], __shfl_xor(kmx[e], o, kWave));
+        }
+      const float rq = recip_refined(QMAX);
+      // the rows are widened again for the codes rather than held widened
+      // through the statistics (128 registers)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) asm volatile("" : "+v"(kr[j]));
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        kmn[e] = fminf(kmn[e], __shfl_xor(kmn[e], o, kWave));
-        kmx[e] = fmaxf(kmx[e], __shfl_xor(kmx[e], o, kWave));
+        ks[e] = stored_meta<M16>(quot_nonneg(kmx[e] - kmn[e], QMAX, rq) + 0.0f);
+        kz[e] = stored_meta<M16>(kmn[e] + 0.0f);
       }
-    const float rq = recip_refined(QMAX);
-    // the rows are widened again for the codes rather than held widened
-    // through the statistics (128 registers)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) asm volatile("" : "+v"(kr[j]));
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      ks[e] = stored_meta<M16>(quot_nonneg(kmx[e] - kmn[e], QMAX, rq) + 0.0f);
-      kz[e] = stored_meta<M16>(kmn[e] + 0.0f);
     }
-  }
-  if (ok && q % QPG == 0) {
-    const size_t si = (pair * (cv.cap / G) + size_t(gstart / G)) * D + 8 * g;
+    if (ok && q % QPG == 0) {
+      const size_t si = (pair * (cv.cap / G) + size_t(gstart / G)) * D + 8 * g;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      store_meta<M16>(cv.k_scale, si + e, ks[e]);
-      store_meta<M16>(cv.k_zero, si + e, kz[e]);
+      for (int e = 0; e < 8; ++e) {
+        store_meta<M16>(cv.k_scale, si + e, ks[e]);
+        store_meta<M16>(cv.k_zero, si + e, kz[e]);
+      }
     }
-  }
 
-  // ---- Key codes and stores ----
-  {
-    // divisor stand-in 1 for a degenerate channel (s == 0), whose code is 0
-    float kdv[8], ky[8];
-    bool fast = true;
+    // ---- Key codes and stores ----
+    {
+      // divisor stand-in 1 for a degenerate channel (s == 0), whose code is 0
+      float kdv[8], ky[8];
+      bool fast = true;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      kdv[e] = ks[e] > 0.0f ? ks[e] : 1.0f;
-      fast = fast && in_div_range(kdv[e]);
-      ky[e] = recip_refined(kdv[e]);
-    }
-    fast = __all(fast);  // wave-uniform
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      uint32_t w = 0;
-      if (fast) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          w += degen(ks[e], code_bits(div_refined<false>(elem(kr[j], e) - kz[e], kdv[e], ky[e]))) << (BITS * e);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          w += degen(ks[e], code_bits((elem(kr[j], e) - kz[e]) / kdv[e])) << (BITS * e);
+      for (int e = 0; e < 8; ++e) {
+        kdv[e] = ks[e] > 0.0f ? ks[e] : 1.0f;
+        fast = fast && in_div_range(kdv[e]);
+        ky[e] = recip_refined(kdv[e]);
       }
-      w -= pack_offset(8);
-      if (ok) {
-        uint8_t* row = cv.k_codes + (pair * cv.cap + size_t(tq + j)) * KRB;
-        if constexpr (BITS == 4) *reinterpret_cast<uint32_t*>(row + 4 * g) = w;
-        else *reinterpret_cast<uint16_t*>(row + 2 * g) = uint16_t(w);
+      fast = __all(fast);  // wave-uniform
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        uint32_t w = 0;
+        if (fast) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            w += degen(ks[e], code_bits(div_refined<false>(elem(kr[j], e) - kz[e], kdv[e], ky[e]))) << (BITS * e);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            w += degen(ks[e], code_bits((elem(kr[j], e) - kz[e]) / kdv[e])) << (BITS * e);
+        }
+        w -= pack_offset(8);
+        if (ok) {
+          uint8_t* row = cv.k_codes + (pair * cv.cap + size_t(tq + j)) * KRB;
+          if constexpr (BITS == 4) *reinterpret_cast<uint32_t*>(row + 4 * g) = w;
+          else *reinterpret_cast<uint16_t*>(row + 2 * g) = uint16_t(w);
+        }
       }
     }
-  }
-  return;
+    return;
   }
 
   // ---- Value: per-token statistics over each channel group, codes ----
