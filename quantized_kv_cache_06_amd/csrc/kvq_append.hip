@@ -233,7 +233,8 @@ __global__ __launch_bounds__(kThreads, 3) void append_tiles(CacheView cv, const 
   for (int j = 0; j < 8; ++j) {
     if (j < v_lo || j >= v_hi) continue;
     uint8_t* dst = cv.k_codes + (pair * cv.cap + size_t(tblk + j)) * RB + (CACHE16 ? 16 : 8) * g;
-    if constexpr (CACHE16) *reinterpret_cast<uint4*>(dst) = make_uint4(kcode[j][0], kcode[j][1], kcode[j][2], kcode[j][3]);
+    if constexpr (CACHE16)
+      *reinterpret_cast<uint4*>(dst) = make_uint4(kcode[j][0], kcode[j][1], kcode[j][2], kcode[j][3]);
     else *reinterpret_cast<uint2*>(dst) = make_uint2(kcode[j][0], kcode[j][1]);
   }
   if constexpr (SCALED) {

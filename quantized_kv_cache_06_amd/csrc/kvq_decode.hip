@@ -225,7 +225,8 @@ template <int BITS, bool KBYTE = false>
 __device__ __forceinline__ constexpr int cperm(int kk, int i) {
   if constexpr (BITS >= 8) return 8 * kk + i;
   else if constexpr (BITS == 4 && KBYTE) return 8 * kk + 2 * (i & 3) + (i >> 2);
-  else if constexpr (BITS == 2 && KBYTE) return 16 * (kk >> 1) + 8 * (kk & 1) + 4 * (i >> 2) + ((i >> 1) & 1) + 2 * (i & 1);
+  else if constexpr (BITS == 2 && KBYTE)
+    return 16 * (kk >> 1) + 8 * (kk & 1) + 4 * (i >> 2) + ((i >> 1) & 1) + 2 * (i & 1);
   else if constexpr (BITS == 4) return 8 * kk + (i >> 1) + 4 * (i & 1);
   else return 16 * (kk >> 1) + 4 * (kk & 1) + (i >> 1) + 8 * (i & 1);
 }
