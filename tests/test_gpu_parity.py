@@ -184,6 +184,37 @@ def test_edge_cases_empty_single_residual_only_and_overflow():
             T.assert_cache_matches(contents, b, h, seqs[b][h], w)
 
 
+@pytest.mark.parametrize("idx", [5, 4])
+def test_kivi_key_scales_subnormal_and_zero(idx):
+    """KIVI Key group scales that are fp32 subnormals (sequence 0: Keys
+    scaled by 2^-130, bf16 subnormals) or all zero (sequence 1: Keys 0): the
+    decode's per-group scale exponent takes its subnormal and zero branches.
+    Appends stay bit-exact, and the attention (about the mean of the Values,
+    since every score is about 0) agrees with the oracle."""
+    w = SMALL[idx].scaled(batch=3, context=400, context_min=400)
+    _log(f"[subnormal and zero Key scales: {w.name}]")
+    cache = T.GpuCache(T.config(w, 400))
+    k, v = kv_tokens(w, 400, device="cuda")
+    kf = k.float().cpu()
+    kf[0] *= 2.0 ** -130
+    kf[1] = 0.0
+    k = kf.to(k.dtype).cuda()  # rounded to the input dtype on the host (subnormals kept)
+    lens = torch.full((w.batch,), 400, dtype=torch.int32)
+    cache.append(k, v, None)
+    seqs = _oracle_all(w, k, v, lens)
+    contents = T.CacheContents(cache)
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            T.assert_cache_matches(contents, b, h, seqs[b][h], w)
+    ks = T.as_f32(k)
+    assert np.any((ks[0] != 0) & (np.abs(ks[0]) < 2.0 ** -126)), "the scaled Keys reach the subnormal range"
+    q = queries(w, device="cuda")
+    sm = O.default_sm_scale(w.head_dim)
+    for st in (0, 64):
+        out = _check_decode(w, cache, seqs, q, sm, st, f"tiny-keys-{w.name}")
+        assert np.all(np.isfinite(out))
+
+
 @pytest.mark.parametrize("d,dtype,hq", [(128, "bf16", 16), (64, "f32", 6)])
 def test_kivi_residual_chunk_boundaries(d, dtype, hq):
     """The residual ring is decoded in chunks of 64 tokens: residual-only
